@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Throughput of the DeepSeekMoE layer (router -> dispatch -> grouped SwiGLU
+experts -> combine -> bias update) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config v3] [--gpus 1]
+
+A step is one moe_forward with update_bias=1 over one batch of T tokens whose
+inputs (u, b, weights) are already resident in HBM. K steps are timed between
+two device synchronisations; the library's stage events (recorded on the same
+stream) give each kernel's average duration. One JSON line goes to stdout;
+progress goes to stderr.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(cfg):
+    """Bytes and flops each stage must move/do at minimum, per forward."""
+    T, d, N, K, Ns, I, Is = cfg.T, cfg.d, cfg.n_routed, cfg.top_k, cfg.n_shared, cfg.inter, cfg.inter_shared
+    ex = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.expert_dtype]
+    io = {"bf16": 2, "f32": 4}[cfg.in_dtype]
+    rt = {"bf16": 2, "f32": 4}[cfg.router_dtype]
+    h = 2 if cfg.expert_dtype == "bf16" else 4
+    y = 4 if cfg.expert_dtype == "f32" else 2
+    R = T * K + Ns * T
+    sc = 4.0 / (128 * 128) if cfg.expert_dtype == "fp8" else 0.0
+    w13 = (N * 2 * I * d + Ns * 2 * Is * d) * (ex + sc)
+    w2 = (N * d * I + Ns * d * Is) * (ex + sc)
+    xin = T * d * (1 if cfg.expert_dtype == "fp8" else io)
+    st = {
+        "route": {"bytes": T * d * io + N * d * rt + T * K * 8, "flops": 2.0 * T * d * N},
+        "permute": {"bytes": T * K * 4 + 2 * R * 4, "flops": 0.0},
+        "gemm1": {"bytes": w13 + xin + T * K * I * h + Ns * T * Is * h,
+                  "flops": 2.0 * d * (T * K * 2 * I + Ns * T * 2 * Is)},
+        "gemm2": {"bytes": w2 + (T * K * I + Ns * T * Is) * (1 if cfg.expert_dtype == "fp8" else h) + R * d * y,
+                  "flops": 2.0 * d * (T * K * I + Ns * T * Is)},
+        "combine": {"bytes": R * d * y + 2 * T * d * io + T * K * 8, "flops": 0.0},
+        "bias": {"bytes": N * 12, "flops": 0.0},
+    }
+    if cfg.expert_dtype == "fp8":
+        st["quant_x"] = {"bytes": T * d * (io + 1) + T * d // 128 * 4, "flops": 0.0}
+    return st
+
+
+def cpu_baseline(cfg, n_sample_experts, log_fn):
+    """The oracle (unchanged) on a bounded sample of one step, scaled to tokens/s.
+
+    Sample: routing of all T tokens (fp64 logits, sigmoid, group-limited top-K,
+    gates); the SwiGLU of the first `n_sample_experts` routed experts over
+    their routed rows; the shared experts over T/8 tokens. Per-forward time =
+    t_route + t_sample * N_r / n_sample + t_shared * 8.
+    """
+    import numpy as np
+    from oracle import ffn, numerics as nx, routing
+    from workloads import gen
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        cores = max((i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"), default=1)
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in info if i.get("user_api") == "blas"}))
+    except Exception:
+        cores, blas = len(os.sched_getaffinity(0)), "?"
+    u = gen.tokens(cfg, 0)
+    E = gen.centroids(cfg)
+    b = gen.bias_init(cfg)
+    sample = list(range(min(n_sample_experts, cfg.n_routed)))
+    w = {e: (gen.expert_w13(cfg, e), gen.expert_w2(cfg, e)) for e in sample}
+    ws = [(gen.shared_w13(cfg, s), gen.shared_w2(cfg, s)) for s in range(cfg.n_shared)]
+    wdt = "bf16" if cfg.expert_dtype == "bf16" else "f32"
+    t0 = time.perf_counter()
+    u64 = nx.to_f64(u, cfg.in_dtype)
+    r, s64, _ = routing.route_tokens(u64, nx.to_f64(E, cfg.router_dtype), b, cfg)
+    t_route = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    rows_done = 0
+    for e in sample:
+        rows, ks = np.nonzero(r.idx == e)
+        y = ffn.swiglu(u64[rows], nx.to_f64(w[e][0], wdt), nx.to_f64(w[e][1], wdt))
+        _ = r.gate[rows, ks][:, None] * y
+        rows_done += len(rows)
+    t_routed = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    Tsub = max(1, cfg.T // 8)
+    for s in range(cfg.n_shared):
+        ffn.swiglu(u64[:Tsub], nx.to_f64(ws[s][0], wdt), nx.to_f64(ws[s][1], wdt))
+    t_shared = time.perf_counter() - t0
+    per_fwd = t_route + t_routed * cfg.n_routed / len(sample) + t_shared * cfg.T / Tsub
+    log_fn("cpu oracle: route %.2fs, %d experts (%d rows) %.2fs, shared %d rows %.2fs -> %.1fs/forward"
+           % (t_route, len(sample), rows_done, t_routed, Tsub, t_shared, per_fwd))
+    return {"value": cfg.T / per_fwd, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": "one %d-token step: routing of all tokens; SwiGLU of experts 0..%d over their %d "
+                      "routed rows, scaled by %d/%d; shared expert over %d tokens, scaled by %d; fp64 numpy "
+                      "(BLAS %s); measured %.1f s of CPU work"
+                      % (cfg.T, len(sample) - 1, rows_done, cfg.n_routed, len(sample), Tsub,
+                         cfg.T // Tsub, blas, t_route + t_routed + t_shared)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="v3")
+    ap.add_argument("--T", type=int, default=0, help="override tokens per batch")
+    ap.add_argument("--cpu-sample-experts", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py measures one GPU only: this layer's hot path is built and timed on a single "
+                  "MI355X (the multi-GPU sharding is described, not run). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import expert_routing_router_amd as M
+    from expert_routing_router_amd.layer import MoELayer, np_to_device
+    from workloads import gen, get_config
+
+    cfg = get_config(args.config)
+    if args.T:
+        cfg = cfg.with_(T=args.T)
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    log("building %s layer (weights drawn and uploaded) ..." % cfg.name)
+    layer = MoELayer(cfg, gen, device="cuda:0")
+    log("layer ready in %.1fs" % (time.time() - t0))
+    nb = max(1, min(4, args.steps + args.warmup))
+    us = [np_to_device(gen.tokens(cfg, s), cfg.in_dtype, "cuda:0") for s in range(nb)]
+    b = np_to_device(gen.bias_init(cfg), "f32", "cuda:0")
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        layer.forward(us[i % nb], b, update_bias=True)
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    M.moe_profile_enable(True)
+    M.moe_profile_read(reset=True)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        layer.forward(us[i % nb], b, update_bias=True)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    stage_ms, calls = M.moe_profile_read(reset=True)
+    M.moe_profile_enable(False)
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = elapsed * 1000.0 / args.steps
+    tokens_per_s = cfg.T * args.steps / elapsed
+    log("timed %d steps: %.3f ms/step (events %.3f ms/step), %.0f tokens/s"
+        % (args.steps, ms_per_step, ev_ms / args.steps, tokens_per_s))
+
+    # load balance over a few extra (untimed) steps
+    loads = []
+    for i in range(min(4, nb)):
+        layer.forward(us[i % nb], b, update_bias=True)
+        c = layer.counts.float()
+        loads.append(float(c.max() / c.mean()))
+
+    alg = algorithmic(cfg)
+    peak_tf = PEAK_TFLOPS[cfg.expert_dtype]
+    kernels = {}
+    for name, a in alg.items():
+        ms = stage_ms.get(name, 0.0) / max(calls, 1)
+        if ms <= 0:
+            continue
+        k = {"ms": round(ms, 4), "GB/s": round(a["bytes"] / ms / 1e6, 1),
+             "hbm_frac": round(a["bytes"] / ms / 1e6 / PEAK_HBM_GBS, 4)}
+        if a["flops"]:
+            tf = a["flops"] / ms / 1e9
+            k["TFLOP/s"] = round(tf, 1)
+            k["mfma_frac"] = round(tf / (peak_tf if name.startswith("gemm") else PEAK_TFLOPS["bf16"]), 4)
+        kernels[name] = k
+    g_ms = (stage_ms["gemm1"] + stage_ms["gemm2"]) / max(calls, 1)
+    g_tf = (alg["gemm1"]["flops"] + alg["gemm2"]["flops"]) / g_ms / 1e9
+    kernels["grouped_gemm"] = {"ms": round(g_ms, 4), "TFLOP/s": round(g_tf, 1),
+                               "mfma_frac": round(g_tf / peak_tf, 4)}
+
+    g1 = alg["gemm1"]
+    g1_ms = stage_ms["gemm1"] / max(calls, 1)
+    achieved = g1["bytes"] / g1_ms / 1e6
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "gemm_%s_kernel (grouped gate/up GEMM + SwiGLU, routed + shared)" % cfg.expert_dtype,
+                "bytes_per_launch": g1["bytes"], "avg_ms": round(g1_ms, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del layer
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(cfg, args.cpu_sample_experts, log)
+
+    dtype = {"bf16": "bf16", "fp8": "fp8_e4m3", "f32": "f32"}[cfg.expert_dtype]
+    rec = {
+        "metric": "MoE-layer tokens/s (V3 shape: T=8192, d=7168, 256 routed experts top-8 in 8 groups / "
+                  "M=4, 1 shared, SwiGLU I=2048) + grouped-GEMM % MFMA peak",
+        "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": "%s: T=%d d=%d N_r=%d K=%d G=%d M=%d q=%d N_s=%d I=%d I_s=%d experts=%s "
+                               "router=%s; forward + bias update per step"
+                               % (cfg.name, cfg.T, cfg.d, cfg.n_routed, cfg.top_k, cfg.n_groups,
+                                  cfg.topk_groups, cfg.group_topk, cfg.n_shared, cfg.inter,
+                                  cfg.inter_shared, cfg.expert_dtype, cfg.router_dtype),
+                   "T": cfg.T, "d": cfg.d, "n_routed": cfg.n_routed, "top_k": cfg.top_k,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "grouped_gemm_mfma_frac": kernels["grouped_gemm"]["mfma_frac"],
+        "max_over_mean_load": [round(x, 3) for x in loads],
+        "event_ms_per_step": round(ev_ms / args.steps, 4),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

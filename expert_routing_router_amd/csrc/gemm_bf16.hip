@@ -1,0 +1,291 @@
+// Grouped expert GEMMs in bf16 on gfx950 MFMA (fp32 accumulation).
+//
+// The layer's expert FFNs (output equation of the DeepSeek-V3 guides,
+// "Metodo" section 2) run as two grouped GEMMs over the permuted rows:
+//   GEMM1 (swiglu): H[r, n] = SiLU(x_r . W1_e[n]) * (x_r . W3_e[n])
+//   GEMM2 (down):   Y[r, n] = H_r . W2_e[n]
+// for every row r of segment e. Segments are the routed experts followed by
+// the shared experts (their rows are every token, identity order).
+//
+// Tiling. A workgroup is 4 waves (2 along M x 2 along N) and owns one
+// (segment, n-tile, m-tile). The m-tile is 64*MB rows tall, sized on the host
+// so that one m-tile covers a typical expert's rows: each weight tile then
+// streams from HBM about once per forward. Waves take interleaved 32-row
+// m-blocks (wave wm: blocks wm, wm+2, ...) so a partly filled m-tile keeps
+// both M-waves equally busy; m-blocks past the segment's end skip their
+// MFMAs. B tiles are 128 weight rows: for GEMM1, 64 rows of W1 and the same
+// 64 rows of W3, so the gate and up accumulators of one output element sit in
+// the same lane and SwiGLU is applied in registers.
+//
+// Data path: global -> registers (prefetch of step k+1) -> LDS (double
+// buffer, 16-byte chunks XOR-swizzled by row so MFMA operand reads are
+// conflict-free) -> v_mfma_f32_32x32x16_bf16.
+#include "common.h"
+#include "moe_internal.h"
+#include <cmath>
+
+namespace moe {
+
+constexpr int GB_BK = 64;          // bf16 elements per K step (128 bytes per row)
+constexpr int GB_BN = 128;         // B rows per tile
+constexpr int GB_THREADS = 256;
+
+template <int MB>
+struct GemmLds {
+  static constexpr int BM = 64 * MB;
+  static constexpr int A_BYTES = BM * GB_BK * 2;
+  static constexpr int B_BYTES = GB_BN * GB_BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int BYTES = 2 * STAGE;
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+// Finds (segment, n-tile, m-tile) of logical tile L; tiles are ordered by
+// segment, then n-tile, then m-tile, so the m-tiles sharing one weight tile
+// are adjacent in dispatch order.
+__device__ __forceinline__ bool decode_tile(const int32_t* sprefix, int n_seg, int n_tiles, int L,
+                                            int& seg, int& nt, int& mt) {
+  const int total = sprefix[n_seg] * n_tiles;
+  if (L >= total) return false;
+  int lo = 0, hi = n_seg - 1;
+  while (lo < hi) {                       // largest seg with sprefix[seg]*n_tiles <= L
+    const int mid = (lo + hi + 1) >> 1;
+    if (sprefix[mid] * n_tiles <= L) lo = mid; else hi = mid - 1;
+  }
+  seg = lo;
+  const int local = L - sprefix[seg] * n_tiles;
+  const int mte = sprefix[seg + 1] - sprefix[seg];
+  nt = local / mte;
+  mt = local - nt * mte;
+  return true;
+}
+
+template <int MB, bool SWIGLU>
+__global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_kernel(GemmArgs a) {
+  using L = GemmLds<MB>;
+  constexpr int BM = L::BM;
+  constexpr int ACH = BM * 8 / GB_THREADS;     // A 16-byte chunks per thread (= 2*MB)
+  constexpr int BCH = GB_BN * 8 / GB_THREADS;  // B chunks per thread (= 4)
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int32_t sprefix[512];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  for (int i = tid; i <= a.n_seg; i += GB_THREADS) sprefix[i] = a.mtile_prefix[i];
+  __syncthreads();
+  const int n_tiles = SWIGLU ? a.N / 64 : a.N / GB_BN;
+  int seg, ntile, mtile;
+  if (!decode_tile(sprefix, a.n_seg, n_tiles, blockIdx.x, seg, ntile, mtile)) return;
+
+  const int seg_begin = a.offsets[seg], seg_end = a.offsets[seg + 1];
+  const int row0 = seg_begin + mtile * BM;
+  const int mvalid = min(BM, seg_end - row0);
+  const int K = a.K;
+  const uint16_t* wbase = seg < a.n_first
+      ? (const uint16_t*)a.w0 + (size_t)seg * a.wstride0
+      : (const uint16_t*)a.w1 + (size_t)(seg - a.n_first) * a.wstride1;
+  const uint16_t* x = (const uint16_t*)a.x;
+
+  // ---- per-thread global source offsets (element units), fixed over K
+  const int cch = tid & 7;          // 16-byte chunk within a 128-byte row slice
+  const int rbase = tid >> 3;       // 0..31
+  int aoff[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; i++) {
+    const int r = rbase + 32 * i;
+    if (r < mvalid) {
+      const int src = a.row_index ? a.row_index[row0 + r] : row0 + r;
+      aoff[i] = src * K + cch * 8;
+    } else {
+      aoff[i] = -1;
+    }
+  }
+  int boff[BCH];
+#pragma unroll
+  for (int i = 0; i < BCH; i++) {
+    const int br = rbase + 32 * i;   // 0..127
+    int wrow;
+    if (SWIGLU) wrow = br < 64 ? ntile * 64 + br : (a.N + ntile * 64 + (br - 64));
+    else wrow = ntile * GB_BN + br;
+    boff[i] = wrow * K + cch * 8;
+  }
+
+  i32x4 ra[ACH], rb[BCH];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < ACH; i++)
+      ra[i] = aoff[i] >= 0 ? *(const i32x4*)(x + aoff[i] + k0) : i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < BCH; i++) rb[i] = *(const i32x4*)(wbase + boff[i] + k0);
+  };
+  auto sstore = [&](int buf) {
+    uint8_t* A = lds + buf * L::STAGE;
+    uint8_t* B = A + L::A_BYTES;
+#pragma unroll
+    for (int i = 0; i < ACH; i++) *(i32x4*)(A + swz(rbase + 32 * i, cch)) = ra[i];
+#pragma unroll
+    for (int i = 0; i < BCH; i++) *(i32x4*)(B + swz(rbase + 32 * i, cch)) = rb[i];
+  };
+
+  f32x16 acc[MB][2];
+#pragma unroll
+  for (int i = 0; i < MB; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+  // active m-blocks of this wave (wave-uniform)
+  int mb_active = 0;
+#pragma unroll
+  for (int i = 0; i < MB; i++)
+    if ((2 * i + wm) * 32 < mvalid) mb_active = i + 1;
+
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int nk = K / GB_BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt++) {
+    if (kt + 1 < nk) gload((kt + 1) * GB_BK);
+    const uint8_t* A = lds + (kt & 1) * L::STAGE;
+    const uint8_t* B = A + L::A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      const int ch = ks * 2 + khalf;
+      bf16x8 bfr[2];
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int brow = (SWIGLU ? j * 64 + wn * 32 : wn * 64 + j * 32) + l32;
+        bfr[j] = *(const bf16x8*)(B + swz(brow, ch));
+      }
+#pragma unroll
+      for (int i = 0; i < MB; i++) {
+        if (i < mb_active) {
+          const int arow = (2 * i + wm) * 32 + l32;
+          const bf16x8 afr = *(const bf16x8*)(A + swz(arow, ch));
+          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[0], acc[i][0], 0, 0, 0);
+          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[1], acc[i][1], 0, 0, 0);
+        }
+      }
+    }
+    if (kt + 1 < nk) sstore((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: D element (8*(r>>2) + 4*(lane>>5) + (r&3), lane&31) in register r
+  uint16_t* out = (uint16_t*)a.out;
+#pragma unroll
+  for (int i = 0; i < MB; i++) {
+    if (i < mb_active) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+        if (row < mvalid) {
+          uint16_t* orow = out + (size_t)(row0 + row) * a.N;
+          if (SWIGLU) {
+            const int col = ntile * 64 + wn * 32 + l32;
+            orow[col] = f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
+          } else {
+            const int col = ntile * GB_BN + wn * 64 + l32;
+            orow[col] = f32_to_bf16(acc[i][0][r]);
+            orow[col + 32] = f32_to_bf16(acc[i][1][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 path
+// fp32 experts (the small fp32 layer): MI355X's fp32 vector rate equals its
+// fp32 matrix rate, so a plain VALU kernel is the fp32 path. One thread per
+// output element, fp32 FMA along K.
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
+  __shared__ int32_t soff[512];
+  for (int i = threadIdx.x; i <= a.n_seg; i += 256) soff[i] = a.offsets[i];
+  __syncthreads();
+  const int col = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (r >= soff[a.n_seg] || col >= a.N) return;
+  int lo = 0, hi = a.n_seg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (soff[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  const int seg = lo;
+  const float* w = seg < a.n_first ? (const float*)a.w0 + (size_t)seg * a.wstride0
+                                   : (const float*)a.w1 + (size_t)(seg - a.n_first) * a.wstride1;
+  const int src = a.row_index ? a.row_index[r] : r;
+  const float* xr = (const float*)a.x + (size_t)src * a.K;
+  float* out = (float*)a.out + (size_t)r * a.N + col;
+  if (SWIGLU) {
+    const float* w1 = w + (size_t)col * a.K;
+    const float* w3 = w + (size_t)(a.N + col) * a.K;
+    float g = 0.f, u = 0.f;
+    for (int k = 0; k < a.K; k++) {
+      g = fmaf(xr[k], w1[k], g);
+      u = fmaf(xr[k], w3[k], u);
+    }
+    *out = g / (1.0f + expf(-g)) * u;
+  } else {
+    const float* w2 = w + (size_t)col * a.K;
+    float y = 0.f;
+    for (int k = 0; k < a.K; k++) y = fmaf(xr[k], w2[k], y);
+    *out = y;
+  }
+}
+
+int gemm_bm(int dtype, int mean_rows) {
+  (void)dtype;
+  // one m-tile per expert when the mean load (+4 sigma of a binomial load) fits
+  const int need = mean_rows + 4 * (int)std::sqrt((double)(mean_rows > 0 ? mean_rows : 1));
+  if (need <= 256) return 256;
+  return 320;
+}
+
+template <int MB, bool SWIGLU>
+static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
+  const int n_tiles = SWIGLU ? a.N / 64 : a.N / GB_BN;
+  const long mtiles_bound = (long)a.rows_bound / (64 * MB) + a.n_seg;
+  const long grid = mtiles_bound * n_tiles;
+  if (grid <= 0) return hipSuccess;
+  auto k = gemm_bf16_kernel<MB, SWIGLU>;
+  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     GemmLds<MB>::BYTES);
+  if (e != hipSuccess) return e;
+  k<<<dim3((unsigned)grid), GB_THREADS, GemmLds<MB>::BYTES, s>>>(a);
+  return hipGetLastError();
+}
+
+template <bool SWIGLU>
+static hipError_t launch_any(const GemmArgs& a, int dtype, int bm, hipStream_t s) {
+  if (dtype == MOE_F32) {
+    const dim3 grid(cdiv(a.N, 64), cdiv(a.rows_bound, 4));
+    if (grid.y == 0) return hipSuccess;
+    gemm_f32_kernel<SWIGLU><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  if (dtype == MOE_BF16) {
+    if (bm == 256) return launch_bf16<4, SWIGLU>(a, s);
+    if (bm == 320) return launch_bf16<5, SWIGLU>(a, s);
+    return hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_fp8(const GemmArgs& a, bool swiglu, int bm, hipStream_t s);
+
+hipError_t launch_gemm_swiglu(const GemmArgs& a, int dtype, int bm, hipStream_t s) {
+  if (dtype == MOE_FP8_E4M3) return launch_gemm_fp8(a, true, bm, s);
+  return launch_any<true>(a, dtype, bm, s);
+}
+hipError_t launch_gemm_down(const GemmArgs& a, int dtype, int bm, hipStream_t s) {
+  if (dtype == MOE_FP8_E4M3) return launch_gemm_fp8(a, false, bm, s);
+  return launch_any<false>(a, dtype, bm, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,242 @@
+// Grouped expert GEMMs with E4M3 operands and fine-grained fp32 scales.
+//
+// The pages' FP8 recipe (DeepSeek-V3 guides on xyznot.com, FP8 key idea;
+// pwwt.cn note section 3): E4M3 inputs, one scale per 1x128 activation tile
+// and per 128x128 weight block, partial sums promoted to fp32 every 128
+// K-elements. On gfx950 the MFMA already accumulates in fp32, so the promotion
+// becomes: for every 128-wide K block, two v_mfma 32x32x64 f8f6f4 produce a
+// fresh fp32 partial, which is folded into the accumulator as
+//   acc += partial * (s_act[row, kb] * s_w[nblock, kb]).
+// The per-row activation scales of the tile are staged in LDS beside A.
+// Tiling, ragged segments and the SwiGLU epilogue follow the bf16 kernel.
+#include "common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int GF_BK = 128;        // fp8 elements (bytes) per K step = one scale block
+constexpr int GF_BN = 128;
+constexpr int GF_THREADS = 256;
+
+template <int MB>
+struct Fp8Lds {
+  static constexpr int BM = 64 * MB;
+  static constexpr int A_BYTES = BM * GF_BK;
+  static constexpr int B_BYTES = GF_BN * GF_BK;
+  static constexpr int SA_BYTES = BM * 4;
+  static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
+  static constexpr int BYTES = 2 * STAGE;
+};
+
+__device__ __forceinline__ int swz8(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ bool decode_tile8(const int32_t* sprefix, int n_seg, int n_tiles, int L,
+                                             int& seg, int& nt, int& mt) {
+  const int total = sprefix[n_seg] * n_tiles;
+  if (L >= total) return false;
+  int lo = 0, hi = n_seg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sprefix[mid] * n_tiles <= L) lo = mid; else hi = mid - 1;
+  }
+  seg = lo;
+  const int local = L - sprefix[seg] * n_tiles;
+  const int mte = sprefix[seg + 1] - sprefix[seg];
+  nt = local / mte;
+  mt = local - nt * mte;
+  return true;
+}
+
+template <int MB, bool SWIGLU>
+__global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
+  using L = Fp8Lds<MB>;
+  constexpr int BM = L::BM;
+  constexpr int ACH = BM * 8 / GF_THREADS;
+  constexpr int BCH = GF_BN * 8 / GF_THREADS;
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int32_t sprefix[512];
+  __shared__ int32_t srow[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  for (int i = tid; i <= a.n_seg; i += GF_THREADS) sprefix[i] = a.mtile_prefix[i];
+  __syncthreads();
+  const int n_tiles = SWIGLU ? a.N / 64 : a.N / GF_BN;
+  int seg, ntile, mtile;
+  if (!decode_tile8(sprefix, a.n_seg, n_tiles, blockIdx.x, seg, ntile, mtile)) return;
+
+  const int row0 = a.offsets[seg] + mtile * BM;
+  const int mvalid = min(BM, a.offsets[seg + 1] - row0);
+  const int K = a.K, KB = K / 128;
+  const bool first = seg < a.n_first;
+  const uint8_t* wbase = first ? (const uint8_t*)a.w0 + (size_t)seg * a.wstride0
+                               : (const uint8_t*)a.w1 + (size_t)(seg - a.n_first) * a.wstride1;
+  const float* wsc = first ? a.ws0 + (size_t)seg * a.sstride0 : a.ws1 + (size_t)(seg - a.n_first) * a.sstride1;
+  const uint8_t* x = (const uint8_t*)a.x;
+
+  for (int r = tid; r < BM; r += GF_THREADS)
+    srow[r] = r < mvalid ? (a.row_index ? a.row_index[row0 + r] : row0 + r) : -1;
+  __syncthreads();
+
+  const int cch = tid & 7, rbase = tid >> 3;
+  int aoff[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; i++) {
+    const int src = srow[rbase + 32 * i];
+    aoff[i] = src >= 0 ? src * K + cch * 16 : -1;
+  }
+  int boff[BCH];
+#pragma unroll
+  for (int i = 0; i < BCH; i++) {
+    const int br = rbase + 32 * i;
+    const int wrow = SWIGLU ? (br < 64 ? ntile * 64 + br : a.N + ntile * 64 + (br - 64)) : ntile * GF_BN + br;
+    boff[i] = wrow * K + cch * 16;
+  }
+  // weight block-row of each of this wave's two 32-row n-blocks
+  int wblk[2];
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int wrow = SWIGLU ? (j == 0 ? ntile * 64 + wn * 32 : a.N + ntile * 64 + wn * 32)
+                            : ntile * GF_BN + wn * 64 + j * 32;
+    wblk[j] = wrow / 128;
+  }
+
+  i32x4 ra[ACH], rb[BCH];
+  float rsa[2];
+  auto gload = [&](int kb) {
+    const int k0 = kb * GF_BK;
+#pragma unroll
+    for (int i = 0; i < ACH; i++)
+      ra[i] = aoff[i] >= 0 ? *(const i32x4*)(x + aoff[i] + k0) : i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < BCH; i++) rb[i] = *(const i32x4*)(wbase + boff[i] + k0);
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int r = tid + i * GF_THREADS;
+      rsa[i] = 0.f;
+      if (r < BM && srow[r] >= 0) rsa[i] = a.x_scale[(size_t)srow[r] * KB + kb];
+    }
+  };
+  auto sstore = [&](int buf) {
+    uint8_t* A = lds + buf * L::STAGE;
+    uint8_t* B = A + L::A_BYTES;
+    float* SA = (float*)(B + L::B_BYTES);
+#pragma unroll
+    for (int i = 0; i < ACH; i++) *(i32x4*)(A + swz8(rbase + 32 * i, cch)) = ra[i];
+#pragma unroll
+    for (int i = 0; i < BCH; i++) *(i32x4*)(B + swz8(rbase + 32 * i, cch)) = rb[i];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int r = tid + i * GF_THREADS;
+      if (r < BM) SA[r] = rsa[i];
+    }
+  };
+
+  f32x16 acc[MB][2];
+#pragma unroll
+  for (int i = 0; i < MB; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+  int mb_active = 0;
+#pragma unroll
+  for (int i = 0; i < MB; i++)
+    if ((2 * i + wm) * 32 < mvalid) mb_active = i + 1;
+
+  const int l32 = lane & 31, khalf = lane >> 5;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kb = 0; kb < KB; kb++) {
+    if (kb + 1 < KB) gload(kb + 1);
+    const uint8_t* A = lds + (kb & 1) * L::STAGE;
+    const uint8_t* B = A + L::A_BYTES;
+    const float* SA = (const float*)(B + L::B_BYTES);
+    const float sw0 = wsc[(size_t)wblk[0] * KB + kb];
+    const float sw1 = wsc[(size_t)wblk[1] * KB + kb];
+    i32x8 bfr[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int brow = (SWIGLU ? j * 64 + wn * 32 : wn * 64 + j * 32) + l32;
+        const int c0 = h * 4 + khalf * 2;
+        const i32x4 lo = *(const i32x4*)(B + swz8(brow, c0));
+        const i32x4 hi = *(const i32x4*)(B + swz8(brow, c0 + 1));
+        bfr[h][j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+    for (int i = 0; i < MB; i++) {
+      if (i < mb_active) {
+        const int arow = (2 * i + wm) * 32 + l32;
+        f32x16 p0, p1;
+#pragma unroll
+        for (int r = 0; r < 16; r++) { p0[r] = 0.f; p1[r] = 0.f; }
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const int c0 = h * 4 + khalf * 2;
+          const i32x4 lo = *(const i32x4*)(A + swz8(arow, c0));
+          const i32x4 hi = *(const i32x4*)(A + swz8(arow, c0 + 1));
+          const i32x8 afr = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          // cbsz = blgp = 0: both operands E4M3; scale exponents 127 = 2^0
+          p0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr, bfr[h][0], p0, 0, 0, 0, 127, 0, 127);
+          p1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr, bfr[h][1], p1, 0, 0, 0, 127, 0, 127);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+          const float sa = SA[row];
+          acc[i][0][r] += p0[r] * (sa * sw0);
+          acc[i][1][r] += p1[r] * (sa * sw1);
+        }
+      }
+    }
+    if (kb + 1 < KB) sstore((kb + 1) & 1);
+    __syncthreads();
+  }
+
+  // GEMM1 writes H in fp32 (it is re-quantised to E4M3 per 1x128 tile next);
+  // GEMM2 writes Y in bf16.
+#pragma unroll
+  for (int i = 0; i < MB; i++) {
+    if (i < mb_active) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+        if (row < mvalid) {
+          if (SWIGLU) {
+            float* orow = (float*)a.out + (size_t)(row0 + row) * a.N;
+            orow[ntile * 64 + wn * 32 + l32] = silu_mul(acc[i][0][r], acc[i][1][r]);
+          } else {
+            uint16_t* orow = (uint16_t*)a.out + (size_t)(row0 + row) * a.N;
+            const int col = ntile * GF_BN + wn * 64 + l32;
+            orow[col] = f32_to_bf16(acc[i][0][r]);
+            orow[col + 32] = f32_to_bf16(acc[i][1][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MB, bool SWIGLU>
+static hipError_t launch_fp8_t(const GemmArgs& a, hipStream_t s) {
+  const int n_tiles = SWIGLU ? a.N / 64 : a.N / GF_BN;
+  const long grid = ((long)a.rows_bound / (64 * MB) + a.n_seg) * n_tiles;
+  if (grid <= 0) return hipSuccess;
+  auto k = gemm_fp8_kernel<MB, SWIGLU>;
+  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     Fp8Lds<MB>::BYTES);
+  if (e != hipSuccess) return e;
+  k<<<dim3((unsigned)grid), GF_THREADS, Fp8Lds<MB>::BYTES, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(const GemmArgs& a, bool swiglu, int bm, hipStream_t s) {
+  if (bm == 256) return swiglu ? launch_fp8_t<4, true>(a, s) : launch_fp8_t<4, false>(a, s);
+  if (bm == 320) return swiglu ? launch_fp8_t<5, true>(a, s) : launch_fp8_t<5, false>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

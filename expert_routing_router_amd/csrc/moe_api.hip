@@ -1,0 +1,487 @@
+// C ABI of the MoE layer: argument validation (before anything is enqueued),
+// workspace layout, and the launch sequence of each call.
+#include <cmath>
+#include <cstring>
+#include "common.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+static thread_local int g_last_hip = 0;
+
+static int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip = (int)e;
+  return MOE_EHIP;
+}
+#define MOE_TRY(x)                           \
+  do {                                       \
+    hipError_t _e = (x);                     \
+    if (_e != hipSuccess) return hip_status(_e); \
+  } while (0)
+
+// ---------------------------------------------------------------- stage timing
+namespace {
+constexpr int kProfPool = 4096;
+struct Prof {
+  bool on = false;
+  hipEvent_t ev[kProfPool];
+  int stage[kProfPool];      // stage that ends at this event; -1 marks the start of a call
+  int used = 0;
+  int created = 0;
+  long calls = 0;
+} g_prof;
+
+void prof_mark(int stage, hipStream_t s) {
+  if (!g_prof.on || g_prof.used >= g_prof.created) return;
+  if (stage < 0 && g_prof.used + 2 * MOE_N_STAGES + 2 > g_prof.created) {
+    g_prof.created = g_prof.used;          // not enough room for a whole call: stop here
+    return;
+  }
+  if (stage < 0) g_prof.calls++;
+  g_prof.stage[g_prof.used] = stage;
+  (void)hipEventRecord(g_prof.ev[g_prof.used], s);
+  g_prof.used++;
+}
+}  // namespace
+
+extern "C" int moe_profile_enable(int on) {
+  if (on && !g_prof.created) {
+    for (int i = 0; i < kProfPool; i++) {
+      hipError_t e = hipEventCreate(&g_prof.ev[i]);
+      if (e != hipSuccess) { g_last_hip = (int)e; return MOE_EHIP; }
+    }
+    g_prof.created = kProfPool;
+  }
+  g_prof.on = on != 0;
+  return MOE_OK;
+}
+
+extern "C" int moe_profile_read(double* ms, int64_t* calls, int reset) {
+  if (!ms || !calls) return MOE_EINVAL;
+  for (int i = 0; i < MOE_N_STAGES; i++) ms[i] = 0.0;
+  if (g_prof.used > 0) {
+    hipError_t e = hipEventSynchronize(g_prof.ev[g_prof.used - 1]);
+    if (e != hipSuccess) { g_last_hip = (int)e; return MOE_EHIP; }
+  }
+  for (int i = 1; i < g_prof.used; i++) {
+    if (g_prof.stage[i] < 0) continue;
+    float t = 0.f;
+    hipError_t e = hipEventElapsedTime(&t, g_prof.ev[i - 1], g_prof.ev[i]);
+    if (e != hipSuccess) { g_last_hip = (int)e; return MOE_EHIP; }
+    ms[g_prof.stage[i]] += t;
+  }
+  *calls = g_prof.calls;
+  if (reset) {
+    g_prof.used = 0;
+    g_prof.calls = 0;
+    if (g_prof.created) g_prof.created = kProfPool;
+  }
+  return MOE_OK;
+}
+
+static bool aligned(const void* p) { return p && (((uintptr_t)p) & 15u) == 0; }
+static bool aligned_or_null(const void* p) { return !p || (((uintptr_t)p) & 15u) == 0; }
+static size_t esize(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+extern "C" int moe_abi_version(void) { return MOE_ABI_VERSION; }
+extern "C" int moe_last_hip_error(void) { return g_last_hip; }
+extern "C" const char* moe_strerror(int st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (dimension, NULL or misaligned pointer)";
+    case MOE_ENOTSUP: return "unsupported dtype or shape combination";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP runtime error (see moe_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int moe_validate(const moe_desc_t* d) {
+  if (!d || d->abi_version != MOE_ABI_VERSION) return MOE_EINVAL;
+  if (d->T < 0 || d->d < 8 || d->d % 8) return MOE_EINVAL;
+  if (d->n_routed < 1 || d->n_routed > 256) return MOE_EINVAL;
+  if (d->top_k < 1 || d->top_k > d->n_routed || d->top_k > 32) return MOE_EINVAL;
+  if (d->n_groups < 1 || d->n_groups > 64 || d->n_routed % d->n_groups) return MOE_EINVAL;
+  if (d->topk_groups < 1 || d->topk_groups > d->n_groups) return MOE_EINVAL;
+  const int S = d->n_routed / d->n_groups;
+  if (d->n_groups > 1) {
+    if (d->group_topk < 1 || d->group_topk > S || d->group_topk > 8) return MOE_EINVAL;
+    if (d->topk_groups * S < d->top_k) return MOE_EINVAL;
+  }
+  if (d->n_shared < 0 || d->n_shared > 64) return MOE_EINVAL;
+  if (d->inter < 1 || (d->n_shared > 0 && d->inter_shared < 1)) return MOE_EINVAL;
+  if (d->group_score_biased != 0 && d->group_score_biased != 1) return MOE_EINVAL;
+  if (!std::isfinite(d->gamma)) return MOE_EINVAL;
+  if (d->in_dtype != MOE_F32 && d->in_dtype != MOE_BF16) return MOE_ENOTSUP;
+  if (d->router_dtype != MOE_F32 && d->router_dtype != MOE_BF16) return MOE_ENOTSUP;
+  if (d->expert_dtype != MOE_F32 && d->expert_dtype != MOE_BF16 && d->expert_dtype != MOE_FP8_E4M3)
+    return MOE_ENOTSUP;
+  if (d->expert_dtype == MOE_F32 && d->in_dtype != MOE_F32) return MOE_ENOTSUP;
+  if (d->expert_dtype == MOE_BF16) {
+    if (d->in_dtype != MOE_BF16) return MOE_ENOTSUP;
+    if (d->d % 128 || d->inter % 64 || (d->n_shared && d->inter_shared % 64)) return MOE_ENOTSUP;
+  }
+  if (d->expert_dtype == MOE_FP8_E4M3) {
+    if (d->d % 128 || d->inter % 128 || (d->n_shared && d->inter_shared % 128)) return MOE_ENOTSUP;
+  }
+  const long rows = (long)d->T * d->top_k + (long)d->n_shared * d->T;
+  const long wide = d->d > d->inter ? d->d : d->inter;
+  const long wide2 = d->inter_shared > wide ? d->inter_shared : wide;
+  if (rows * wide2 >= (1L << 31) || (long)d->T * d->d >= (1L << 31)) return MOE_ENOTSUP;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- workspace layout
+struct Ws {
+  size_t idx, gate, counts, bitmap, wprefix, offsets, mtile, row_token, slot_row, H, Y;
+  size_t qu, su, qh, sh, offs_s, mtile_s, total;
+};
+
+static bool fused_shared(const moe_desc_t* d) { return d->n_shared == 0 || d->inter == d->inter_shared; }
+
+static Ws layout(const moe_desc_t* d) {
+  Ws w;
+  const size_t T = d->T, K = d->top_k, N = d->n_routed, Ns = d->n_shared;
+  const size_t W = (T + 63) / 64;
+  const size_t n_seg = N + Ns;
+  const size_t R = T * K + Ns * T;
+  const size_t Imax = d->inter > d->inter_shared || Ns == 0 ? d->inter : d->inter_shared;
+  const size_t hy = d->expert_dtype == MOE_BF16 ? 2 : 4;   // H: fp32 for F32 and FP8 experts
+  const size_t yy = d->expert_dtype == MOE_F32 ? 4 : 2;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += al256(bytes); return at; };
+  w.idx = take(T * K * 4);
+  w.gate = take(T * K * 4);
+  w.counts = take(N * 4);
+  w.bitmap = take(W * N * 8);
+  w.wprefix = take(W * N * 4);
+  w.offsets = take((n_seg + 1) * 4);
+  w.mtile = take((n_seg + 1) * 4);
+  w.row_token = take(R * 4);
+  w.slot_row = take(T * K * 4);
+  w.offs_s = take((Ns + 1) * 4);
+  w.mtile_s = take((Ns + 1) * 4);
+  w.H = take(R * Imax * hy);
+  w.Y = take(R * (size_t)d->d * yy);
+  if (d->expert_dtype == MOE_FP8_E4M3) {
+    w.qu = take(T * d->d);
+    w.su = take(T * (d->d / 128) * 4);
+    w.qh = take(R * Imax);
+    w.sh = take(R * (Imax / 128) * 4);
+  } else {
+    w.qu = w.su = w.qh = w.sh = 0;
+  }
+  w.total = o;
+  return w;
+}
+
+extern "C" size_t moe_workspace_bytes(const moe_desc_t* d) {
+  if (moe_validate(d) != MOE_OK) return 0;
+  return layout(d).total;
+}
+
+extern "C" size_t moe_expert_ffn_workspace_bytes(const moe_desc_t* d, int32_t n_experts, int32_t inter,
+                                                 int32_t rows) {
+  if (moe_validate(d) != MOE_OK || n_experts < 1 || inter < 1 || rows < 0) return 0;
+  const size_t hy = d->expert_dtype == MOE_BF16 ? 2 : 4;
+  size_t o = al256((size_t)(n_experts + 1) * 4);                 // m-tile prefix
+  o += al256((size_t)rows * inter * hy);                         // H
+  if (d->expert_dtype == MOE_FP8_E4M3) {
+    o += al256((size_t)rows * inter);                            // H codes
+    o += al256((size_t)rows * (inter / 128) * 4);                // H scales
+  }
+  return o;
+}
+
+static int route_front(const moe_desc_t* d) {
+  const bool mfma_ok = d->in_dtype == MOE_BF16 && d->n_routed % 16 == 0 && d->d % 32 == 0;
+  if (!mfma_ok) return kFrontF64;
+  return d->router_dtype == MOE_BF16 ? kFrontMfma : kFrontMfmaSplitE;
+}
+
+static RouteArgs route_args(const moe_desc_t* d, const void* u, const void* E, const float* b,
+                            const float* scores_in, float* scores_out, int32_t* idx, float* gate,
+                            int32_t* counts) {
+  RouteArgs a;
+  a.u = u; a.E = E; a.b = b; a.scores_in = scores_in; a.scores_out = scores_out;
+  a.idx = idx; a.gate = gate; a.counts = counts;
+  a.T = d->T; a.d = d->d; a.n_routed = d->n_routed; a.top_k = d->top_k;
+  a.n_groups = d->n_groups; a.topk_groups = d->topk_groups;
+  a.group_topk = d->n_groups > 1 ? d->group_topk : 1;
+  a.group_score_biased = d->group_score_biased;
+  a.in_dtype = d->in_dtype; a.router_dtype = d->router_dtype;
+  return a;
+}
+
+extern "C" int moe_route(const moe_desc_t* d, const void* u, const void* E, const float* b,
+                         const float* scores_in, float* scores_out, int32_t* topk_idx, float* topk_gate,
+                         int32_t* counts, moe_stream_t stream) {
+  int st = moe_validate(d);
+  if (st) return st;
+  const bool have_ue = u || E;
+  if (have_ue == (scores_in != nullptr)) return MOE_EINVAL;            // exactly one source
+  if (have_ue && (!aligned(u) || !aligned(E))) return MOE_EINVAL;
+  if (scores_in && !aligned(scores_in)) return MOE_EINVAL;
+  if (!aligned(b) || !aligned(topk_idx) || !aligned(topk_gate) || !aligned(counts)) return MOE_EINVAL;
+  if (!aligned_or_null(scores_out)) return MOE_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (d->T == 0) return hip_status(launch_fill_i32(counts, 0, d->n_routed, s));
+  RouteArgs a = route_args(d, u, E, b, scores_in, scores_out, topk_idx, topk_gate, counts);
+  return hip_status(launch_route(a, scores_in ? kFrontScoresIn : route_front(d), s));
+}
+
+extern "C" int moe_permute(const moe_desc_t* d, const int32_t* topk_idx, int32_t* offsets, int32_t* row_token,
+                           int32_t* slot_row, int32_t* counts, const void* u, void* x_perm, void* ws,
+                           size_t ws_bytes, moe_stream_t stream) {
+  int st = moe_validate(d);
+  if (st) return st;
+  if (!aligned(topk_idx) || !aligned(offsets) || !aligned(row_token) || !aligned(slot_row)) return MOE_EINVAL;
+  if (!aligned_or_null(counts) || !aligned_or_null(u) || !aligned_or_null(x_perm)) return MOE_EINVAL;
+  if ((u == nullptr) != (x_perm == nullptr)) return MOE_EINVAL;
+  if (!aligned(ws)) return MOE_EINVAL;
+  const Ws w = layout(d);
+  if (ws_bytes < w.total) return MOE_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* base = (uint8_t*)ws;
+  if (d->T == 0) {
+    MOE_TRY(launch_fill_i32(offsets, 0, d->n_routed + 1, s));
+    if (counts) MOE_TRY(launch_fill_i32(counts, 0, d->n_routed, s));
+    return MOE_OK;
+  }
+  PermuteArgs p;
+  p.idx = topk_idx; p.T = d->T; p.K = d->top_k; p.n_routed = d->n_routed;
+  p.bitmap = (uint64_t*)(base + w.bitmap); p.wprefix = (int32_t*)(base + w.wprefix);
+  p.counts_ws = (int32_t*)(base + w.counts);
+  p.offsets = offsets; p.row_token = row_token; p.slot_row = slot_row; p.counts_out = counts;
+  p.n_extra_seg = 0; p.mtile_prefix = nullptr; p.bm = 0;
+  MOE_TRY(launch_permute(p, s));
+  if (x_perm)
+    MOE_TRY(launch_gather_rows(u, row_token, x_perm, (long)d->T * d->top_k, d->d * (int)esize(d->in_dtype), s));
+  return MOE_OK;
+}
+
+static GemmArgs gemm_args(const void* x, const float* xs, const int32_t* ridx, const int32_t* offsets,
+                          const int32_t* mtile, int n_seg, const void* w0, const float* s0, long ws0,
+                          long ss0, void* out, int N, int K, int rows_bound) {
+  GemmArgs g;
+  g.x = x; g.x_scale = xs; g.row_index = ridx; g.offsets = offsets; g.mtile_prefix = mtile;
+  g.n_seg = n_seg; g.w0 = w0; g.w1 = w0; g.wstride0 = ws0; g.wstride1 = ws0;
+  g.ws0 = s0; g.ws1 = s0; g.sstride0 = ss0; g.sstride1 = ss0; g.n_first = n_seg;
+  g.out = out; g.N = N; g.K = K; g.rows_bound = rows_bound;
+  return g;
+}
+
+// GEMM1 + (FP8: quantise H) + GEMM2 over one set of segments.
+static int run_ffn(const moe_desc_t* d, int inter, const void* x, const float* xs, const int32_t* ridx,
+                   const int32_t* offsets, const int32_t* mtile, int n_seg, int rows_bound,
+                   const void* w13, const float* s13, const void* w13b, const float* s13b,
+                   const void* w2, const float* s2, const void* w2b, const float* s2b, int n_first,
+                   void* H, uint8_t* qh, float* sh, void* Y, int bm, hipStream_t s) {
+  const int dt = d->expert_dtype;
+  const bool f8 = dt == MOE_FP8_E4M3;
+  const long ws13 = 2L * inter * d->d, ws2 = (long)d->d * inter;
+  const long ss13 = f8 ? (2L * inter / 128) * (d->d / 128) : 0, ss2 = f8 ? (long)(d->d / 128) * (inter / 128) : 0;
+  GemmArgs g1 = gemm_args(x, xs, ridx, offsets, mtile, n_seg, w13, s13, ws13, ss13, H, inter, d->d, rows_bound);
+  g1.w1 = w13b; g1.ws1 = s13b; g1.n_first = n_first;
+  MOE_TRY(launch_gemm_swiglu(g1, dt, bm, s));
+  prof_mark(MOE_STAGE_GEMM1, s);
+  const void* x2 = H;
+  const float* xs2 = nullptr;
+  if (f8) {
+    MOE_TRY(launch_quant_act(H, MOE_F32, rows_bound, inter, nullptr, qh, sh, s));
+    x2 = qh;
+    xs2 = sh;
+  }
+  GemmArgs g2 = gemm_args(x2, xs2, nullptr, offsets, mtile, n_seg, w2, s2, ws2, ss2, Y, d->d, inter, rows_bound);
+  g2.w1 = w2b; g2.ws1 = s2b; g2.n_first = n_first;
+  MOE_TRY(launch_gemm_down(g2, dt, bm, s));
+  prof_mark(MOE_STAGE_GEMM2, s);
+  return MOE_OK;
+}
+
+extern "C" int moe_expert_ffn(const moe_desc_t* d, int32_t n_experts, int32_t inter, int32_t rows,
+                              const void* x, const float* x_scale, const int32_t* row_token,
+                              const int32_t* offsets, const void* w13, const float* w13_scale,
+                              const void* w2, const float* w2_scale, void* y, void* ws, size_t ws_bytes,
+                              moe_stream_t stream) {
+  int st = moe_validate(d);
+  if (st) return st;
+  if (n_experts < 1 || n_experts > 320 || inter < 1 || rows < 0) return MOE_EINVAL;
+  const bool f8 = d->expert_dtype == MOE_FP8_E4M3;
+  if (d->expert_dtype == MOE_BF16 && inter % 64) return MOE_ENOTSUP;
+  if (f8 && inter % 128) return MOE_ENOTSUP;
+  if ((long)rows * (d->d > inter ? d->d : inter) >= (1L << 31)) return MOE_ENOTSUP;
+  if (!aligned(x) || !aligned(offsets) || !aligned(w13) || !aligned(w2) || !aligned(y) || !aligned(ws))
+    return MOE_EINVAL;
+  if (!aligned_or_null(row_token)) return MOE_EINVAL;
+  if (f8 && (!aligned(x_scale) || !aligned(w13_scale) || !aligned(w2_scale))) return MOE_EINVAL;
+  if (ws_bytes < moe_expert_ffn_workspace_bytes(d, n_experts, inter, rows)) return MOE_EWORKSPACE;
+  if (rows == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t hy = d->expert_dtype == MOE_BF16 ? 2 : 4;
+  uint8_t* base = (uint8_t*)ws;
+  int32_t* mtile = (int32_t*)base;
+  size_t o = al256((size_t)(n_experts + 1) * 4);
+  void* H = base + o;
+  o += al256((size_t)rows * inter * hy);
+  uint8_t* qh = f8 ? base + o : nullptr;
+  if (f8) o += al256((size_t)rows * inter);
+  float* sh = f8 ? (float*)(base + o) : nullptr;
+  const int bm = gemm_bm(d->expert_dtype, rows / n_experts);
+  if (d->expert_dtype != MOE_F32) MOE_TRY(launch_mtile_prefix(offsets, n_experts, bm, mtile, s));
+  return run_ffn(d, inter, x, x_scale, row_token, offsets, mtile, n_experts, rows, w13, w13_scale, w13,
+                 w13_scale, w2, w2_scale, w2, w2_scale, n_experts, H, qh, sh, y, bm, s);
+}
+
+extern "C" int moe_combine(const moe_desc_t* d, const void* u, const void* y, const void* y_shared,
+                           const int32_t* slot_row, const float* topk_gate, void* out, moe_stream_t stream) {
+  int st = moe_validate(d);
+  if (st) return st;
+  if (!aligned(u) || !aligned(y) || !aligned(slot_row) || !aligned(topk_gate) || !aligned(out)) return MOE_EINVAL;
+  if (d->n_shared > 0 ? !aligned(y_shared) : !aligned_or_null(y_shared)) return MOE_EINVAL;
+  CombineArgs c;
+  c.u = u; c.y = y; c.y_shared = y_shared; c.slot_row = slot_row; c.gate = topk_gate; c.out = out;
+  c.T = d->T; c.d = d->d; c.K = d->top_k; c.n_shared = y_shared ? d->n_shared : 0; c.shared_stride = d->T;
+  c.io_dtype = d->in_dtype; c.y_dtype = d->expert_dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
+  return hip_status(launch_combine(c, (hipStream_t)stream));
+}
+
+extern "C" int moe_update_bias(const moe_desc_t* d, const int32_t* counts, float* b, moe_stream_t stream) {
+  int st = moe_validate(d);
+  if (st) return st;
+  if (!aligned(counts) || !aligned(b)) return MOE_EINVAL;
+  return hip_status(launch_update_bias(counts, b, d->n_routed, (long)d->T * d->top_k, d->gamma,
+                                       (hipStream_t)stream));
+}
+
+__global__ void iota_kernel(int32_t* p, int n, int step) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i <= n) p[i] = i * step;
+}
+
+extern "C" int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* u, float* b, void* out,
+                           moe_route_out_t* dbg, int32_t update_bias, void* ws, size_t ws_bytes,
+                           moe_stream_t stream) {
+  int st = moe_validate(d);
+  if (st) return st;
+  if (!w || !aligned(u) || !aligned(b) || !aligned(out) || !aligned(ws)) return MOE_EINVAL;
+  if (!aligned(w->centroids) || !aligned(w->w13) || !aligned(w->w2)) return MOE_EINVAL;
+  const bool f8 = d->expert_dtype == MOE_FP8_E4M3;
+  if (d->n_shared > 0) {
+    if (!aligned(w->w13_shared) || !aligned(w->w2_shared)) return MOE_EINVAL;
+    if (f8 && (!aligned(w->w13_shared_scale) || !aligned(w->w2_shared_scale))) return MOE_EINVAL;
+  }
+  if (f8 && (!aligned(w->w13_scale) || !aligned(w->w2_scale))) return MOE_EINVAL;
+  if (dbg && (!aligned_or_null(dbg->topk_idx) || !aligned_or_null(dbg->topk_gate) ||
+              !aligned_or_null(dbg->counts)))
+    return MOE_EINVAL;
+  const Ws L = layout(d);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (d->T == 0) {
+    if (dbg && dbg->counts) MOE_TRY(launch_fill_i32(dbg->counts, 0, d->n_routed, s));
+    return MOE_OK;
+  }
+  uint8_t* base = (uint8_t*)ws;
+  const int T = d->T, K = d->top_k, N = d->n_routed, Ns = d->n_shared;
+  int32_t* idx = dbg && dbg->topk_idx ? dbg->topk_idx : (int32_t*)(base + L.idx);
+  float* gate = dbg && dbg->topk_gate ? dbg->topk_gate : (float*)(base + L.gate);
+  int32_t* counts = dbg && dbg->counts ? dbg->counts : (int32_t*)(base + L.counts);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* mtile = (int32_t*)(base + L.mtile);
+  int32_t* row_token = (int32_t*)(base + L.row_token);
+  int32_t* slot_row = (int32_t*)(base + L.slot_row);
+  const size_t hy = d->expert_dtype == MOE_BF16 ? 2 : 4;
+  const size_t yy = d->expert_dtype == MOE_F32 ? 4 : 2;
+  uint8_t* H = base + L.H;
+  uint8_t* Y = base + L.Y;
+
+  // 1. router
+  prof_mark(-1, s);
+  RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, nullptr, idx, gate, counts);
+  MOE_TRY(launch_route(ra, route_front(d), s));
+  prof_mark(MOE_STAGE_ROUTE, s);
+
+  // 2. dispatch layout; shared experts become extra identity segments
+  const bool fused = fused_shared(d);
+  const long TK = (long)T * K;
+  const int bm = gemm_bm(d->expert_dtype, (int)(TK / N));
+  PermuteArgs p;
+  p.idx = idx; p.T = T; p.K = K; p.n_routed = N;
+  p.bitmap = (uint64_t*)(base + L.bitmap); p.wprefix = (int32_t*)(base + L.wprefix);
+  p.counts_ws = nullptr; p.offsets = offsets; p.row_token = row_token; p.slot_row = slot_row;
+  p.counts_out = nullptr; p.n_extra_seg = Ns;
+  p.mtile_prefix = d->expert_dtype == MOE_F32 ? nullptr : mtile;
+  p.bm = bm;
+  MOE_TRY(launch_permute(p, s));
+  prof_mark(MOE_STAGE_PERMUTE, s);
+
+  // 3. FP8: quantise u once per 1x128 tile
+  const void* x = u;
+  const float* xs = nullptr;
+  if (f8) {
+    MOE_TRY(launch_quant_act(u, d->in_dtype, T, d->d, nullptr, base + L.qu, (float*)(base + L.su), s));
+    x = base + L.qu;
+    xs = (const float*)(base + L.su);
+    prof_mark(MOE_STAGE_QUANT_X, s);
+  }
+  uint8_t* qh = f8 ? base + L.qh : nullptr;
+  float* shs = f8 ? (float*)(base + L.sh) : nullptr;
+
+  // 4. experts
+  const void* y_shared = nullptr;
+  if (fused) {
+    int st2 = run_ffn(d, d->inter, x, xs, row_token, offsets, mtile, N + Ns, (int)(TK + (long)Ns * T),
+                      w->w13, w->w13_scale, Ns ? w->w13_shared : w->w13, Ns ? w->w13_shared_scale : w->w13_scale,
+                      w->w2, w->w2_scale, Ns ? w->w2_shared : w->w2, Ns ? w->w2_shared_scale : w->w2_scale, N,
+                      H, qh, shs, Y, bm, s);
+    if (st2) return st2;
+    if (Ns) y_shared = Y + (size_t)TK * d->d * yy;
+  } else {
+    int st2 = run_ffn(d, d->inter, x, xs, row_token, offsets, mtile, N, (int)TK, w->w13, w->w13_scale, w->w13,
+                      w->w13_scale, w->w2, w->w2_scale, w->w2, w->w2_scale, N, H, qh, shs, Y, bm, s);
+    if (st2) return st2;
+    int32_t* offs_s = (int32_t*)(base + L.offs_s);
+    int32_t* mtile_s = (int32_t*)(base + L.mtile_s);
+    iota_kernel<<<cdiv(Ns + 1, 64), 64, 0, s>>>(offs_s, Ns, T);
+    MOE_TRY(hipGetLastError());
+    const int bms = gemm_bm(d->expert_dtype, T);
+    if (d->expert_dtype != MOE_F32) MOE_TRY(launch_mtile_prefix(offs_s, Ns, bms, mtile_s, s));
+    uint8_t* Hs = H + (size_t)TK * (d->inter > d->inter_shared ? d->inter : d->inter_shared) * hy;
+    uint8_t* Ys = Y + (size_t)TK * d->d * yy;
+    uint8_t* qhs = f8 ? qh + (size_t)TK * d->inter : nullptr;
+    float* shss = f8 ? shs + (size_t)TK * (d->inter / 128) : nullptr;
+    st2 = run_ffn(d, d->inter_shared, x, xs, row_token + TK, offs_s, mtile_s, Ns, Ns * T, w->w13_shared,
+                  w->w13_shared_scale, w->w13_shared, w->w13_shared_scale, w->w2_shared, w->w2_shared_scale,
+                  w->w2_shared, w->w2_shared_scale, Ns, Hs, qhs, shss, Ys, bms, s);
+    if (st2) return st2;
+    y_shared = Ys;
+  }
+
+  // 5. combine
+  CombineArgs c;
+  c.u = u; c.y = Y; c.y_shared = y_shared; c.slot_row = slot_row; c.gate = gate; c.out = out;
+  c.T = T; c.d = d->d; c.K = K; c.n_shared = Ns; c.shared_stride = T;
+  c.io_dtype = d->in_dtype; c.y_dtype = d->expert_dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
+  MOE_TRY(launch_combine(c, s));
+  prof_mark(MOE_STAGE_COMBINE, s);
+
+  // 6. end-of-step bias update from this batch's loads
+  if (update_bias) MOE_TRY(launch_update_bias(counts, b, N, TK, d->gamma, s));
+  prof_mark(MOE_STAGE_BIAS, s);
+  return MOE_OK;
+}
+
+extern "C" int moe_quantize_fp8(int32_t kind, const void* src, int32_t src_dtype, int32_t rows, int32_t cols,
+                                uint8_t* q, float* scale, moe_stream_t stream) {
+  if (kind != MOE_QUANT_ACT_1x128 && kind != MOE_QUANT_W_128x128) return MOE_EINVAL;
+  if (src_dtype != MOE_F32 && src_dtype != MOE_BF16) return MOE_ENOTSUP;
+  if (rows < 0 || cols < 128 || cols % 128) return MOE_EINVAL;
+  if (kind == MOE_QUANT_W_128x128 && rows % 128) return MOE_EINVAL;
+  if (!aligned(src) || !aligned(q) || !aligned(scale)) return MOE_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (kind == MOE_QUANT_ACT_1x128) return hip_status(launch_quant_act(src, src_dtype, rows, cols, nullptr, q, scale, s));
+  return hip_status(launch_quant_w(src, src_dtype, rows, cols, q, scale, s));
+}

@@ -1,0 +1,75 @@
+// Internal launch interface between the C ABI (moe_api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "../../include/moe_rocm.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- router
+enum RouterFront { kFrontScoresIn = 0, kFrontMfma = 1, kFrontMfmaSplitE = 2, kFrontF64 = 3 };
+struct RouteArgs {
+  const void* u; const void* E; const float* b; const float* scores_in;
+  float* scores_out; int32_t* idx; float* gate; int32_t* counts;
+  int T, d, n_routed, top_k, n_groups, topk_groups, group_topk, group_score_biased;
+  int in_dtype, router_dtype;
+};
+hipError_t launch_route(const RouteArgs& a, int front, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, long n, hipStream_t s);
+
+// ---------------------------------------------------------------- permute
+// Workspace pieces: bitmap [N_r][W] u64 (W = ceil(T/64)), wprefix [N_r][W] i32.
+struct PermuteArgs {
+  const int32_t* idx; int T, K, n_routed;
+  uint64_t* bitmap; int32_t* wprefix; int32_t* counts_ws;   // counts_ws [N_r] scratch
+  int32_t* offsets;       // [n_seg+1], n_seg = n_routed + n_extra_seg
+  int32_t* row_token;     // [T*K + n_extra_seg*T]
+  int32_t* slot_row;      // [T*K]
+  int32_t* counts_out;    // nullable [N_r]
+  int n_extra_seg;        // shared-expert segments appended after the routed rows (identity rows)
+  int32_t* mtile_prefix;  // nullable [n_seg+1]: prefix of ceil(n_e/bm)
+  int bm;
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+hipError_t launch_gather_rows(const void* src, const int32_t* row_token, void* dst,
+                              long rows, int row_bytes, hipStream_t s);
+hipError_t launch_mtile_prefix(const int32_t* offsets, int n_seg, int bm, int32_t* out,
+                               hipStream_t s);
+
+// ---------------------------------------------------------------- grouped GEMMs
+// Segment e uses weights (e < n_first ? w0 + e*stride0 : w1 + (e-n_first)*stride1).
+struct GemmArgs {
+  const void* x;              // A source rows (through row_index when not null)
+  const float* x_scale;       // FP8: [.., K/128] per source row
+  const int32_t* row_index;   // nullable
+  const int32_t* offsets;     // [n_seg+1]
+  const int32_t* mtile_prefix;// [n_seg+1]
+  int n_seg;
+  const void* w0; const void* w1; long wstride0, wstride1;       // elements
+  const float* ws0; const float* ws1; long sstride0, sstride1;   // FP8 block scales
+  int n_first;
+  void* out;                  // [rows, N]
+  int N;                      // output columns (I for the SwiGLU GEMM, d for down)
+  int K;                      // reduction length
+  int rows_bound;             // upper bound on total rows (grid sizing)
+};
+int gemm_bm(int dtype, int mean_rows);
+hipError_t launch_gemm_swiglu(const GemmArgs& a, int dtype, int bm, hipStream_t s);
+hipError_t launch_gemm_down(const GemmArgs& a, int dtype, int bm, hipStream_t s);
+
+// ---------------------------------------------------------------- combine / bias / quant
+struct CombineArgs {
+  const void* u; const void* y; const void* y_shared; const int32_t* slot_row;
+  const float* gate; void* out; int T, d, K, n_shared; long shared_stride;  // rows
+  int io_dtype;   // MOE_F32 or MOE_BF16 (u/out)
+  int y_dtype;    // MOE_F32 or MOE_BF16
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_update_bias(const int32_t* counts, float* b, int n_routed, long total,
+                              float gamma, hipStream_t s);
+hipError_t launch_quant_act(const void* src, int src_dtype, long rows, int cols,
+                            const int32_t* row_index, uint8_t* q, float* scale, hipStream_t s);
+hipError_t launch_quant_w(const void* src, int src_dtype, long rows, int cols, uint8_t* q,
+                          float* scale, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,151 @@
+// Dispatch layout on one GPU: per-expert loads, exclusive scan, and a stable
+// token permutation with no capacity limit.
+//
+// The pwwt.cn note (section 4) describes dispatch as sending each token to the
+// devices that hold its experts and combine as the gated sum on the home
+// device; on one GPU the same step is a permutation that groups the T*K
+// (token, expert) rows by expert. No row is ever dropped (note section 1.4).
+//
+// Construction (deterministic, no float atomics, no sort):
+//   1. bitmap[w][e]: bit j set when token 64*w + j picked expert e
+//      (one wave per 64 tokens, OR-ed in LDS, written coalesced over e);
+//   2. per expert, the running popcount over words gives wprefix[w][e] and
+//      the load c_e; an exclusive scan over experts gives offsets;
+//   3. row of (t, k) = offsets[e] + wprefix[t/64][e] + popcount of the bits of
+//      tokens below t in t's word -- rows of an expert are in token order.
+#include "common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int PM_NMAX = 256;
+
+__global__ __launch_bounds__(256) void bitmap_kernel(const int32_t* __restrict__ idx, int T, int K,
+                                                     int N, uint64_t* __restrict__ bitmap) {
+  __shared__ uint64_t words[4][PM_NMAX];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = lane; e < N; e += 64) words[wave][e] = 0ull;
+  __syncthreads();
+  const int w = blockIdx.x * 4 + wave;
+  const int t = w * 64 + lane;
+  if (t < T)
+    for (int k = 0; k < K; k++)
+      atomicOr((unsigned long long*)&words[wave][idx[(size_t)t * K + k]], 1ull << lane);
+  __syncthreads();
+  const int W = cdiv(T, 64);
+  if (w < W)
+    for (int e = lane; e < N; e += 64) bitmap[(size_t)w * N + e] = words[wave][e];
+}
+
+// One workgroup: per-expert word prefix, loads, offsets (+ identity segments
+// for the shared experts appended after the routed rows), m-tile prefix.
+__global__ __launch_bounds__(256) void scan_kernel(const uint64_t* __restrict__ bitmap, int T, int K,
+                                                   int N, int n_extra, int32_t* __restrict__ wprefix,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ counts_out,
+                                                   int32_t* __restrict__ mtile_prefix, int bm) {
+  __shared__ int32_t sc[PM_NMAX + 64];
+  __shared__ int32_t sm[PM_NMAX + 64];
+  const int tid = threadIdx.x;
+  const int W = cdiv(T, 64);
+  const int n_seg = N + n_extra;
+  int c = 0;
+  if (tid < N) {
+    for (int w = 0; w < W; w++) {
+      wprefix[(size_t)w * N + tid] = c;
+      c += __popcll(bitmap[(size_t)w * N + tid]);
+    }
+    if (counts_out) counts_out[tid] = c;
+  }
+  for (int e = tid; e < n_seg; e += 256) {
+    const int n = e < N ? (e == tid ? c : 0) : T;
+    sc[e] = n;
+    sm[e] = bm > 0 ? cdiv(n, bm) : 0;
+  }
+  __syncthreads();
+  if (tid == 0) {   // n_seg <= 320: a serial scan is cheaper than a tree here
+    int acc = 0, accm = 0;
+    for (int e = 0; e < n_seg; e++) {
+      const int n = sc[e], m = sm[e];
+      offsets[e] = acc;
+      if (mtile_prefix) mtile_prefix[e] = accm;
+      acc += n;
+      accm += m;
+    }
+    offsets[n_seg] = acc;
+    if (mtile_prefix) mtile_prefix[n_seg] = accm;
+  }
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ idx, int T, int K,
+                                                      int N, int n_extra,
+                                                      const uint64_t* __restrict__ bitmap,
+                                                      const int32_t* __restrict__ wprefix,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ row_token,
+                                                      int32_t* __restrict__ slot_row) {
+  const long TK = (long)T * K;
+  const long total = TK + (long)n_extra * T;
+  for (long p = (long)blockIdx.x * blockDim.x + threadIdx.x; p < total; p += (long)gridDim.x * blockDim.x) {
+    if (p < TK) {
+      const int t = (int)(p / K);
+      const int e = idx[p];
+      const int w = t >> 6, bit = t & 63;
+      const uint64_t word = bitmap[(size_t)w * N + e];
+      const int below = __popcll(word & ((1ull << bit) - 1ull));
+      const int r = offsets[e] + wprefix[(size_t)w * N + e] + below;
+      row_token[r] = t;
+      slot_row[p] = r;
+    } else {
+      row_token[p] = (int)((p - TK) % T);   // shared experts: every token, in order
+    }
+  }
+}
+
+__global__ void mtile_prefix_kernel(const int32_t* __restrict__ offsets, int n_seg, int bm,
+                                    int32_t* __restrict__ out) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    int acc = 0;
+    for (int e = 0; e < n_seg; e++) {
+      out[e] = acc;
+      acc += cdiv(offsets[e + 1] - offsets[e], bm);
+    }
+    out[n_seg] = acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ src,
+                                                          const int32_t* __restrict__ row_token,
+                                                          uint8_t* __restrict__ dst, int row_bytes) {
+  const long r = blockIdx.x;
+  const uint8_t* s = src + (size_t)row_token[r] * row_bytes;
+  uint8_t* d = dst + (size_t)r * row_bytes;
+  for (int c = threadIdx.x * 16; c < row_bytes; c += blockDim.x * 16)
+    *(i32x4*)(d + c) = *(const i32x4*)(s + c);
+}
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+  const int W = cdiv(a.T, 64);
+  bitmap_kernel<<<cdiv(W, 4), 256, 0, s>>>(a.idx, a.T, a.K, a.n_routed, a.bitmap);
+  scan_kernel<<<1, 256, 0, s>>>(a.bitmap, a.T, a.K, a.n_routed, a.n_extra_seg, a.wprefix, a.offsets,
+                                a.counts_out, a.mtile_prefix, a.bm);
+  const long total = (long)a.T * a.K + (long)a.n_extra_seg * a.T;
+  const int blocks = (int)std::min<long>(cdiv<long>(total, 256), 2048);
+  scatter_kernel<<<blocks, 256, 0, s>>>(a.idx, a.T, a.K, a.n_routed, a.n_extra_seg, a.bitmap,
+                                        a.wprefix, a.offsets, a.row_token, a.slot_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_mtile_prefix(const int32_t* offsets, int n_seg, int bm, int32_t* out, hipStream_t s) {
+  mtile_prefix_kernel<<<1, 64, 0, s>>>(offsets, n_seg, bm, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* src, const int32_t* row_token, void* dst, long rows,
+                              int row_bytes, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  gather_rows_kernel<<<(unsigned)rows, 256, 0, s>>>((const uint8_t*)src, row_token, (uint8_t*)dst, row_bytes);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,289 @@
+// Router of the DeepSeekMoE layer on gfx950: affinities, biased group-limited
+// top-K, normalised gates and per-expert loads, fused in one kernel.
+//
+//   s_{i,t} = sigmoid(u_t . e_i)       -- DeepSeek-V3 Technical Report guides
+//                                         (xyznot.com), "Metodo" section 2
+//   top-K_r on s + b, gates from s      -- same section, gating equation; the
+//                                         pwwt.cn note 1.1.2 (bias only routes)
+//   groups ranked by the sum of their   -- pwwt.cn note 1.3 (node-limited
+//   top K_r/M scores, at most M kept       routing; nodes = expert groups here)
+//
+// One workgroup (4 waves) owns 32 tokens and every expert. The front end
+// writes the fp32 affinities of its tokens into LDS; the selection back end is
+// one code path whatever the front end was (MFMA logits, fp64 logits, or
+// affinities handed in by the caller), so the scores-in mode exercises exactly
+// the production selection.
+//
+// Precision: the MFMA front end accumulates bf16 products (exact in fp32) in
+// fp32 over 512-element chunks of d and sums the chunks in fp64; the sigmoid
+// is evaluated in fp64 and rounded once to fp32. fp32 centroids are split into
+// three bf16 terms (hi + mid + lo reproduces the fp32 value exactly), so the
+// products stay exact on the bf16 MFMA path.
+#include "common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int RT_BT = 32;
+constexpr int RT_THREADS = 256;
+constexpr int RT_NMAX = 256;
+constexpr int RT_CHUNK = 512;
+constexpr int RT_QMAX = 8;
+
+struct RouterLds {
+  float s[RT_BT][RT_NMAX];
+  float b[RT_NMAX];
+  int cnt[RT_NMAX];
+};
+
+__device__ __forceinline__ double sigmoid64(double z) {
+  if (z >= 0.0) return 1.0 / (1.0 + exp(-z));
+  double ez = exp(z);
+  return ez / (1.0 + ez);
+}
+
+union V16 { i32x4 i; bf16x8 h; uint16_t s[8]; };
+
+__device__ __forceinline__ void split3(const float* x, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+  V16 a, b, c;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    float v = x[i];
+    uint16_t h = f32_to_bf16(v);
+    float r1 = v - bf16_to_f32(h);          // exact
+    uint16_t m = f32_to_bf16(r1);
+    float r2 = r1 - bf16_to_f32(m);         // exact
+    a.s[i] = h; b.s[i] = m; c.s[i] = f32_to_bf16(r2);
+  }
+  hi = a.h; mid = b.h; lo = c.h;
+}
+
+// ---------------------------------------------------------------- front ends
+// MFMA 16x16x32 bf16: lane l holds A row (l&15), B column (l&15), 8 k-values
+// at k-group (l>>4); D element (4*(l>>4)+r, l&15) in register r.
+template <bool SPLIT_E>
+__device__ void front_mfma(const RouteArgs& a, RouterLds& sh, int t0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int nblk = a.n_routed >> 4;
+  const int nb = nblk > wave ? (nblk - wave + 3) >> 2 : 0;   // blocks wave, wave+4, ...
+  const uint16_t* u = (const uint16_t*)a.u;
+  const int ta0 = min(t0 + r16, a.T - 1), ta1 = min(t0 + 16 + r16, a.T - 1);
+  const uint16_t* pa0 = u + (size_t)ta0 * a.d + kg * 8;
+  const uint16_t* pa1 = u + (size_t)ta1 * a.d + kg * 8;
+
+  double z64[2][4][4];
+#pragma unroll
+  for (int m = 0; m < 2; m++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) z64[m][j][r] = 0.0;
+
+  for (int kc = 0; kc < a.d; kc += RT_CHUNK) {
+    const int kend = min(kc + RT_CHUNK, a.d);
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int m = 0; m < 2; m++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int k = kc; k < kend; k += 32) {
+      const bf16x8 A0 = *(const bf16x8*)(pa0 + k);
+      const bf16x8 A1 = *(const bf16x8*)(pa1 + k);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (j < nb) {
+          const int e = ((wave + 4 * j) << 4) + r16;
+          if (!SPLIT_E) {
+            const bf16x8 B = *(const bf16x8*)((const uint16_t*)a.E + (size_t)e * a.d + k + kg * 8);
+            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, acc[0][j], 0, 0, 0);
+            acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, acc[1][j], 0, 0, 0);
+          } else {
+            const float* pe = (const float*)a.E + (size_t)e * a.d + k + kg * 8;
+            float x[8];
+            *(f32x4*)&x[0] = *(const f32x4*)pe;
+            *(f32x4*)&x[4] = *(const f32x4*)(pe + 4);
+            bf16x8 h, md, lo;
+            split3(x, h, md, lo);
+            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, lo, acc[0][j], 0, 0, 0);
+            acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, lo, acc[1][j], 0, 0, 0);
+            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, md, acc[0][j], 0, 0, 0);
+            acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, md, acc[1][j], 0, 0, 0);
+            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, h, acc[0][j], 0, 0, 0);
+            acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, h, acc[1][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 2; m++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) z64[m][j][r] += (double)acc[m][j][r];
+  }
+#pragma unroll
+  for (int m = 0; m < 2; m++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      if (j < nb) {
+        const int e = ((wave + 4 * j) << 4) + r16;
+#pragma unroll
+        for (int r = 0; r < 4; r++) sh.s[m * 16 + 4 * kg + r][e] = (float)sigmoid64(z64[m][j][r]);
+      }
+}
+
+template <bool U_BF16, bool E_BF16>
+__device__ void front_f64(const RouteArgs& a, RouterLds& sh, int t0, int nt) {
+  for (int p = threadIdx.x; p < nt * a.n_routed; p += RT_THREADS) {
+    const int t = p / a.n_routed, e = p - t * a.n_routed;
+    double z = 0.0;
+    for (int k = 0; k < a.d; k++) {
+      const size_t iu = (size_t)(t0 + t) * a.d + k, ie = (size_t)e * a.d + k;
+      const double x = U_BF16 ? bf16_to_f32(((const uint16_t*)a.u)[iu]) : ((const float*)a.u)[iu];
+      const double w = E_BF16 ? bf16_to_f32(((const uint16_t*)a.E)[ie]) : ((const float*)a.E)[ie];
+      z = fma(x, w, z);
+    }
+    sh.s[t][e] = (float)sigmoid64(z);
+  }
+}
+
+// ---------------------------------------------------------------- selection
+// One wave per token. Expert e lives in lane (e & 63), slot (e >> 6).
+__device__ void select_tokens(const RouteArgs& a, RouterLds& sh, int t0, int nt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int N = a.n_routed, K = a.top_k, G = a.n_groups, M = a.topk_groups, q = a.group_topk;
+  const int S = N / G;
+  for (int t = wave; t < nt; t += RT_THREADS / kWave) {
+    const float* srow = sh.s[t];
+    uint64_t pk[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int e = lane + 64 * j;
+      pk[j] = e < N ? rank_key(srow[e] + sh.b[e], (uint32_t)e) : 0ull;
+    }
+    if (G > 1) {
+      uint64_t gk = 0ull;
+      if (lane < G) {
+        float top[RT_QMAX];
+#pragma unroll
+        for (int i = 0; i < RT_QMAX; i++) top[i] = -INFINITY;
+        for (int i = 0; i < S; i++) {
+          const int e = lane * S + i;
+          float v = a.group_score_biased ? srow[e] + sh.b[e] : srow[e];
+#pragma unroll
+          for (int j = 0; j < RT_QMAX; j++) {
+            if (j < q && v > top[j]) { const float tmp = top[j]; top[j] = v; v = tmp; }
+          }
+        }
+        float acc = top[0];
+#pragma unroll
+        for (int j = 1; j < RT_QMAX; j++)
+          if (j < q) acc = acc + top[j];                    // fp32, largest first
+        gk = rank_key(acc, (uint32_t)lane);
+      }
+      uint64_t chosen = 0ull;
+      for (int m = 0; m < M; m++) {
+        const uint64_t c = ((chosen >> lane) & 1ull) ? 0ull : gk;
+        chosen |= 1ull << rank_key_index(wave_max_u64(c));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int e = lane + 64 * j;
+        if (e < N && !((chosen >> (e / S)) & 1ull)) pk[j] = 0ull;
+      }
+    }
+    int my_e = 0;
+    for (int k = 0; k < K; k++) {
+      uint64_t best = pk[0];
+#pragma unroll
+      for (int j = 1; j < 4; j++) best = pk[j] > best ? pk[j] : best;
+      best = wave_max_u64(best);
+      const int e = (int)rank_key_index(best);
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        if (e == lane + 64 * j) pk[j] = 0ull;
+      if (lane == k) my_e = e;
+    }
+    double sum = 0.0;
+    for (int k = 0; k < K; k++) sum += (double)srow[__shfl(my_e, k, kWave)];
+    if (lane < K) {
+      const float sv = srow[my_e];
+      const float g = sum > 0.0 ? (float)((double)sv / sum) : 1.0f / (float)K;
+      const size_t o = (size_t)(t0 + t) * K + lane;
+      a.idx[o] = my_e;
+      a.gate[o] = g;
+      atomicAdd(&sh.cnt[my_e], 1);
+    }
+  }
+}
+
+template <int FRONT, bool U_BF16, bool E_BF16>
+__global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
+  __shared__ RouterLds sh;
+  const int t0 = blockIdx.x * RT_BT;
+  const int nt = min(RT_BT, a.T - t0);
+  for (int e = threadIdx.x; e < a.n_routed; e += RT_THREADS) {
+    sh.b[e] = a.b[e];
+    sh.cnt[e] = 0;
+  }
+  if (FRONT == kFrontScoresIn) {
+    for (int p = threadIdx.x; p < nt * a.n_routed; p += RT_THREADS) {
+      const int t = p / a.n_routed, e = p - t * a.n_routed;
+      sh.s[t][e] = a.scores_in[(size_t)(t0 + t) * a.n_routed + e];
+    }
+  } else if (FRONT == kFrontMfma) {
+    front_mfma<false>(a, sh, t0);
+  } else if (FRONT == kFrontMfmaSplitE) {
+    front_mfma<true>(a, sh, t0);
+  } else {
+    front_f64<U_BF16, E_BF16>(a, sh, t0, nt);
+  }
+  __syncthreads();
+  if (a.scores_out) {
+    for (int p = threadIdx.x; p < nt * a.n_routed; p += RT_THREADS) {
+      const int t = p / a.n_routed, e = p - t * a.n_routed;
+      a.scores_out[(size_t)(t0 + t) * a.n_routed + e] = sh.s[t][e];
+    }
+  }
+  select_tokens(a, sh, t0, nt);
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.n_routed; e += RT_THREADS)
+    if (sh.cnt[e]) atomicAdd(&a.counts[e], sh.cnt[e]);
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int32_t v, long n) {
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (int)std::min<long>(cdiv<long>(n, 256), 1024);
+  fill_i32_kernel<<<blocks, 256, 0, s>>>(p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const RouteArgs& a, int front, hipStream_t s) {
+  hipError_t e = launch_fill_i32(a.counts, 0, a.n_routed, s);
+  if (e != hipSuccess) return e;
+  const dim3 grid(cdiv(a.T, RT_BT));
+  const bool ub = a.in_dtype == MOE_BF16;
+  switch (front) {
+    case kFrontScoresIn: route_kernel<kFrontScoresIn, false, false><<<grid, RT_THREADS, 0, s>>>(a); break;
+    case kFrontMfma: route_kernel<kFrontMfma, true, true><<<grid, RT_THREADS, 0, s>>>(a); break;
+    case kFrontMfmaSplitE: route_kernel<kFrontMfmaSplitE, true, false><<<grid, RT_THREADS, 0, s>>>(a); break;
+    default: {
+      // fp64 VALU logits, any dtype combination
+      const bool eb = a.router_dtype == MOE_BF16;
+      if (ub && eb) route_kernel<kFrontF64, true, true><<<grid, RT_THREADS, 0, s>>>(a);
+      else if (ub) route_kernel<kFrontF64, true, false><<<grid, RT_THREADS, 0, s>>>(a);
+      else if (eb) route_kernel<kFrontF64, false, true><<<grid, RT_THREADS, 0, s>>>(a);
+      else route_kernel<kFrontF64, false, false><<<grid, RT_THREADS, 0, s>>>(a);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

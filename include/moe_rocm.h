@@ -1,0 +1,217 @@
+/*
+ * moe_rocm.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer with
+ * auxiliary-loss-free load balancing.
+ *
+ * What the layer computes (DeepSeek-V3 Technical Report; the xyznot.com
+ * reading guides, "Metodo"/"al-tariqa" section 2, and the pwwt.cn study note):
+ *   s_{i,t} = sigmoid(u_t . e_i)                               (affinity)
+ *   g'_{i,t} = s_{i,t} if s_{i,t}+b_i is among the top K_r of
+ *              {s_{j,t}+b_j}, else 0                            (gating equation)
+ *   g_{i,t}  = g'_{i,t} / sum_j g'_{j,t}                        (normalised gate)
+ *   h'_t     = u_t + sum_s FFN^(s)(u_t) + sum_i g_{i,t} FFN^(r)_i(u_t)
+ *   b_i     <- b_i - gamma if expert i is overloaded, + gamma if underloaded
+ * with top-K_r restricted to the M expert groups whose top K_r/M scores sum
+ * highest (pwwt.cn note section 1.3) and no token dropped (note section 1.4).
+ *
+ * Conventions
+ *   - Every tensor argument is a DEVICE pointer owned by the caller, 16-byte
+ *     aligned, row-major and dense. The library never allocates, frees or
+ *     synchronises; scratch memory comes from the caller's workspace.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *     Results are valid once the stream has reached the end of the call.
+ *   - Each call validates every argument before enqueueing anything: a call
+ *     that returns an error has enqueued nothing (MOE_EHIP aside, which
+ *     reports a failed launch; moe_last_hip_error() gives the HIP code).
+ *   - The library holds no state between calls; calls on different streams
+ *     are independent provided they use different workspaces and outputs.
+ *   - Ties are broken deterministically and every result is reproducible
+ *     bit-for-bit from run to run (integer atomics only; fixed-order sums).
+ */
+#ifndef MOE_ROCM_H
+#define MOE_ROCM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* status codes */
+#define MOE_OK          0
+#define MOE_EINVAL     -1  /* bad dimension, NULL required pointer, misaligned pointer */
+#define MOE_ENOTSUP    -2  /* dtype / shape combination this build does not implement */
+#define MOE_EWORKSPACE -3  /* workspace smaller than the call needs */
+#define MOE_EHIP       -4  /* a HIP launch or runtime call failed */
+
+/* element types */
+#define MOE_F32       0
+#define MOE_BF16      1
+#define MOE_FP8_E4M3  2    /* OCP E4M3FN: bias 7, max 448, no infinities */
+
+/* moe_quantize_fp8 kinds */
+#define MOE_QUANT_ACT_1x128   0   /* one fp32 scale per row per 128 columns */
+#define MOE_QUANT_W_128x128   1   /* one fp32 scale per 128x128 block */
+
+typedef void* moe_stream_t;      /* hipStream_t */
+
+/* Layer description. Groups are contiguous blocks of n_routed/n_groups
+ * experts (the pages' nodes); n_groups = topk_groups = 1 disables the limit. */
+typedef struct moe_desc {
+  int32_t abi_version;        /* MOE_ABI_VERSION */
+  int32_t T;                  /* tokens in the batch */
+  int32_t d;                  /* hidden size */
+  int32_t n_routed;           /* N_r, 1..256 */
+  int32_t top_k;              /* K_r, 1..min(N_r, 32) */
+  int32_t n_groups;           /* G, divides N_r, <= 64 */
+  int32_t topk_groups;        /* M, 1..G */
+  int32_t group_topk;         /* q: scores summed per group (K_r/M on the pages), 1..N_r/G */
+  int32_t n_shared;           /* N_s >= 0 */
+  int32_t inter;              /* I, routed expert intermediate size */
+  int32_t inter_shared;       /* I_s, shared expert intermediate size */
+  int32_t in_dtype;           /* u and out: MOE_F32 | MOE_BF16 */
+  int32_t router_dtype;       /* centroids: MOE_F32 | MOE_BF16 */
+  int32_t expert_dtype;       /* expert weights: MOE_F32 | MOE_BF16 | MOE_FP8_E4M3 */
+  int32_t group_score_biased; /* 1: group scores from s+b (default); 0: from s */
+  float   gamma;              /* bias update speed, 0.001 on the pages */
+} moe_desc_t;
+
+/* Weights for moe_forward. Layouts:
+ *   centroids   [N_r, d]        router_dtype
+ *   w13         [N_r, 2I, d]    rows 0..I-1: W1 (gate, goes through SiLU); I..2I-1: W3 (up)
+ *   w2          [N_r, d, I]
+ *   w13_shared  [N_s, 2I_s, d], w2_shared [N_s, d, I_s]
+ *   FP8 only: E4M3 codes in w13/w2/..., and fp32 block scales
+ *   w13_scale [N_r, 2I/128, d/128], w2_scale [N_r, d/128, I/128] (same for shared). */
+typedef struct moe_weights {
+  const void*  centroids;
+  const void*  w13;
+  const void*  w2;
+  const void*  w13_shared;
+  const void*  w2_shared;
+  const float* w13_scale;
+  const float* w2_scale;
+  const float* w13_shared_scale;
+  const float* w2_shared_scale;
+} moe_weights_t;
+
+/* Optional routing outputs of moe_forward (any member may be NULL). */
+typedef struct moe_route_out {
+  int32_t* topk_idx;   /* [T, K] */
+  float*   topk_gate;  /* [T, K] */
+  int32_t* counts;     /* [N_r] */
+} moe_route_out_t;
+
+int         moe_abi_version(void);
+const char* moe_strerror(int status);
+int         moe_last_hip_error(void);
+
+/* Checks a descriptor alone (dims, dtypes, group rule). MOE_OK or MOE_EINVAL/ENOTSUP. */
+int moe_validate(const moe_desc_t* desc);
+
+/* Workspace bytes moe_forward needs for this descriptor (0 on invalid desc). */
+size_t moe_workspace_bytes(const moe_desc_t* desc);
+
+/* Router: affinities, biased group-limited top-K, normalised gates, loads.
+ * (xyznot.com guides section 2, gating equation; pwwt.cn note 1.1.2, 1.3.)
+ *   u [T,d] in_dtype and E [N_r,d] router_dtype; or scores_in [T,N_r] fp32
+ *   (exactly one of the two sources). With scores_in the affinities are taken
+ *   as given and the selection runs on the same code path.
+ *   b [N_r] fp32 (read only).
+ *   scores_out [T,N_r] fp32, nullable: the fp32 affinities used.
+ *   topk_idx [T,K] int32: selected experts in rank order (key desc, index asc).
+ *   topk_gate [T,K] fp32: s / sum(s) over the selected experts (unbiased s;
+ *     1/K if the sum is 0).
+ *   counts [N_r] int32: overwritten with the number of tokens per expert. */
+int moe_route(const moe_desc_t* desc, const void* u, const void* E, const float* b,
+              const float* scores_in, float* scores_out, int32_t* topk_idx,
+              float* topk_gate, int32_t* counts, moe_stream_t stream);
+
+/* Dispatch layout (single-GPU analog of the pwwt.cn note's section 4
+ * dispatch; no capacity, note 1.4).
+ *   offsets [N_r+1]: rows of expert e are [offsets[e], offsets[e+1]).
+ *   row_token [T*K]: token of each permuted row, ascending within an expert.
+ *   slot_row [T*K]: permuted row of (t, topk_idx[t,k]) at index t*K+k.
+ *   counts [N_r], nullable: loads recomputed from topk_idx.
+ *   u [T,d] and x_perm [T*K,d] (in_dtype), nullable together: gathered rows.
+ *   ws: at least moe_workspace_bytes(desc) bytes. */
+int moe_permute(const moe_desc_t* desc, const int32_t* topk_idx, int32_t* offsets,
+                int32_t* row_token, int32_t* slot_row, int32_t* counts,
+                const void* u, void* x_perm, void* ws, size_t ws_bytes,
+                moe_stream_t stream);
+
+/* Grouped SwiGLU experts over `rows` permuted rows in n_experts segments:
+ *   y[r] = W2_e (SiLU(W1_e x_r) * (W3_e x_r)) for offsets[e] <= r < offsets[e+1].
+ * (xyznot.com guides section 2, output equation; the SwiGLU form is a
+ *  reading, the pages do not state the FFN's inner form.)
+ *   x: [T,d] read through row_token (x_r = x[row_token[r]]) or, with
+ *      row_token NULL, [rows,d] read directly. Type: in_dtype for F32/BF16
+ *      experts; E4M3 codes for FP8 experts, with x_scale [.., d/128] fp32.
+ *   w13 [n_experts, 2*inter, d], w2 [n_experts, d, inter] expert_dtype; FP8
+ *      scales w13_scale/w2_scale as in moe_weights_t.
+ *   y [rows, d]: fp32 for F32 experts, bf16 otherwise.
+ *   ws: at least moe_expert_ffn_workspace_bytes(...) bytes. */
+size_t moe_expert_ffn_workspace_bytes(const moe_desc_t* desc, int32_t n_experts,
+                                      int32_t inter, int32_t rows);
+int moe_expert_ffn(const moe_desc_t* desc, int32_t n_experts, int32_t inter, int32_t rows,
+                   const void* x, const float* x_scale, const int32_t* row_token,
+                   const int32_t* offsets, const void* w13, const float* w13_scale,
+                   const void* w2, const float* w2_scale, void* y, void* ws,
+                   size_t ws_bytes, moe_stream_t stream);
+
+/* Combine: out_t = u_t + sum_s y_shared[s,t] + sum_k gate[t,k] * y[slot_row[t*K+k]]
+ * accumulated in fp32 in that fixed order (output equation; the pwwt.cn
+ * note's section 4 combine).  u, out [T,d] in_dtype; y [T*K,d] and
+ * y_shared [N_s,T,d] (nullable when N_s = 0) fp32 for F32 experts, bf16 otherwise. */
+int moe_combine(const moe_desc_t* desc, const void* u, const void* y, const void* y_shared,
+                const int32_t* slot_row, const float* topk_gate, void* out,
+                moe_stream_t stream);
+
+/* End-of-step bias update (pwwt.cn note 1.1.3; guides section 2):
+ *   b_i <- fl32(b_i - gamma) if N_r*c_i > T*K (overloaded),
+ *          fl32(b_i + gamma) if N_r*c_i < T*K (underloaded), unchanged otherwise. */
+int moe_update_bias(const moe_desc_t* desc, const int32_t* counts, float* b,
+                    moe_stream_t stream);
+
+/* Whole layer: route -> permute -> grouped experts (routed + shared) ->
+ * combine -> (update_bias != 0) bias update. b is read by the router and, if
+ * update_bias, updated in place after the loads are known.
+ *   u, out [T,d] in_dtype. dbg nullable. ws: moe_workspace_bytes(desc). */
+int moe_forward(const moe_desc_t* desc, const moe_weights_t* w, const void* u, float* b,
+                void* out, moe_route_out_t* dbg, int32_t update_bias, void* ws,
+                size_t ws_bytes, moe_stream_t stream);
+
+/* FP8 quantiser (xyznot.com guides, FP8 key idea; pwwt.cn note section 3):
+ *   scale = fl32(amax/448) per 1x128 tile (ACT) or 128x128 block (W), 1 when
+ *   amax = 0; q = E4M3(fl32(x/scale)), round to nearest even, saturated.
+ *   src [rows, cols] fp32 or bf16 (src_dtype); cols % 128 == 0, and for W
+ *   rows % 128 == 0. q [rows, cols] uint8; scale [rows, cols/128] (ACT) or
+ *   [rows/128, cols/128] (W). */
+int moe_quantize_fp8(int32_t kind, const void* src, int32_t src_dtype, int32_t rows,
+                     int32_t cols, uint8_t* q, float* scale, moe_stream_t stream);
+
+/* Stage timing (diagnostics, for benchmarks; not thread-safe). While enabled,
+ * moe_forward records a hipEvent on its stream at every stage boundary (a
+ * pool of events created by moe_profile_enable; recording stops when the pool
+ * is used up). moe_profile_read waits for the recorded events, writes the
+ * summed milliseconds of each stage into ms[MOE_N_STAGES] and the number of
+ * recorded moe_forward calls into *calls, and with reset != 0 starts over.
+ * Stage intervals are measured between consecutive events on the caller's
+ * stream, so each covers exactly the kernels of that stage. */
+#define MOE_STAGE_ROUTE    0   /* counts fill + router kernel */
+#define MOE_STAGE_PERMUTE  1   /* bitmap, scan, scatter */
+#define MOE_STAGE_QUANT_X  2   /* FP8 only: 1x128 quantiser of u */
+#define MOE_STAGE_GEMM1    3   /* grouped gate/up GEMM with SwiGLU epilogue */
+#define MOE_STAGE_GEMM2    4   /* (FP8: quantiser of H +) grouped down GEMM */
+#define MOE_STAGE_COMBINE  5
+#define MOE_STAGE_BIAS     6
+#define MOE_N_STAGES       7
+int moe_profile_enable(int on);
+int moe_profile_read(double* ms, int64_t* calls, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_ROCM_H */

@@ -1,0 +1,152 @@
+"""The C-ABI library loads, exports every entry point its header declares, and
+rejects bad arguments synchronously (before enqueueing anything) -- all
+without a GPU: every call below returns from host-side validation."""
+
+import ctypes
+import os
+
+import pytest
+
+import expert_routing_router_amd as M
+from expert_routing_router_amd import _lib as L
+from workloads import CONFIGS
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from expert_routing_router_amd import build
+        build.build()
+    return L.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = L.header_symbols()
+    assert len(names) == 15, names
+    raw = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_strerror(lib):
+    assert lib.moe_abi_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert lib.moe_strerror(st)
+    assert b"unknown" in lib.moe_strerror(7)
+
+
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_configs_validate(lib, name):
+    d = M.desc_from_config(CONFIGS[name])
+    assert M.moe_validate(d) == M.MOE_OK
+    assert M.moe_workspace_bytes(d) > 0
+
+
+def _v3(**kw):
+    base = dict(T=8192, d=7168, n_routed=256, top_k=8, n_groups=8, topk_groups=4, group_topk=2,
+                n_shared=1, inter=2048)
+    base.update(kw)
+    return M.make_desc(**base)
+
+
+BAD = [
+    (dict(top_k=0), M.MOE_EINVAL),
+    (dict(top_k=257), M.MOE_EINVAL),
+    (dict(n_routed=300), M.MOE_EINVAL),
+    (dict(n_groups=7), M.MOE_EINVAL),            # does not divide N_r
+    (dict(topk_groups=9), M.MOE_EINVAL),         # M > G
+    (dict(topk_groups=0), M.MOE_EINVAL),
+    (dict(group_topk=33), M.MOE_EINVAL),         # q > N_r/G
+    (dict(topk_groups=1, group_topk=2, top_k=40), M.MOE_EINVAL),   # M*N_r/G < K
+    (dict(d=100), M.MOE_EINVAL),                 # d % 8
+    (dict(T=-1), M.MOE_EINVAL),
+    (dict(inter=0), M.MOE_EINVAL),
+    (dict(group_score_biased=2), M.MOE_EINVAL),
+    (dict(gamma=float("nan")), M.MOE_EINVAL),
+    (dict(in_dtype=5), M.MOE_ENOTSUP),
+    (dict(expert_dtype="fp8", d=7168 + 64), M.MOE_ENOTSUP),     # FP8 needs d % 128
+    (dict(expert_dtype="fp8", inter=2048 + 64), M.MOE_ENOTSUP),
+    (dict(expert_dtype="bf16", in_dtype="f32"), M.MOE_ENOTSUP),
+    (dict(T=1 << 20), M.MOE_ENOTSUP),            # row offsets beyond 2^31
+]
+
+
+@pytest.mark.parametrize("kw,want", BAD, ids=[str(k) for k, _ in BAD])
+def test_descriptor_rules(lib, kw, want):
+    d = _v3(**kw)
+    assert M.moe_validate(d) == want
+    assert M.moe_workspace_bytes(d) == 0
+
+
+def test_bad_abi_version(lib):
+    d = _v3()
+    d.abi_version = 2
+    assert M.moe_validate(d) == M.MOE_EINVAL
+    assert lib.moe_validate(None) == M.MOE_EINVAL
+
+
+A = 0x10000          # aligned dummy device addresses: validation never dereferences them
+MIS = 0x10004
+
+
+def test_route_argument_errors(lib):
+    d = _v3()
+    r = lambda *a: lib.moe_route(ctypes.byref(d), *a, None)
+    # neither source, both sources
+    assert r(None, None, A, None, None, A, A, A) == M.MOE_EINVAL
+    assert r(A, A, A, A, None, A, A, A) == M.MOE_EINVAL
+    # missing outputs / bias, misaligned pointers
+    assert r(A, A, None, None, None, A, A, A) == M.MOE_EINVAL
+    assert r(A, A, A, None, None, None, A, A) == M.MOE_EINVAL
+    assert r(MIS, A, A, None, None, A, A, A) == M.MOE_EINVAL
+    assert r(A, A, A, None, MIS, A, A, A) == M.MOE_EINVAL
+
+
+def test_permute_workspace_and_pointer_errors(lib):
+    d = _v3()
+    need = M.moe_workspace_bytes(d)
+    p = lambda ws, nbytes, u=None, x=None: lib.moe_permute(
+        ctypes.byref(d), A, A, A, A, None, u, x, ws, nbytes, None)
+    assert p(A, need - 1) == M.MOE_EWORKSPACE
+    assert p(None, need) == M.MOE_EINVAL
+    assert p(A, need, u=A) == M.MOE_EINVAL          # u without x_perm
+
+
+def test_ffn_combine_bias_forward_errors(lib):
+    d = _v3()
+    assert lib.moe_expert_ffn(ctypes.byref(d), 0, 2048, 10, A, None, None, A, A, None, A, None, A,
+                              A, 1 << 40, None) == M.MOE_EINVAL
+    need = M.moe_expert_ffn_workspace_bytes(d, 4, 2048, 1000)
+    assert need > 0
+    assert lib.moe_expert_ffn(ctypes.byref(d), 4, 2048, 1000, A, None, None, A, A, None, A, None,
+                              A, A, need - 1, None) == M.MOE_EWORKSPACE
+    assert lib.moe_expert_ffn(ctypes.byref(d), 4, 2048 + 32, 1000, A, None, None, A, A, None, A,
+                              None, A, A, 1 << 40, None) == M.MOE_ENOTSUP
+    f8 = _v3(expert_dtype="fp8")
+    assert lib.moe_expert_ffn(ctypes.byref(f8), 4, 2048, 1000, A, None, None, A, A, None, A,
+                              None, A, A, 1 << 40, None) == M.MOE_EINVAL      # scales missing
+    assert lib.moe_combine(ctypes.byref(d), A, A, None, A, A, A, None) == M.MOE_EINVAL  # N_s=1
+    assert lib.moe_combine(ctypes.byref(d), A, MIS, A, A, A, A, None) == M.MOE_EINVAL
+    assert lib.moe_update_bias(ctypes.byref(d), None, A, None) == M.MOE_EINVAL
+    w = M.MoeWeights(A, A, A, A, A, None, None, None, None)
+    need = M.moe_workspace_bytes(d)
+    fw = lambda desc, ws_bytes, weights=w: lib.moe_forward(
+        ctypes.byref(desc), ctypes.byref(weights), A, A, A, None, 1, A, ws_bytes, None)
+    assert fw(d, need - 256) == M.MOE_EWORKSPACE
+    assert fw(f8, M.moe_workspace_bytes(f8)) == M.MOE_EINVAL                 # FP8 scales missing
+    w2 = M.MoeWeights(A, A, A, None, None, None, None, None, None)
+    assert fw(d, need, w2) == M.MOE_EINVAL                                     # shared weights missing
+
+
+def test_quantize_errors(lib):
+    assert lib.moe_quantize_fp8(3, A, 0, 128, 128, A, A, None) == M.MOE_EINVAL
+    assert lib.moe_quantize_fp8(0, A, 0, 4, 100, A, A, None) == M.MOE_EINVAL
+    assert lib.moe_quantize_fp8(1, A, 0, 100, 128, A, A, None) == M.MOE_EINVAL
+    assert lib.moe_quantize_fp8(0, A, 2, 4, 128, A, A, None) == M.MOE_ENOTSUP
+
+
+def test_binding_requires_device_tensors(lib):
+    import torch
+    d = _v3()
+    with pytest.raises(ValueError):
+        M.moe_update_bias(d, torch.zeros(256, dtype=torch.int32), torch.zeros(256))

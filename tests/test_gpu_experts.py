@@ -1,0 +1,110 @@
+"""Grouped SwiGLU experts (moe_expert_ffn) on the GPU against the fp64 oracle.
+
+Segments are ragged on purpose: empty experts, a single row, rows around the
+32-row MFMA block and the 256/320-row m-tile edges, and one large segment that
+needs several m-tiles; rows are gathered through row_token (random token ids,
+with repeats across experts, as after routing).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import expert_routing_router_amd as M
+from oracle import ffn, numerics as nx
+from tests.gpu_util import dev, host, log, rel_l2
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+COUNTS = [0, 1, 31, 32, 33, 255, 256, 257, 319, 320, 321, 0, 700, 5]
+
+
+def _weights(rng, n, inter, d, wdtype):
+    w13 = (rng.standard_normal((n, 2 * inter, d)) / np.sqrt(d)).astype(np.float32)
+    w2 = (rng.standard_normal((n, d, inter)) / np.sqrt(d)).astype(np.float32)
+    if wdtype == "bf16":
+        return gen.f32_to_bf16_bits(w13), gen.f32_to_bf16_bits(w2)
+    return w13, w2
+
+
+@pytest.mark.parametrize("dtype,d,inter", [("bf16", 256, 128), ("bf16", 1024, 384), ("f32", 256, 96),
+                                           ("bf16", 7168, 2048)])
+def test_grouped_swiglu(dtype, d, inter):
+    rng = np.random.default_rng(d + inter)
+    counts = COUNTS if d < 7168 else [0, 250, 262, 1]
+    n = len(counts)
+    rows = sum(counts)
+    T = 600
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    row_token = rng.integers(0, T, rows).astype(np.int32)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    if dtype == "bf16":
+        x = gen.f32_to_bf16_bits(x)
+    w13, w2 = _weights(rng, n, inter, d, dtype)
+    desc = M.make_desc(T=T, d=d, n_routed=16, top_k=2, n_shared=0, inter=inter, in_dtype=dtype,
+                       router_dtype=dtype, expert_dtype=dtype)
+    ws = torch.empty(M.moe_expert_ffn_workspace_bytes(desc, n, inter, rows), dtype=torch.uint8, device="cuda")
+    y = torch.empty((rows, d), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+    M.moe_expert_ffn(desc, n, inter, rows, dev(x, dtype), dev(offsets, "i32"), dev(w13, dtype),
+                     dev(w2, dtype), y, ws, row_token=dev(row_token, "i32"))
+    torch.cuda.synchronize()
+    got = host(y)
+    x64 = nx.to_f64(x, dtype)
+    worst = 0.0
+    for e in range(n):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi == lo:
+            continue
+        ref = ffn.swiglu(x64[row_token[lo:hi]], nx.to_f64(w13[e], dtype), nx.to_f64(w2[e], dtype))
+        err = rel_l2(got[lo:hi], ref)
+        worst = max(worst, err)
+    log("experts", dtype, d, inter, "worst per-expert rel-L2 %.2e" % worst)
+    assert worst < (1e-2 if dtype == "bf16" else 1e-5)
+
+
+def test_grouped_swiglu_direct_rows_and_fp8():
+    """x read directly (row_token NULL), and the FP8 path against oracle B."""
+    rng = np.random.default_rng(5)
+    d, inter = 512, 256
+    counts = [3, 0, 300, 64, 129]
+    n, rows = len(counts), sum(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = rng.standard_normal((rows, d)).astype(np.float32)
+    x[rng.integers(0, rows, 20), rng.integers(0, d, 20)] = 50.0
+    w13, w2 = _weights(rng, n, inter, d, "f32")
+    desc = M.make_desc(T=rows, d=d, n_routed=16, top_k=1, n_shared=0, inter=inter, in_dtype="bf16",
+                       router_dtype="f32", expert_dtype="fp8")
+    xb = gen.f32_to_bf16_bits(x)
+    xq = torch.empty((rows, d), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((rows, d // 128), dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8(M.MOE_QUANT_ACT_1x128, dev(xb, "bf16"), rows, d, xq, xs)
+    q13 = torch.empty((n, 2 * inter, d), dtype=torch.uint8, device="cuda")
+    s13 = torch.empty((n, 2 * inter // 128, d // 128), dtype=torch.float32, device="cuda")
+    q2 = torch.empty((n, d, inter), dtype=torch.uint8, device="cuda")
+    s2 = torch.empty((n, d // 128, inter // 128), dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8(M.MOE_QUANT_W_128x128, dev(w13.reshape(-1, d), "f32"), n * 2 * inter, d, q13, s13)
+    M.moe_quantize_fp8(M.MOE_QUANT_W_128x128, dev(w2.reshape(-1, inter), "f32"), n * d, inter, q2, s2)
+    ws = torch.empty(M.moe_expert_ffn_workspace_bytes(desc, n, inter, rows), dtype=torch.uint8, device="cuda")
+    y = torch.empty((rows, d), dtype=torch.bfloat16, device="cuda")
+    M.moe_expert_ffn(desc, n, inter, rows, xq, dev(offsets, "i32"), q13, q2, y, ws, x_scale=xs,
+                     w13_scale=s13, w2_scale=s2)
+    torch.cuda.synchronize()
+    # the quantisers are bit-exact against the oracle's encoder
+    cq, cs = nx.quant_act_1x128(nx.bf16_to_f64(xb).astype(np.float32))
+    assert np.array_equal(host(xq), cq) and np.array_equal(host(xs), cs)
+    cw, sw = nx.quant_w_128x128(w13[2])
+    assert np.array_equal(host(q13[2]), cw) and np.array_equal(host(s13[2]), sw)
+    got = host(y)
+    x64 = nx.bf16_to_f64(xb)
+    for e in range(n):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi == lo:
+            continue
+        xq64 = nx.dequant_act(*nx.quant_act_1x128(x64[lo:hi].astype(np.float32)))
+        refB = ffn._expert(xq64, w13[e].astype(np.float64), w2[e].astype(np.float64), True)
+        refA = ffn.swiglu(x64[lo:hi], w13[e].astype(np.float64), w2[e].astype(np.float64))
+        eB, eA, eAB = rel_l2(got[lo:hi], refB), rel_l2(got[lo:hi], refA), rel_l2(refB, refA)
+        log("fp8 expert", e, "vs oracle B %.2e" % eB, "vs A %.2e" % eA, "(B vs A %.2e)" % eAB)
+        assert eB < 1.5e-2
+        assert eA < eAB * 1.25 + 5e-3

@@ -1,0 +1,133 @@
+"""Router parity on the GPU against the oracle.
+
+* scores-in mode: with the oracle's fp32 affinities fed in, topk_idx, counts
+  and the updated bias are bit-exact, and so are the gates (both sides divide
+  the same fp64 sums, the GPU rounds once to fp32);
+* end to end (u, E on the GPU): any routing difference is confined to tokens
+  whose K-th/(K+1)-th key gap (or M-th/(M+1)-th group-score gap) is below
+  1e-6 relative.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import expert_routing_router_amd as M
+from oracle import numerics as nx, routing
+from tests.gpu_util import dev, host, log
+from workloads import gen, get_config
+
+pytestmark = pytest.mark.gpu
+
+
+def _desc(T, N, K, G=1, Mg=1, q=None, biased=1, d=256, in_dtype="bf16", router_dtype="bf16"):
+    return M.make_desc(T=T, d=d, n_routed=N, top_k=K, n_groups=G, topk_groups=Mg,
+                       group_topk=q if q is not None else max(1, K // Mg), n_shared=0, inter=128,
+                       in_dtype=in_dtype, router_dtype=router_dtype,
+                       expert_dtype="bf16" if in_dtype == "bf16" else "f32",
+                       group_score_biased=biased)
+
+
+def _gpu_route_scores(desc, s32, b32):
+    T, N = s32.shape
+    K = desc.top_k
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    counts = torch.empty(N, dtype=torch.int32, device="cuda")
+    sout = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    bd = dev(b32, "f32")
+    M.moe_route(desc, bd, idx, gate, counts, scores_in=dev(s32, "f32"), scores_out=sout)
+    M.moe_update_bias(desc, counts, bd)
+    torch.cuda.synchronize()
+    return host(idx), host(gate), host(counts), host(sout), host(bd)
+
+
+SCORE_CASES = [
+    # name, T, N, K, G, M, q, biased, tie_heavy
+    ("tiny_shape", 64, 16, 4, 4, 2, 2, 1, False),
+    ("mid_shape", 4096, 64, 6, 1, 1, 6, 1, False),
+    ("v3_shape", 8192, 256, 8, 8, 4, 2, 1, False),
+    ("v3_unbiased_groups", 8192, 256, 8, 8, 4, 2, 0, False),
+    ("v3_tie_heavy", 2048, 256, 8, 8, 4, 2, 1, True),
+    ("ragged_T", 1000, 64, 6, 4, 2, 3, 1, True),
+    ("single_token", 1, 256, 8, 8, 4, 2, 1, False),
+    ("k1_g64", 33, 128, 1, 64, 1, 1, 1, True),
+    ("q3_groups", 257, 96, 6, 6, 2, 3, 1, False),
+    ("all_experts", 50, 16, 16, 1, 1, 16, 1, True),
+]
+
+
+@pytest.mark.parametrize("case", SCORE_CASES, ids=[c[0] for c in SCORE_CASES])
+def test_scores_in_bit_exact(case):
+    name, T, N, K, G, Mg, q, biased, ties = case
+    rng = np.random.default_rng(abs(hash(name)) % 2 ** 32)
+    if ties:
+        s = rng.choice(np.array([0.125, 0.25, 0.375, 0.5, 0.625, 0.75, 1.0, 0.0], np.float32), (T, N))
+        b = rng.choice(np.array([0, 0.125, -0.125, 0.25, -0.0], np.float32), N)
+    else:
+        s = rng.uniform(0, 1, (T, N)).astype(np.float32)
+        b = rng.uniform(-0.01, 0.01, N).astype(np.float32)
+    desc = _desc(T, N, K, G, Mg, q, biased)
+    r = routing.select(s, b, K, G, Mg, q, biased)
+    idx, gate, counts, sout, b1 = _gpu_route_scores(desc, s, b)
+    assert np.array_equal(sout, s)
+    assert np.array_equal(idx, r.idx), np.nonzero((idx != r.idx).any(axis=1))[0][:10]
+    assert np.array_equal(counts, r.counts)
+    assert np.array_equal(gate, r.gate.astype(np.float32))
+    want_b = routing.bias_step(r.counts, b, T, K, 0.001)
+    assert np.array_equal(b1.view(np.uint32), want_b.view(np.uint32))
+
+
+def test_scores_from_oracle_logits_tiny_and_mid():
+    for name in ("tiny", "mid"):
+        cfg = get_config(name)
+        u = nx.to_f64(gen.tokens(cfg, 0), cfg.in_dtype)
+        E = nx.to_f64(gen.centroids(cfg), cfg.router_dtype)
+        b = gen.bias_init(cfg)
+        s32 = routing.sigmoid(routing.logits(u, E)).astype(np.float32)
+        desc = M.desc_from_config(cfg)
+        r = routing.select(s32, b, cfg.top_k, cfg.n_groups, cfg.topk_groups, cfg.group_topk)
+        idx, gate, counts, _, b1 = _gpu_route_scores(desc, s32, b)
+        assert np.array_equal(idx, r.idx) and np.array_equal(counts, r.counts)
+        assert np.array_equal(b1, routing.bias_step(r.counts, b, cfg.T, cfg.top_k))
+        log(name, "scores-in routing bit-exact")
+
+
+def _e2e(cfg, step=0, b=None, T=None):
+    if T is not None:
+        cfg = cfg.with_(T=T)
+    u = gen.tokens(cfg, step)
+    E = gen.centroids(cfg)
+    b = gen.bias_init(cfg) if b is None else b
+    desc = M.desc_from_config(cfg)
+    T, N, K = cfg.T, cfg.n_routed, cfg.top_k
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    counts = torch.empty(N, dtype=torch.int32, device="cuda")
+    sout = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    M.moe_route(desc, dev(b, "f32"), idx, gate, counts, u=dev(u, cfg.in_dtype),
+                E=dev(E, cfg.router_dtype), scores_out=sout)
+    torch.cuda.synchronize()
+    r, s64, s32 = routing.route_tokens(nx.to_f64(u, cfg.in_dtype), nx.to_f64(E, cfg.router_dtype), b, cfg)
+    kgap, ggap = routing.near_tie_gaps(r, K, cfg.topk_groups)
+    return r, s64, s32, kgap, ggap, host(idx), host(gate), host(counts), host(sout)
+
+
+@pytest.mark.parametrize("name,T", [("tiny", None), ("mid", None), ("v3", None), ("fp8", 2048),
+                                    ("skew", 4096), ("v3", 77)])
+def test_end_to_end_routing(name, T):
+    cfg = get_config(name)
+    r, s64, s32, kgap, ggap, idx, gate, counts, sout = _e2e(cfg, T=T)
+    # affinities agree to a few fp32 ulps (logit error is ~1e-7 absolute)
+    assert np.max(np.abs(sout.astype(np.float64) - s64)) < 1e-6
+    diff = np.nonzero((idx != r.idx).any(axis=1))[0]
+    exempt = (kgap < 1e-6) | (ggap < 1e-6)
+    log(name, "T=%d" % r.idx.shape[0], "tokens routed differently:", len(diff),
+        "exempt tokens:", int(exempt.sum()))
+    assert exempt[diff].all(), diff[~exempt[diff]][:10]
+    ok = ~exempt
+    assert np.array_equal(idx[ok], r.idx[ok])
+    assert np.allclose(gate[ok], r.gate[ok], rtol=2e-6, atol=0)
+    if len(diff) == 0:
+        assert np.array_equal(counts, r.counts)
+    assert counts.sum() == r.idx.size
