@@ -62,8 +62,8 @@ def cpu_baseline(cfg, n_sample_experts, log_fn):
 
     Sample: routing of all T tokens (fp64 logits, sigmoid, group-limited top-K,
     gates); the SwiGLU of the first `n_sample_experts` routed experts over
-    their routed rows; the shared experts over T/8 tokens. Per-forward time =
-    t_route + t_sample * N_r / n_sample + t_shared * 8.
+    their routed rows; the shared experts over T/2 tokens. Per-forward time =
+    t_route + t_sample * N_r / n_sample + t_shared * 2.
     """
     import numpy as np
     from oracle import ffn, numerics as nx, routing
@@ -95,7 +95,7 @@ def cpu_baseline(cfg, n_sample_experts, log_fn):
         rows_done += len(rows)
     t_routed = time.perf_counter() - t0
     t0 = time.perf_counter()
-    Tsub = max(1, cfg.T // 8)
+    Tsub = max(1, cfg.T // 2)
     for s in range(cfg.n_shared):
         ffn.swiglu(u64[:Tsub], nx.to_f64(ws[s][0], wdt), nx.to_f64(ws[s][1], wdt))
     t_shared = time.perf_counter() - t0
@@ -117,8 +117,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="v3")
     ap.add_argument("--T", type=int, default=0, help="override tokens per batch")
-    ap.add_argument("--cpu-sample-experts", type=int, default=8)
+    ap.add_argument("--cpu-sample-experts", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (5 times) and exit: the "
+                         "reference dispatch for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -131,6 +134,16 @@ def main():
     import expert_routing_router_amd as M
     from expert_routing_router_amd.layer import MoELayer, np_to_device
     from workloads import gen, get_config
+
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "dispatches": 5}))
+        return
 
     cfg = get_config(args.config)
     if args.T:

@@ -54,6 +54,17 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer loads return zeros for offsets at or beyond num_records instead of
+// faulting, so a row that does not exist is loaded from kOutOfRange without a
+// branch (a branch around a load forces a full vmcnt wait at the join).
+constexpr int kOutOfRange = (int)0x80000000u;
+constexpr int kRawBufferFlags = 0x00020000;   // gfx9 raw buffer: DATA_FORMAT = 32-bit
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  const int n = bytes >= 0x7FFFFFFFL ? 0x7FFFFFFF : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRawBufferFlags);
+}
+
 // ---------------------------------------------------------------- misc
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;

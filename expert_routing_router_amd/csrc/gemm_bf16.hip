@@ -23,6 +23,7 @@
 #include "common.h"
 #include "moe_internal.h"
 #include <cmath>
+#include <type_traits>
 
 namespace moe {
 
@@ -77,7 +78,15 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_kernel(GemmArgs a) {
   __syncthreads();
   const int n_tiles = SWIGLU ? a.N / 64 : a.N / GB_BN;
   int seg, ntile, mtile;
-  if (!decode_tile(sprefix, a.n_seg, n_tiles, blockIdx.x, seg, ntile, mtile)) return;
+  // Workgroup i runs on XCD i % 8, and each XCD starts its workgroups in order of i.
+  // Give XCD x the contiguous logical range [x*per, (x+1)*per): the tiles of one
+  // expert (all its n-tiles) then run side by side on one XCD and share the
+  // expert's gathered rows in that XCD's L2.
+  const int total_tiles = sprefix[a.n_seg] * n_tiles;
+  const int per_xcd = (total_tiles + 7) >> 3;
+  const int lt = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd) return;
+  if (!decode_tile(sprefix, a.n_seg, n_tiles, lt, seg, ntile, mtile)) return;
 
   const int seg_begin = a.offsets[seg], seg_end = a.offsets[seg + 1];
   const int row0 = seg_begin + mtile * BM;
@@ -86,21 +95,19 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_kernel(GemmArgs a) {
   const uint16_t* wbase = seg < a.n_first
       ? (const uint16_t*)a.w0 + (size_t)seg * a.wstride0
       : (const uint16_t*)a.w1 + (size_t)(seg - a.n_first) * a.wstride1;
-  const uint16_t* x = (const uint16_t*)a.x;
 
   // ---- per-thread global source offsets (element units), fixed over K
   const int cch = tid & 7;          // 16-byte chunk within a 128-byte row slice
   const int rbase = tid >> 3;       // 0..31
+  // A rows: byte offsets into x; rows past the segment read zeros (out of range)
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_rows * (long)K * 2);
   int aoff[ACH];
 #pragma unroll
   for (int i = 0; i < ACH; i++) {
     const int r = rbase + 32 * i;
-    if (r < mvalid) {
-      const int src = a.row_index ? a.row_index[row0 + r] : row0 + r;
-      aoff[i] = src * K + cch * 8;
-    } else {
-      aoff[i] = -1;
-    }
+    const int rr = row0 + min(r, mvalid - 1);
+    const int src = a.row_index ? a.row_index[rr] : rr;
+    aoff[i] = r < mvalid ? (src * K + cch * 8) * 2 : kOutOfRange;
   }
   int boff[BCH];
 #pragma unroll
@@ -112,15 +119,18 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_kernel(GemmArgs a) {
     boff[i] = wrow * K + cch * 8;
   }
 
-  i32x4 ra[ACH], rb[BCH];
-  auto gload = [&](int k0) {
+  // Two register sets: the loads for K-step k+2 are issued while step k is
+  // computed from LDS and step k+1 waits in the other set, so each global load
+  // has about two steps of MFMA work to land.
+  i32x4 ra0[ACH], rb0[BCH], ra1[ACH], rb1[BCH];
+  auto gload = [&](i32x4 (&ra)[ACH], i32x4 (&rb)[BCH], int k0) {
 #pragma unroll
-    for (int i = 0; i < ACH; i++)
-      ra[i] = aoff[i] >= 0 ? *(const i32x4*)(x + aoff[i] + k0) : i32x4{0, 0, 0, 0};
+    for (int i = 0; i < ACH; i++) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, aoff[i] + k0 * 2, 0, 0);
 #pragma unroll
-    for (int i = 0; i < BCH; i++) rb[i] = *(const i32x4*)(wbase + boff[i] + k0);
+    for (int i = 0; i < BCH; i++)   // weights are streamed once: keep them out of L2's reuse set
+      rb[i] = __builtin_nontemporal_load((const i32x4*)(wbase + boff[i] + k0));
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](const i32x4 (&ra)[ACH], const i32x4 (&rb)[BCH], int buf) {
     uint8_t* A = lds + buf * L::STAGE;
     uint8_t* B = A + L::A_BYTES;
 #pragma unroll
@@ -144,35 +154,62 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_kernel(GemmArgs a) {
     if ((2 * i + wm) * 32 < mvalid) mb_active = i + 1;
 
   const int l32 = lane & 31, khalf = lane >> 5;
-  const int nk = K / GB_BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt++) {
-    if (kt + 1 < nk) gload((kt + 1) * GB_BK);
-    const uint8_t* A = lds + (kt & 1) * L::STAGE;
+  // One K step from LDS buffer `buf` with NA active m-blocks, NA a compile-time
+  // count: straight-line code, all LDS reads of a k-substep ahead of its MFMAs.
+  auto compute_na = [&](auto na_tag, int buf) __attribute__((always_inline)) {
+    constexpr int NA = decltype(na_tag)::value;
+    const uint8_t* A = lds + buf * L::STAGE;
     const uint8_t* B = A + L::A_BYTES;
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
       const int ch = ks * 2 + khalf;
-      bf16x8 bfr[2];
+      bf16x8 bfr[2], afr[NA > 0 ? NA : 1];
 #pragma unroll
       for (int j = 0; j < 2; j++) {
         const int brow = (SWIGLU ? j * 64 + wn * 32 : wn * 64 + j * 32) + l32;
         bfr[j] = *(const bf16x8*)(B + swz(brow, ch));
       }
 #pragma unroll
-      for (int i = 0; i < MB; i++) {
-        if (i < mb_active) {
-          const int arow = (2 * i + wm) * 32 + l32;
-          const bf16x8 afr = *(const bf16x8*)(A + swz(arow, ch));
-          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[0], acc[i][0], 0, 0, 0);
-          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[1], acc[i][1], 0, 0, 0);
-        }
+      for (int i = 0; i < NA; i++) afr[i] = *(const bf16x8*)(A + swz((2 * i + wm) * 32 + l32, ch));
+#pragma unroll
+      for (int i = 0; i < NA; i++) {
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[i], bfr[0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[i], bfr[1], acc[i][1], 0, 0, 0);
       }
     }
-    if (kt + 1 < nk) sstore((kt + 1) & 1);
+  };
+  // Every load and LDS store in the K loop is unconditional (the trailing
+  // prefetches re-read the last step): with no branch around a memory op the
+  // compiler's wait counting stays in order and each LDS store waits only for
+  // its own register set.
+  const int nk = K / GB_BK;
+  auto k_loop = [&](auto na_tag) __attribute__((always_inline)) {
+    gload(ra0, rb0, 0);
+    gload(ra1, rb1, min(1, nk - 1) * GB_BK);
+    sstore(ra0, rb0, 0);
     __syncthreads();
+    for (int kt = 0; kt < (nk & ~1); kt += 2) {
+      // even half: LDS buf 0 holds step kt, set 1 holds kt+1, set 0 receives kt+2
+      gload(ra0, rb0, min(kt + 2, nk - 1) * GB_BK);
+      compute_na(na_tag, 0);
+      sstore(ra1, rb1, 1);
+      __syncthreads();
+      // odd half: LDS buf 1 holds kt+1, set 0 holds kt+2, set 1 receives kt+3
+      gload(ra1, rb1, min(kt + 3, nk - 1) * GB_BK);
+      compute_na(na_tag, 1);
+      sstore(ra0, rb0, 0);
+      __syncthreads();
+    }
+    if (nk & 1) compute_na(na_tag, 0);   // odd step count: buf 0 holds the last step
+  };
+  // mb_active is the same in every lane of the wave: branch once, outside the loop
+  switch (__builtin_amdgcn_readfirstlane(mb_active)) {
+    case 0: k_loop(std::integral_constant<int, 0>{}); break;
+    case 1: k_loop(std::integral_constant<int, 1>{}); break;
+    case 2: k_loop(std::integral_constant<int, 2>{}); break;
+    case 3: k_loop(std::integral_constant<int, (MB >= 3 ? 3 : MB)>{}); break;
+    case 4: k_loop(std::integral_constant<int, (MB >= 4 ? 4 : MB)>{}); break;
+    default: k_loop(std::integral_constant<int, MB>{}); break;
   }
 
   // ---- epilogue: D element (8*(r>>2) + 4*(lane>>5) + (r&3), lane&31) in register r
@@ -240,7 +277,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 }
 
 int gemm_bm(int dtype, int mean_rows) {
-  (void)dtype;
+  // The FP8 tile keeps its accumulators in VGPRs (the per-block scale fold is
+  // VALU work), so it is 128 rows tall to leave the MFMA operands room in VGPRs.
+  if (dtype == MOE_FP8_E4M3) return 128;
   // one m-tile per expert when the mean load (+4 sigma of a binomial load) fits
   const int need = mean_rows + 4 * (int)std::sqrt((double)(mean_rows > 0 ? mean_rows : 1));
   if (need <= 256) return 256;
@@ -251,7 +290,7 @@ template <int MB, bool SWIGLU>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   const int n_tiles = SWIGLU ? a.N / 64 : a.N / GB_BN;
   const long mtiles_bound = (long)a.rows_bound / (64 * MB) + a.n_seg;
-  const long grid = mtiles_bound * n_tiles;
+  const long grid = (mtiles_bound * n_tiles + 7) / 8 * 8;   // a multiple of the 8 XCDs
   if (grid <= 0) return hipSuccess;
   auto k = gemm_bf16_kernel<MB, SWIGLU>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,

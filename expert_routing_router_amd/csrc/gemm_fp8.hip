@@ -11,6 +11,7 @@
 // Tiling, ragged segments and the SwiGLU epilogue follow the bf16 kernel.
 #include "common.h"
 #include "moe_internal.h"
+#include <type_traits>
 
 namespace moe {
 
@@ -63,7 +64,15 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
   __syncthreads();
   const int n_tiles = SWIGLU ? a.N / 64 : a.N / GF_BN;
   int seg, ntile, mtile;
-  if (!decode_tile8(sprefix, a.n_seg, n_tiles, blockIdx.x, seg, ntile, mtile)) return;
+  // Workgroup i runs on XCD i % 8, and each XCD starts its workgroups in order of i.
+  // Give XCD x the contiguous logical range [x*per, (x+1)*per): the tiles of one
+  // expert (all its n-tiles) then run side by side on one XCD and share the
+  // expert's gathered rows in that XCD's L2.
+  const int total_tiles = sprefix[a.n_seg] * n_tiles;
+  const int per_xcd = (total_tiles + 7) >> 3;
+  const int lt = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd) return;
+  if (!decode_tile8(sprefix, a.n_seg, n_tiles, lt, seg, ntile, mtile)) return;
 
   const int row0 = a.offsets[seg] + mtile * BM;
   const int mvalid = min(BM, a.offsets[seg + 1] - row0);
@@ -72,18 +81,27 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
   const uint8_t* wbase = first ? (const uint8_t*)a.w0 + (size_t)seg * a.wstride0
                                : (const uint8_t*)a.w1 + (size_t)(seg - a.n_first) * a.wstride1;
   const float* wsc = first ? a.ws0 + (size_t)seg * a.sstride0 : a.ws1 + (size_t)(seg - a.n_first) * a.sstride1;
-  const uint8_t* x = (const uint8_t*)a.x;
 
   for (int r = tid; r < BM; r += GF_THREADS)
     srow[r] = r < mvalid ? (a.row_index ? a.row_index[row0 + r] : row0 + r) : -1;
   __syncthreads();
 
   const int cch = tid & 7, rbase = tid >> 3;
+  // rows past the segment (and scale slots past BM) load zeros through out-of-range offsets
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_rows * (long)K);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.x_scale, a.x_rows * (long)KB * 4);
   int aoff[ACH];
 #pragma unroll
   for (int i = 0; i < ACH; i++) {
     const int src = srow[rbase + 32 * i];
-    aoff[i] = src >= 0 ? src * K + cch * 16 : -1;
+    aoff[i] = src >= 0 ? src * K + cch * 16 : kOutOfRange;
+  }
+  int soff[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int r = tid + i * GF_THREADS;
+    const int src = r < BM ? srow[r] : -1;
+    soff[i] = src >= 0 ? src * KB * 4 : kOutOfRange;
   }
   int boff[BCH];
 #pragma unroll
@@ -101,23 +119,21 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
     wblk[j] = wrow / 128;
   }
 
+  // One register set for the next K block (the accumulators live in VGPRs
+  // here because the scale fold is VALU work, which leaves no room for two).
   i32x4 ra[ACH], rb[BCH];
-  float rsa[2];
-  auto gload = [&](int kb) {
+  float rs[2];
+  auto gload = [&](int kb) __attribute__((always_inline)) {
     const int k0 = kb * GF_BK;
 #pragma unroll
-    for (int i = 0; i < ACH; i++)
-      ra[i] = aoff[i] >= 0 ? *(const i32x4*)(x + aoff[i] + k0) : i32x4{0, 0, 0, 0};
+    for (int i = 0; i < ACH; i++) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, aoff[i] + k0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < BCH; i++) rb[i] = *(const i32x4*)(wbase + boff[i] + k0);
+    for (int i = 0; i < BCH; i++) rb[i] = __builtin_nontemporal_load((const i32x4*)(wbase + boff[i] + k0));
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-      const int r = tid + i * GF_THREADS;
-      rsa[i] = 0.f;
-      if (r < BM && srow[r] >= 0) rsa[i] = a.x_scale[(size_t)srow[r] * KB + kb];
-    }
+    for (int i = 0; i < 2; i++)
+      rs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, soff[i] + kb * 4, 0, 0));
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf) __attribute__((always_inline)) {
     uint8_t* A = lds + buf * L::STAGE;
     uint8_t* B = A + L::A_BYTES;
     float* SA = (float*)(B + L::B_BYTES);
@@ -128,7 +144,7 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       const int r = tid + i * GF_THREADS;
-      if (r < BM) SA[r] = rsa[i];
+      if (r < BM) SA[r] = rs[i];
     }
   };
 
@@ -145,34 +161,36 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
     if ((2 * i + wm) * 32 < mvalid) mb_active = i + 1;
 
   const int l32 = lane & 31, khalf = lane >> 5;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kb = 0; kb < KB; kb++) {
-    if (kb + 1 < KB) gload(kb + 1);
-    const uint8_t* A = lds + (kb & 1) * L::STAGE;
+  // One 128-wide K block from LDS buffer `buf` with NA active m-blocks: for
+  // each 32x32 block, two MFMAs into a fresh fp32 partial, then the scale fold.
+  auto compute_na = [&](auto na_tag, int buf, int kb) __attribute__((always_inline)) {
+    constexpr int NA = decltype(na_tag)::value;
+    const uint8_t* A = lds + buf * L::STAGE;
     const uint8_t* B = A + L::A_BYTES;
     const float* SA = (const float*)(B + L::B_BYTES);
-    const float sw0 = wsc[(size_t)wblk[0] * KB + kb];
-    const float sw1 = wsc[(size_t)wblk[1] * KB + kb];
-    i32x8 bfr[2][2];
 #pragma unroll
-    for (int h = 0; h < 2; h++)
+    for (int j = 0; j < 2; j++) {
+      const float sw = wsc[(size_t)wblk[j] * KB + kb];
+      const int brow = (SWIGLU ? j * 64 + wn * 32 : wn * 64 + j * 32) + l32;
+      i32x8 bfr[2];
 #pragma unroll
-      for (int j = 0; j < 2; j++) {
-        const int brow = (SWIGLU ? j * 64 + wn * 32 : wn * 64 + j * 32) + l32;
+      for (int h = 0; h < 2; h++) {
         const int c0 = h * 4 + khalf * 2;
         const i32x4 lo = *(const i32x4*)(B + swz8(brow, c0));
         const i32x4 hi = *(const i32x4*)(B + swz8(brow, c0 + 1));
-        bfr[h][j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        bfr[h] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
 #pragma unroll
-    for (int i = 0; i < MB; i++) {
-      if (i < mb_active) {
+      for (int i = 0; i < NA; i++) {
         const int arow = (2 * i + wm) * 32 + l32;
-        f32x16 p0, p1;
+        // Each partial starts from its own zero (0 * acc, which the compiler can
+        // neither fold nor share between blocks), so C dies at the first MFMA
+        // and the accumulate form with D tied to C is used. With a shared or
+        // constant C the compiler may give the MFMA a destination overlapping
+        // its A operand, and this multi-pass instruction then returns garbage.
+        f32x16 p;
 #pragma unroll
-        for (int r = 0; r < 16; r++) { p0[r] = 0.f; p1[r] = 0.f; }
+        for (int r = 0; r < 16; r++) p[r] = acc[i][j][r] * a.fzero;
 #pragma unroll
         for (int h = 0; h < 2; h++) {
           const int c0 = h * 4 + khalf * 2;
@@ -180,20 +198,35 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
           const i32x4 hi = *(const i32x4*)(A + swz8(arow, c0 + 1));
           const i32x8 afr = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           // cbsz = blgp = 0: both operands E4M3; scale exponents 127 = 2^0
-          p0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr, bfr[h][0], p0, 0, 0, 0, 127, 0, 127);
-          p1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr, bfr[h][1], p1, 0, 0, 0, 127, 0, 127);
+          p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr, bfr[h], p, 0, 0, 0, 127, 0, 127);
         }
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-          const float sa = SA[row];
-          acc[i][0][r] += p0[r] * (sa * sw0);
-          acc[i][1][r] += p1[r] * (sa * sw1);
+          acc[i][j][r] += p[r] * (SA[row] * sw);
         }
+        // one partial live at a time
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (kb + 1 < KB) sstore((kb + 1) & 1);
+  };
+
+  auto k_loop = [&](auto na_tag) __attribute__((always_inline)) {
+    gload(0);
+    sstore(0);
     __syncthreads();
+    for (int kb = 0; kb < KB; kb++) {
+      gload(min(kb + 1, KB - 1));        // unconditional: in-order wait counting
+      compute_na(na_tag, kb & 1, kb);
+      sstore((kb + 1) & 1);
+      __syncthreads();
+    }
+  };
+  switch (__builtin_amdgcn_readfirstlane(mb_active)) {
+    case 0: break;
+    case 1: k_loop(std::integral_constant<int, 1>{}); break;
+    case 2: k_loop(std::integral_constant<int, 2>{}); break;
+    default: k_loop(std::integral_constant<int, MB>{}); break;
   }
 
   // GEMM1 writes H in fp32 (it is re-quantised to E4M3 per 1x128 tile next);
@@ -223,7 +256,7 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
 template <int MB, bool SWIGLU>
 static hipError_t launch_fp8_t(const GemmArgs& a, hipStream_t s) {
   const int n_tiles = SWIGLU ? a.N / 64 : a.N / GF_BN;
-  const long grid = ((long)a.rows_bound / (64 * MB) + a.n_seg) * n_tiles;
+  const long grid = (((long)a.rows_bound / (64 * MB) + a.n_seg) * n_tiles + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
   auto k = gemm_fp8_kernel<MB, SWIGLU>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -234,8 +267,7 @@ static hipError_t launch_fp8_t(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, bool swiglu, int bm, hipStream_t s) {
-  if (bm == 256) return swiglu ? launch_fp8_t<4, true>(a, s) : launch_fp8_t<4, false>(a, s);
-  if (bm == 320) return swiglu ? launch_fp8_t<5, true>(a, s) : launch_fp8_t<5, false>(a, s);
+  if (bm == 128) return swiglu ? launch_fp8_t<2, true>(a, s) : launch_fp8_t<2, false>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -129,7 +129,8 @@ extern "C" int moe_validate(const moe_desc_t* d) {
   const long rows = (long)d->T * d->top_k + (long)d->n_shared * d->T;
   const long wide = d->d > d->inter ? d->d : d->inter;
   const long wide2 = d->inter_shared > wide ? d->inter_shared : wide;
-  if (rows * wide2 >= (1L << 31) || (long)d->T * d->d >= (1L << 31)) return MOE_ENOTSUP;
+  // byte offsets of 2-byte rows stay below 2^31 (buffer-load range and int offsets)
+  if (rows * wide2 >= (1L << 30) || (long)d->T * d->d >= (1L << 30)) return MOE_ENOTSUP;
   return MOE_OK;
 }
 
@@ -196,7 +197,7 @@ extern "C" size_t moe_expert_ffn_workspace_bytes(const moe_desc_t* d, int32_t n_
 }
 
 static int route_front(const moe_desc_t* d) {
-  const bool mfma_ok = d->in_dtype == MOE_BF16 && d->n_routed % 16 == 0 && d->d % 32 == 0;
+  const bool mfma_ok = d->in_dtype == MOE_BF16 && d->n_routed % 16 == 0 && d->d % 128 == 0;
   if (!mfma_ok) return kFrontF64;
   return d->router_dtype == MOE_BF16 ? kFrontMfma : kFrontMfmaSplitE;
 }
@@ -262,19 +263,20 @@ extern "C" int moe_permute(const moe_desc_t* d, const int32_t* topk_idx, int32_t
   return MOE_OK;
 }
 
-static GemmArgs gemm_args(const void* x, const float* xs, const int32_t* ridx, const int32_t* offsets,
-                          const int32_t* mtile, int n_seg, const void* w0, const float* s0, long ws0,
-                          long ss0, void* out, int N, int K, int rows_bound) {
+static GemmArgs gemm_args(const void* x, long x_rows, const float* xs, const int32_t* ridx,
+                          const int32_t* offsets, const int32_t* mtile, int n_seg, const void* w0,
+                          const float* s0, long ws0, long ss0, void* out, int N, int K, int rows_bound) {
   GemmArgs g;
-  g.x = x; g.x_scale = xs; g.row_index = ridx; g.offsets = offsets; g.mtile_prefix = mtile;
+  g.x = x; g.x_rows = x_rows; g.x_scale = xs; g.row_index = ridx; g.offsets = offsets; g.mtile_prefix = mtile;
   g.n_seg = n_seg; g.w0 = w0; g.w1 = w0; g.wstride0 = ws0; g.wstride1 = ws0;
   g.ws0 = s0; g.ws1 = s0; g.sstride0 = ss0; g.sstride1 = ss0; g.n_first = n_seg;
   g.out = out; g.N = N; g.K = K; g.rows_bound = rows_bound;
+  g.fzero = 0.0f;
   return g;
 }
 
 // GEMM1 + (FP8: quantise H) + GEMM2 over one set of segments.
-static int run_ffn(const moe_desc_t* d, int inter, const void* x, const float* xs, const int32_t* ridx,
+static int run_ffn(const moe_desc_t* d, int inter, const void* x, long x_rows, const float* xs, const int32_t* ridx,
                    const int32_t* offsets, const int32_t* mtile, int n_seg, int rows_bound,
                    const void* w13, const float* s13, const void* w13b, const float* s13b,
                    const void* w2, const float* s2, const void* w2b, const float* s2b, int n_first,
@@ -283,7 +285,8 @@ static int run_ffn(const moe_desc_t* d, int inter, const void* x, const float* x
   const bool f8 = dt == MOE_FP8_E4M3;
   const long ws13 = 2L * inter * d->d, ws2 = (long)d->d * inter;
   const long ss13 = f8 ? (2L * inter / 128) * (d->d / 128) : 0, ss2 = f8 ? (long)(d->d / 128) * (inter / 128) : 0;
-  GemmArgs g1 = gemm_args(x, xs, ridx, offsets, mtile, n_seg, w13, s13, ws13, ss13, H, inter, d->d, rows_bound);
+  GemmArgs g1 = gemm_args(x, x_rows, xs, ridx, offsets, mtile, n_seg, w13, s13, ws13, ss13, H, inter, d->d,
+                          rows_bound);
   g1.w1 = w13b; g1.ws1 = s13b; g1.n_first = n_first;
   MOE_TRY(launch_gemm_swiglu(g1, dt, bm, s));
   prof_mark(MOE_STAGE_GEMM1, s);
@@ -294,7 +297,8 @@ static int run_ffn(const moe_desc_t* d, int inter, const void* x, const float* x
     x2 = qh;
     xs2 = sh;
   }
-  GemmArgs g2 = gemm_args(x2, xs2, nullptr, offsets, mtile, n_seg, w2, s2, ws2, ss2, Y, d->d, inter, rows_bound);
+  GemmArgs g2 = gemm_args(x2, rows_bound, xs2, nullptr, offsets, mtile, n_seg, w2, s2, ws2, ss2, Y, d->d, inter,
+                          rows_bound);
   g2.w1 = w2b; g2.ws1 = s2b; g2.n_first = n_first;
   MOE_TRY(launch_gemm_down(g2, dt, bm, s));
   prof_mark(MOE_STAGE_GEMM2, s);
@@ -312,7 +316,7 @@ extern "C" int moe_expert_ffn(const moe_desc_t* d, int32_t n_experts, int32_t in
   const bool f8 = d->expert_dtype == MOE_FP8_E4M3;
   if (d->expert_dtype == MOE_BF16 && inter % 64) return MOE_ENOTSUP;
   if (f8 && inter % 128) return MOE_ENOTSUP;
-  if ((long)rows * (d->d > inter ? d->d : inter) >= (1L << 31)) return MOE_ENOTSUP;
+  if ((long)rows * (d->d > inter ? d->d : inter) >= (1L << 30)) return MOE_ENOTSUP;
   if (!aligned(x) || !aligned(offsets) || !aligned(w13) || !aligned(w2) || !aligned(y) || !aligned(ws))
     return MOE_EINVAL;
   if (!aligned_or_null(row_token)) return MOE_EINVAL;
@@ -331,7 +335,8 @@ extern "C" int moe_expert_ffn(const moe_desc_t* d, int32_t n_experts, int32_t in
   float* sh = f8 ? (float*)(base + o) : nullptr;
   const int bm = gemm_bm(d->expert_dtype, rows / n_experts);
   if (d->expert_dtype != MOE_F32) MOE_TRY(launch_mtile_prefix(offsets, n_experts, bm, mtile, s));
-  return run_ffn(d, inter, x, x_scale, row_token, offsets, mtile, n_experts, rows, w13, w13_scale, w13,
+  return run_ffn(d, inter, x, row_token ? (long)d->T : (long)rows, x_scale, row_token, offsets, mtile, n_experts,
+                 rows, w13, w13_scale, w13,
                  w13_scale, w2, w2_scale, w2, w2_scale, n_experts, H, qh, sh, y, bm, s);
 }
 
@@ -433,14 +438,14 @@ extern "C" int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const vo
   // 4. experts
   const void* y_shared = nullptr;
   if (fused) {
-    int st2 = run_ffn(d, d->inter, x, xs, row_token, offsets, mtile, N + Ns, (int)(TK + (long)Ns * T),
+    int st2 = run_ffn(d, d->inter, x, T, xs, row_token, offsets, mtile, N + Ns, (int)(TK + (long)Ns * T),
                       w->w13, w->w13_scale, Ns ? w->w13_shared : w->w13, Ns ? w->w13_shared_scale : w->w13_scale,
                       w->w2, w->w2_scale, Ns ? w->w2_shared : w->w2, Ns ? w->w2_shared_scale : w->w2_scale, N,
                       H, qh, shs, Y, bm, s);
     if (st2) return st2;
     if (Ns) y_shared = Y + (size_t)TK * d->d * yy;
   } else {
-    int st2 = run_ffn(d, d->inter, x, xs, row_token, offsets, mtile, N, (int)TK, w->w13, w->w13_scale, w->w13,
+    int st2 = run_ffn(d, d->inter, x, T, xs, row_token, offsets, mtile, N, (int)TK, w->w13, w->w13_scale, w->w13,
                       w->w13_scale, w->w2, w->w2_scale, w->w2, w->w2_scale, N, H, qh, shs, Y, bm, s);
     if (st2) return st2;
     int32_t* offs_s = (int32_t*)(base + L.offs_s);
@@ -453,7 +458,7 @@ extern "C" int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const vo
     uint8_t* Ys = Y + (size_t)TK * d->d * yy;
     uint8_t* qhs = f8 ? qh + (size_t)TK * d->inter : nullptr;
     float* shss = f8 ? shs + (size_t)TK * (d->inter / 128) : nullptr;
-    st2 = run_ffn(d, d->inter_shared, x, xs, row_token + TK, offs_s, mtile_s, Ns, Ns * T, w->w13_shared,
+    st2 = run_ffn(d, d->inter_shared, x, T, xs, row_token + TK, offs_s, mtile_s, Ns, Ns * T, w->w13_shared,
                   w->w13_shared_scale, w->w13_shared, w->w13_shared_scale, w->w2_shared, w->w2_shared_scale,
                   w->w2_shared, w->w2_shared_scale, Ns, Hs, qhs, shss, Ys, bms, s);
     if (st2) return st2;

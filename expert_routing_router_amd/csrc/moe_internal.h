@@ -40,6 +40,7 @@ hipError_t launch_mtile_prefix(const int32_t* offsets, int n_seg, int bm, int32_
 // Segment e uses weights (e < n_first ? w0 + e*stride0 : w1 + (e-n_first)*stride1).
 struct GemmArgs {
   const void* x;              // A source rows (through row_index when not null)
+  long x_rows;                // rows of x (for the buffer-load range check)
   const float* x_scale;       // FP8: [.., K/128] per source row
   const int32_t* row_index;   // nullable
   const int32_t* offsets;     // [n_seg+1]
@@ -52,6 +53,7 @@ struct GemmArgs {
   int N;                      // output columns (I for the SwiGLU GEMM, d for down)
   int K;                      // reduction length
   int rows_bound;             // upper bound on total rows (grid sizing)
+  float fzero;                // 0.0f, opaque to the compiler (fresh MFMA partials start from it)
 };
 int gemm_bm(int dtype, int mean_rows);
 hipError_t launch_gemm_swiglu(const GemmArgs& a, int dtype, int bm, hipStream_t s);

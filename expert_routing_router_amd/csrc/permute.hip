@@ -37,43 +37,80 @@ __global__ __launch_bounds__(256) void bitmap_kernel(const int32_t* __restrict__
     for (int e = lane; e < N; e += 64) bitmap[(size_t)w * N + e] = words[wave][e];
 }
 
-// One workgroup: per-expert word prefix, loads, offsets (+ identity segments
-// for the shared experts appended after the routed rows), m-tile prefix.
+// Inclusive prefix sum over one workgroup of 256 threads (4 waves).
+__device__ __forceinline__ int block_inclusive_scan(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; w++) base += wsum[w];
+  __syncthreads();
+  return v + base;
+}
+
+// One workgroup: per-expert word prefix and load, then offsets over the
+// segments (routed experts, then identity segments of T rows for the shared
+// experts) and the prefix of m-tiles of `bm` rows per segment.
 __global__ __launch_bounds__(256) void scan_kernel(const uint64_t* __restrict__ bitmap, int T, int K,
                                                    int N, int n_extra, int32_t* __restrict__ wprefix,
                                                    int32_t* __restrict__ offsets,
                                                    int32_t* __restrict__ counts_out,
                                                    int32_t* __restrict__ mtile_prefix, int bm) {
-  __shared__ int32_t sc[PM_NMAX + 64];
-  __shared__ int32_t sm[PM_NMAX + 64];
+  __shared__ int wsum[4];
   const int tid = threadIdx.x;
   const int W = cdiv(T, 64);
   const int n_seg = N + n_extra;
   int c = 0;
   if (tid < N) {
-    for (int w = 0; w < W; w++) {
+    int w = 0;
+    for (; w + 8 <= W; w += 8) {          // eight independent loads in flight
+      uint64_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) v[i] = bitmap[(size_t)(w + i) * N + tid];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        wprefix[(size_t)(w + i) * N + tid] = c;
+        c += __popcll(v[i]);
+      }
+    }
+    for (; w < W; w++) {
       wprefix[(size_t)w * N + tid] = c;
       c += __popcll(bitmap[(size_t)w * N + tid]);
     }
     if (counts_out) counts_out[tid] = c;
   }
-  for (int e = tid; e < n_seg; e += 256) {
-    const int n = e < N ? (e == tid ? c : 0) : T;
-    sc[e] = n;
-    sm[e] = bm > 0 ? cdiv(n, bm) : 0;
+  // each thread owns segments 2*tid and 2*tid+1 (n_seg <= 320 < 512)
+  int n[2], m[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int e = 2 * tid + i;
+    n[i] = e < N ? 0 : (e < n_seg ? T : 0);
   }
+  __shared__ int sc[512];
+  if (tid < N) sc[tid] = c;
   __syncthreads();
-  if (tid == 0) {   // n_seg <= 320: a serial scan is cheaper than a tree here
-    int acc = 0, accm = 0;
-    for (int e = 0; e < n_seg; e++) {
-      const int n = sc[e], m = sm[e];
-      offsets[e] = acc;
-      if (mtile_prefix) mtile_prefix[e] = accm;
-      acc += n;
-      accm += m;
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int e = 2 * tid + i;
+    if (e < N) n[i] = sc[e];
+    m[i] = bm > 0 ? cdiv(n[i], bm) : 0;
+  }
+  const int n_inc = block_inclusive_scan(n[0] + n[1], wsum);
+  const int m_inc = block_inclusive_scan(m[0] + m[1], wsum);
+  const int n_exc = n_inc - n[0] - n[1], m_exc = m_inc - m[0] - m[1];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int e = 2 * tid + i;
+    const int no = n_exc + (i ? n[0] : 0), mo = m_exc + (i ? m[0] : 0);
+    if (e <= n_seg) {
+      offsets[e] = no;
+      if (mtile_prefix) mtile_prefix[e] = mo;
     }
-    offsets[n_seg] = acc;
-    if (mtile_prefix) mtile_prefix[n_seg] = accm;
   }
 }
 

@@ -15,19 +15,24 @@
 // the production selection.
 //
 // Precision: the MFMA front end accumulates bf16 products (exact in fp32) in
-// fp32 over 512-element chunks of d and sums the chunks in fp64; the sigmoid
+// fp32 over 64-element chunks of d and sums the chunks in fp64; the sigmoid
 // is evaluated in fp64 and rounded once to fp32. fp32 centroids are split into
 // three bf16 terms (hi + mid + lo reproduces the fp32 value exactly), so the
-// products stay exact on the bf16 MFMA path.
+// products stay exact on the bf16 MFMA path; the hi products and the much
+// smaller mid+lo products go to separate accumulators so the small terms are
+// not rounded against the large running sum.
 #include "common.h"
 #include "moe_internal.h"
+#include <type_traits>
+
+extern "C" __device__ unsigned int __ockl_wfred_max_u32(unsigned int);
+extern "C" __device__ unsigned int __ockl_wfred_min_u32(unsigned int);
 
 namespace moe {
 
 constexpr int RT_BT = 32;
 constexpr int RT_THREADS = 256;
 constexpr int RT_NMAX = 256;
-constexpr int RT_CHUNK = 512;
 constexpr int RT_QMAX = 8;
 
 struct RouterLds {
@@ -61,6 +66,16 @@ __device__ __forceinline__ void split3(const float* x, bf16x8& hi, bf16x8& mid, 
 // ---------------------------------------------------------------- front ends
 // MFMA 16x16x32 bf16: lane l holds A row (l&15), B column (l&15), 8 k-values
 // at k-group (l>>4); D element (4*(l>>4)+r, l&15) in register r.
+// Wave w owns expert blocks w, w+4, ... (16 experts each) for all 32 tokens.
+// Fragments are loaded straight from global memory three k-steps ahead of
+// their MFMAs (four rotating register sets); every two k-steps the fp32 MFMA
+// sums are flushed into fp64 accumulators.
+template <bool SPLIT_E>
+struct RouterFrag {
+  bf16x8 a0, a1;
+  typename std::conditional<SPLIT_E, f32x4, bf16x8>::type b[4][SPLIT_E ? 2 : 1];
+};
+
 template <bool SPLIT_E>
 __device__ void front_mfma(const RouteArgs& a, RouterLds& sh, int t0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -71,6 +86,33 @@ __device__ void front_mfma(const RouteArgs& a, RouterLds& sh, int t0) {
   const int ta0 = min(t0 + r16, a.T - 1), ta1 = min(t0 + 16 + r16, a.T - 1);
   const uint16_t* pa0 = u + (size_t)ta0 * a.d + kg * 8;
   const uint16_t* pa1 = u + (size_t)ta1 * a.d + kg * 8;
+  // B rows of this wave's blocks (blocks past nblk re-read block `wave`: loads stay in bounds)
+  const uint16_t* pb16[4];
+  const float* pb32[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int blk = j < nb ? wave + 4 * j : wave;
+    const size_t row = (size_t)((blk << 4) + r16) * a.d + kg * 8;
+    pb16[j] = (const uint16_t*)a.E + row;
+    pb32[j] = (const float*)a.E + row;
+  }
+  const int nsteps = a.d >> 5;     // d % 128 == 0 on this path
+
+  RouterFrag<SPLIT_E> f[4];
+  auto load = [&](RouterFrag<SPLIT_E>& g, int step) __attribute__((always_inline)) {
+    const int k = min(step, nsteps - 1) << 5;
+    g.a0 = *(const bf16x8*)(pa0 + k);
+    g.a1 = *(const bf16x8*)(pa1 + k);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      if (!SPLIT_E) {
+        *(bf16x8*)&g.b[j][0] = *(const bf16x8*)(pb16[j] + k);
+      } else {
+        *(f32x4*)&g.b[j][0] = *(const f32x4*)(pb32[j] + k);
+        *(f32x4*)&g.b[j][1] = *(const f32x4*)(pb32[j] + k + 4);
+      }
+    }
+  };
 
   double z64[2][4][4];
 #pragma unroll
@@ -79,49 +121,65 @@ __device__ void front_mfma(const RouteArgs& a, RouterLds& sh, int t0) {
     for (int j = 0; j < 4; j++)
 #pragma unroll
       for (int r = 0; r < 4; r++) z64[m][j][r] = 0.0;
-
-  for (int kc = 0; kc < a.d; kc += RT_CHUNK) {
-    const int kend = min(kc + RT_CHUNK, a.d);
-    f32x4 acc[2][4];
+  f32x4 acc[2][4], acs[2][4];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < 2; m++)
 #pragma unroll
-      for (int j = 0; j < 4; j++) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int k = kc; k < kend; k += 32) {
-      const bf16x8 A0 = *(const bf16x8*)(pa0 + k);
-      const bf16x8 A1 = *(const bf16x8*)(pa1 + k);
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        if (j < nb) {
-          const int e = ((wave + 4 * j) << 4) + r16;
-          if (!SPLIT_E) {
-            const bf16x8 B = *(const bf16x8*)((const uint16_t*)a.E + (size_t)e * a.d + k + kg * 8);
-            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, acc[0][j], 0, 0, 0);
-            acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, acc[1][j], 0, 0, 0);
-          } else {
-            const float* pe = (const float*)a.E + (size_t)e * a.d + k + kg * 8;
-            float x[8];
-            *(f32x4*)&x[0] = *(const f32x4*)pe;
-            *(f32x4*)&x[4] = *(const f32x4*)(pe + 4);
-            bf16x8 h, md, lo;
-            split3(x, h, md, lo);
-            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, lo, acc[0][j], 0, 0, 0);
-            acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, lo, acc[1][j], 0, 0, 0);
-            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, md, acc[0][j], 0, 0, 0);
-            acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, md, acc[1][j], 0, 0, 0);
-            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, h, acc[0][j], 0, 0, 0);
-            acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, h, acc[1][j], 0, 0, 0);
-          }
-        }
-      }
-    }
+      for (int j = 0; j < 4; j++) acc[m][j] = acs[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto flush = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < 2; m++)
 #pragma unroll
       for (int j = 0; j < 4; j++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) z64[m][j][r] += (double)acc[m][j][r];
+        for (int r = 0; r < 4; r++) {
+          z64[m][j][r] += (double)acc[m][j][r];
+          if (SPLIT_E) z64[m][j][r] += (double)acs[m][j][r];
+        }
+  };
+  auto mfma = [&](const RouterFrag<SPLIT_E>& g) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      if (j < nb) {
+        if (!SPLIT_E) {
+          const bf16x8 B = *(const bf16x8*)&g.b[j][0];
+          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a0, B, acc[0][j], 0, 0, 0);
+          acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a1, B, acc[1][j], 0, 0, 0);
+        } else {
+          float x[8];
+          *(f32x4*)&x[0] = *(const f32x4*)&g.b[j][0];
+          *(f32x4*)&x[4] = *(const f32x4*)&g.b[j][1];
+          bf16x8 h, md, lo;
+          split3(x, h, md, lo);
+          acs[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a0, lo, acs[0][j], 0, 0, 0);
+          acs[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a1, lo, acs[1][j], 0, 0, 0);
+          acs[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a0, md, acs[0][j], 0, 0, 0);
+          acs[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a1, md, acs[1][j], 0, 0, 0);
+          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a0, h, acc[0][j], 0, 0, 0);
+          acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a1, h, acc[1][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  load(f[0], 0);
+  load(f[1], 1);
+  load(f[2], 2);
+  for (int s0 = 0; s0 < nsteps; s0 += 4) {      // nsteps % 4 == 0
+    load(f[3], s0 + 3);
+    zero_acc();
+    mfma(f[0]);
+    load(f[0], s0 + 4);
+    mfma(f[1]);
+    flush();
+    load(f[1], s0 + 5);
+    zero_acc();
+    mfma(f[2]);
+    load(f[2], s0 + 6);
+    mfma(f[3]);
+    flush();
   }
 #pragma unroll
   for (int m = 0; m < 2; m++)
@@ -150,21 +208,24 @@ __device__ void front_f64(const RouteArgs& a, RouterLds& sh, int t0, int nt) {
 }
 
 // ---------------------------------------------------------------- selection
-// One wave per token. Expert e lives in lane (e & 63), slot (e >> 6).
+// One wave per token. Expert e lives in lane (e & 63), slot (e >> 6). Each
+// selection round is two wave reductions (device-library, DPP based): the
+// largest ordered key, then the lowest expert index holding it -- the total
+// order (key desc, index asc); -0 and +0 share one ordered key.
 __device__ void select_tokens(const RouteArgs& a, RouterLds& sh, int t0, int nt) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int N = a.n_routed, K = a.top_k, G = a.n_groups, M = a.topk_groups, q = a.group_topk;
   const int S = N / G;
   for (int t = wave; t < nt; t += RT_THREADS / kWave) {
     const float* srow = sh.s[t];
-    uint64_t pk[4];
+    uint32_t ok[4];                       // ordered keys; 0 = not a candidate
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int e = lane + 64 * j;
-      pk[j] = e < N ? rank_key(srow[e] + sh.b[e], (uint32_t)e) : 0ull;
+      ok[j] = e < N ? ordered_f32(srow[e] + sh.b[e]) : 0u;
     }
     if (G > 1) {
-      uint64_t gk = 0ull;
+      uint32_t gk = 0u;
       if (lane < G) {
         float top[RT_QMAX];
 #pragma unroll
@@ -181,29 +242,33 @@ __device__ void select_tokens(const RouteArgs& a, RouterLds& sh, int t0, int nt)
 #pragma unroll
         for (int j = 1; j < RT_QMAX; j++)
           if (j < q) acc = acc + top[j];                    // fp32, largest first
-        gk = rank_key(acc, (uint32_t)lane);
+        gk = ordered_f32(acc);
       }
       uint64_t chosen = 0ull;
       for (int m = 0; m < M; m++) {
-        const uint64_t c = ((chosen >> lane) & 1ull) ? 0ull : gk;
-        chosen |= 1ull << rank_key_index(wave_max_u64(c));
+        const uint32_t gmax = __ockl_wfred_max_u32(gk);
+        const uint32_t g = __ockl_wfred_min_u32(lane < G && gk == gmax ? (uint32_t)lane : 0xFFFFFFFFu);
+        chosen |= 1ull << g;
+        if (lane == (int)g) gk = 0u;
       }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const int e = lane + 64 * j;
-        if (e < N && !((chosen >> (e / S)) & 1ull)) pk[j] = 0ull;
+        if (e < N && !((chosen >> (e / S)) & 1ull)) ok[j] = 0u;
       }
     }
     int my_e = 0;
     for (int k = 0; k < K; k++) {
-      uint64_t best = pk[0];
+      const uint32_t lmax = max(max(ok[0], ok[1]), max(ok[2], ok[3]));
+      const uint32_t kmax = __ockl_wfred_max_u32(lmax);
+      uint32_t li = 0xFFFFFFFFu;
 #pragma unroll
-      for (int j = 1; j < 4; j++) best = pk[j] > best ? pk[j] : best;
-      best = wave_max_u64(best);
-      const int e = (int)rank_key_index(best);
+      for (int j = 3; j >= 0; j--)
+        if (ok[j] == kmax) li = (uint32_t)(lane + 64 * j);    // lowest index of this lane
+      const int e = (int)__ockl_wfred_min_u32(kmax ? li : 0xFFFFFFFFu);
 #pragma unroll
       for (int j = 0; j < 4; j++)
-        if (e == lane + 64 * j) pk[j] = 0ull;
+        if (e == lane + 64 * j) ok[j] = 0u;
       if (lane == k) my_e = e;
     }
     double sum = 0.0;

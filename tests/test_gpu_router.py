@@ -118,16 +118,41 @@ def _e2e(cfg, step=0, b=None, T=None):
 def test_end_to_end_routing(name, T):
     cfg = get_config(name)
     r, s64, s32, kgap, ggap, idx, gate, counts, sout = _e2e(cfg, T=T)
-    # affinities agree to a few fp32 ulps (logit error is ~1e-7 absolute)
-    assert np.max(np.abs(sout.astype(np.float64) - s64)) < 1e-6
-    diff = np.nonzero((idx != r.idx).any(axis=1))[0]
+    # the GPU's fp32 affinities: logit error ~1e-7 absolute, one rounding of the fp64 sigmoid
+    serr = np.abs(sout.astype(np.float64) - s64)
+    log(name, "max |s_gpu - s_oracle| %.3e (fp32 ulp at 1: %.1e)" % (serr.max(), 2.0 ** -24))
+    assert serr.max() < 2.5e-7
+    diff = routing_set_diff(idx, r.idx)
     exempt = (kgap < 1e-6) | (ggap < 1e-6)
-    log(name, "T=%d" % r.idx.shape[0], "tokens routed differently:", len(diff),
+    log(name, "T=%d" % r.idx.shape[0], "tokens routed to a different expert set:", len(diff),
         "exempt tokens:", int(exempt.sum()))
-    assert exempt[diff].all(), diff[~exempt[diff]][:10]
-    ok = ~exempt
-    assert np.array_equal(idx[ok], r.idx[ok])
-    assert np.allclose(gate[ok], r.gate[ok], rtol=2e-6, atol=0)
+    explain(diff, exempt, idx, r, kgap, ggap, sout)
+    assert exempt[diff].all()
+    ok = np.setdiff1d(np.arange(len(idx)), diff)
+    check_order_and_gates(idx[ok], gate[ok], sout[ok], r.idx[ok], r.gate[ok], r.key[ok], cfg, s64[ok])
     if len(diff) == 0:
         assert np.array_equal(counts, r.counts)
     assert counts.sum() == r.idx.size
+
+
+def routing_set_diff(idx_gpu, idx_ref):
+    """Tokens whose *set* of selected experts differs (the rank order of near-equal keys is not unique)."""
+    return np.nonzero((np.sort(idx_gpu, axis=1) != np.sort(idx_ref, axis=1)).any(axis=1))[0]
+
+
+def explain(diff, exempt, idx, r, kgap, ggap, sout):
+    for t in diff[~exempt[diff]][:5]:
+        log("  token", t, "gpu", idx[t].tolist(), "oracle", r.idx[t].tolist(),
+            "kgap %.3e ggap %.3e" % (kgap[t], ggap[t]),
+            "oracle keys", r.key[t, r.idx[t]].tolist(), "gpu s", sout[t, idx[t]].tolist())
+
+
+def check_order_and_gates(idx, gate, s_gpu, idx_ref, gate_ref, key_ref, cfg, s64):
+    """Same sets; the GPU's rank order is valid (keys non-increasing under the oracle's keys up to
+    1e-6 relative); gates agree per expert."""
+    o1, o2 = np.argsort(idx, axis=1), np.argsort(idx_ref, axis=1)
+    assert np.array_equal(np.take_along_axis(idx, o1, 1), np.take_along_axis(idx_ref, o2, 1))
+    g1, g2 = np.take_along_axis(gate, o1, 1), np.take_along_axis(gate_ref, o2, 1)
+    assert np.allclose(g1, g2, rtol=2e-6, atol=0)
+    k = np.take_along_axis(key_ref.astype(np.float64), idx, 1)
+    assert (k[:, :-1] >= k[:, 1:] - 1e-6 * np.abs(k[:, 1:])).all()
