@@ -28,19 +28,30 @@
 namespace moe {
 
 constexpr int GB_BK = 64;          // bf16 elements per K step (128 bytes per row)
-constexpr int GB_BN = 128;         // B rows per tile
-constexpr int GB_THREADS = 256;
 
-template <int MB>
-struct GemmLds {
+// MB: 32-row m-blocks per wave (tile height 64*MB); WN: waves along N. The
+// workgroup is 2*WN waves (2 along M); its B tile is 64*WN weight rows.
+template <int MB, int WN>
+struct GemmCfg {
+  static constexpr int THREADS = 128 * WN;
   static constexpr int BM = 64 * MB;
+  static constexpr int BN = 64 * WN;
   static constexpr int A_BYTES = BM * GB_BK * 2;
-  static constexpr int B_BYTES = GB_BN * GB_BK * 2;
+  static constexpr int B_BYTES = BN * GB_BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int BYTES = 2 * STAGE;
+  static constexpr int ROWS_PER_PASS = THREADS / 8;   // rows one load instruction covers per WG
+  static constexpr int ACH = BM / ROWS_PER_PASS;       // A 16-byte chunks per thread
+  static constexpr int BCH = BN / ROWS_PER_PASS;       // B chunks per thread
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk c of row r sits in slot c ^ (r & 7) ^ ((r >> 3) & 1) of the
+// row's 128 bytes: the MFMA operand reads (16 consecutive lanes = 16
+// consecutive rows, one chunk) then touch 16 distinct 4-bank groups of a
+// 64-bank LDS, and any 8 consecutive rows 8 distinct groups of a 32-bank one.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * 128 + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+}
 
 // Finds (segment, n-tile, m-tile) of logical tile L; tiles are ordered by
 // segment, then n-tile, then m-tile, so the m-tiles sharing one weight tile
@@ -62,21 +73,20 @@ __device__ __forceinline__ bool decode_tile(const int32_t* sprefix, int n_seg, i
   return true;
 }
 
-template <int MB, bool SWIGLU>
-__global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_kernel(GemmArgs a) {
-  using L = GemmLds<MB>;
-  constexpr int BM = L::BM;
-  constexpr int ACH = BM * 8 / GB_THREADS;     // A 16-byte chunks per thread (= 2*MB)
-  constexpr int BCH = GB_BN * 8 / GB_THREADS;  // B chunks per thread (= 4)
+template <int MB, int WN, bool SWIGLU>
+__global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs a) {
+  using C = GemmCfg<MB, WN>;
+  constexpr int BM = C::BM, BN = C::BN, ACH = C::ACH, BCH = C::BCH, RPP = C::ROWS_PER_PASS;
+  constexpr int HN = BN / 2;              // SwiGLU: output columns per tile
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int32_t sprefix[512];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
 
-  for (int i = tid; i <= a.n_seg; i += GB_THREADS) sprefix[i] = a.mtile_prefix[i];
+  for (int i = tid; i <= a.n_seg; i += C::THREADS) sprefix[i] = a.mtile_prefix[i];
   __syncthreads();
-  const int n_tiles = SWIGLU ? a.N / 64 : a.N / GB_BN;
+  const int n_tiles = SWIGLU ? a.N / HN : a.N / BN;
   int seg, ntile, mtile;
   // Workgroup i runs on XCD i % 8, and each XCD starts its workgroups in order of i.
   // Give XCD x the contiguous logical range [x*per, (x+1)*per): the tiles of one
@@ -96,47 +106,45 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_kernel(GemmArgs a) {
       ? (const uint16_t*)a.w0 + (size_t)seg * a.wstride0
       : (const uint16_t*)a.w1 + (size_t)(seg - a.n_first) * a.wstride1;
 
-  // ---- per-thread global source offsets (element units), fixed over K
+  // ---- per-thread global source offsets, fixed over K
   const int cch = tid & 7;          // 16-byte chunk within a 128-byte row slice
-  const int rbase = tid >> 3;       // 0..31
+  const int rbase = tid >> 3;       // 0 .. RPP-1
   // A rows: byte offsets into x; rows past the segment read zeros (out of range)
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_rows * (long)K * 2);
   int aoff[ACH];
 #pragma unroll
   for (int i = 0; i < ACH; i++) {
-    const int r = rbase + 32 * i;
+    const int r = rbase + RPP * i;
     const int rr = row0 + min(r, mvalid - 1);
     const int src = a.row_index ? a.row_index[rr] : rr;
     aoff[i] = r < mvalid ? (src * K + cch * 8) * 2 : kOutOfRange;
   }
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (long)(SWIGLU ? 2 * a.N : a.N) * K * 2);
   int boff[BCH];
 #pragma unroll
   for (int i = 0; i < BCH; i++) {
-    const int br = rbase + 32 * i;   // 0..127
+    const int br = rbase + RPP * i;   // 0 .. BN-1
     int wrow;
-    if (SWIGLU) wrow = br < 64 ? ntile * 64 + br : (a.N + ntile * 64 + (br - 64));
-    else wrow = ntile * GB_BN + br;
-    boff[i] = wrow * K + cch * 8;
+    if (SWIGLU) wrow = br < HN ? ntile * HN + br : (a.N + ntile * HN + (br - HN));
+    else wrow = ntile * BN + br;
+    boff[i] = (wrow * K + cch * 8) * 2;
   }
 
-  // Two register sets: the loads for K-step k+2 are issued while step k is
-  // computed from LDS and step k+1 waits in the other set, so each global load
-  // has about two steps of MFMA work to land.
-  i32x4 ra0[ACH], rb0[BCH], ra1[ACH], rb1[BCH];
-  auto gload = [&](i32x4 (&ra)[ACH], i32x4 (&rb)[BCH], int k0) {
+  i32x4 ra[ACH], rb[BCH];
+  auto gload = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < ACH; i++) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, aoff[i] + k0 * 2, 0, 0);
 #pragma unroll
-    for (int i = 0; i < BCH; i++)   // weights are streamed once: keep them out of L2's reuse set
-      rb[i] = __builtin_nontemporal_load((const i32x4*)(wbase + boff[i] + k0));
+    for (int i = 0; i < BCH; i++)   // weights are streamed once: non-temporal (slc)
+      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, boff[i] + k0 * 2, 0, 2);
   };
-  auto sstore = [&](const i32x4 (&ra)[ACH], const i32x4 (&rb)[BCH], int buf) {
-    uint8_t* A = lds + buf * L::STAGE;
-    uint8_t* B = A + L::A_BYTES;
+  auto sstore = [&](int buf) __attribute__((always_inline)) {
+    uint8_t* A = lds + buf * C::STAGE;
+    uint8_t* B = A + C::A_BYTES;
 #pragma unroll
-    for (int i = 0; i < ACH; i++) *(i32x4*)(A + swz(rbase + 32 * i, cch)) = ra[i];
+    for (int i = 0; i < ACH; i++) *(i32x4*)(A + swz(rbase + RPP * i, cch)) = ra[i];
 #pragma unroll
-    for (int i = 0; i < BCH; i++) *(i32x4*)(B + swz(rbase + 32 * i, cch)) = rb[i];
+    for (int i = 0; i < BCH; i++) *(i32x4*)(B + swz(rbase + RPP * i, cch)) = rb[i];
   };
 
   f32x16 acc[MB][2];
@@ -158,15 +166,15 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_kernel(GemmArgs a) {
   // count: straight-line code, all LDS reads of a k-substep ahead of its MFMAs.
   auto compute_na = [&](auto na_tag, int buf) __attribute__((always_inline)) {
     constexpr int NA = decltype(na_tag)::value;
-    const uint8_t* A = lds + buf * L::STAGE;
-    const uint8_t* B = A + L::A_BYTES;
+    const uint8_t* A = lds + buf * C::STAGE;
+    const uint8_t* B = A + C::A_BYTES;
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
       const int ch = ks * 2 + khalf;
       bf16x8 bfr[2], afr[NA > 0 ? NA : 1];
 #pragma unroll
       for (int j = 0; j < 2; j++) {
-        const int brow = (SWIGLU ? j * 64 + wn * 32 : wn * 64 + j * 32) + l32;
+        const int brow = (SWIGLU ? j * HN + wn * 32 : wn * 64 + j * 32) + l32;
         bfr[j] = *(const bf16x8*)(B + swz(brow, ch));
       }
 #pragma unroll
@@ -179,30 +187,23 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_kernel(GemmArgs a) {
     }
   };
   // Every load and LDS store in the K loop is unconditional (the trailing
-  // prefetches re-read the last step): with no branch around a memory op the
-  // compiler's wait counting stays in order and each LDS store waits only for
-  // its own register set.
+  // prefetch re-reads the last step): with no branch around a memory op the
+  // compiler's wait counting stays in order.
   const int nk = K / GB_BK;
   auto k_loop = [&](auto na_tag) __attribute__((always_inline)) {
-    gload(ra0, rb0, 0);
-    gload(ra1, rb1, min(1, nk - 1) * GB_BK);
-    sstore(ra0, rb0, 0);
+    gload(0);
+    sstore(0);
     __syncthreads();
-    for (int kt = 0; kt < (nk & ~1); kt += 2) {
-      // even half: LDS buf 0 holds step kt, set 1 holds kt+1, set 0 receives kt+2
-      gload(ra0, rb0, min(kt + 2, nk - 1) * GB_BK);
-      compute_na(na_tag, 0);
-      sstore(ra1, rb1, 1);
-      __syncthreads();
-      // odd half: LDS buf 1 holds kt+1, set 0 holds kt+2, set 1 receives kt+3
-      gload(ra1, rb1, min(kt + 3, nk - 1) * GB_BK);
-      compute_na(na_tag, 1);
-      sstore(ra0, rb0, 0);
+    for (int kt = 0; kt < nk; kt++) {
+      gload(min(kt + 1, nk - 1) * GB_BK);
+      compute_na(na_tag, kt & 1);
+      sstore((kt + 1) & 1);
       __syncthreads();
     }
-    if (nk & 1) compute_na(na_tag, 0);   // odd step count: buf 0 holds the last step
   };
-  // mb_active is the same in every lane of the wave: branch once, outside the loop
+  // mb_active is the same in every lane of the wave: branch once, outside the
+  // loop. A wave with no active m-block still loads its share and takes part
+  // in every barrier.
   switch (__builtin_amdgcn_readfirstlane(mb_active)) {
     case 0: k_loop(std::integral_constant<int, 0>{}); break;
     case 1: k_loop(std::integral_constant<int, 1>{}); break;
@@ -223,10 +224,10 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_kernel(GemmArgs a) {
         if (row < mvalid) {
           uint16_t* orow = out + (size_t)(row0 + row) * a.N;
           if (SWIGLU) {
-            const int col = ntile * 64 + wn * 32 + l32;
+            const int col = ntile * HN + wn * 32 + l32;
             orow[col] = f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
           } else {
-            const int col = ntile * GB_BN + wn * 64 + l32;
+            const int col = ntile * BN + wn * 64 + l32;
             orow[col] = f32_to_bf16(acc[i][0][r]);
             orow[col + 32] = f32_to_bf16(acc[i][1][r]);
           }
@@ -278,25 +279,25 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 
 int gemm_bm(int dtype, int mean_rows) {
   // The FP8 tile keeps its accumulators in VGPRs (the per-block scale fold is
-  // VALU work), so it is 128 rows tall to leave the MFMA operands room in VGPRs.
-  if (dtype == MOE_FP8_E4M3) return 128;
+  // VALU work): 192 rows is the tallest tile that fits without spilling.
+  if (dtype == MOE_FP8_E4M3) return 192;
   // one m-tile per expert when the mean load (+4 sigma of a binomial load) fits
   const int need = mean_rows + 4 * (int)std::sqrt((double)(mean_rows > 0 ? mean_rows : 1));
   if (need <= 256) return 256;
   return 320;
 }
 
-template <int MB, bool SWIGLU>
+template <int MB, int WN, bool SWIGLU>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
-  const int n_tiles = SWIGLU ? a.N / 64 : a.N / GB_BN;
-  const long mtiles_bound = (long)a.rows_bound / (64 * MB) + a.n_seg;
+  using C = GemmCfg<MB, WN>;
+  const int n_tiles = SWIGLU ? a.N / (C::BN / 2) : a.N / C::BN;
+  const long mtiles_bound = (long)a.rows_bound / C::BM + a.n_seg;
   const long grid = (mtiles_bound * n_tiles + 7) / 8 * 8;   // a multiple of the 8 XCDs
   if (grid <= 0) return hipSuccess;
-  auto k = gemm_bf16_kernel<MB, SWIGLU>;
-  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     GemmLds<MB>::BYTES);
+  auto k = gemm_bf16_kernel<MB, WN, SWIGLU>;
+  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
   if (e != hipSuccess) return e;
-  k<<<dim3((unsigned)grid), GB_THREADS, GemmLds<MB>::BYTES, s>>>(a);
+  k<<<dim3((unsigned)grid), C::THREADS, C::BYTES, s>>>(a);
   return hipGetLastError();
 }
 
@@ -309,8 +310,11 @@ static hipError_t launch_any(const GemmArgs& a, int dtype, int bm, hipStream_t s
     return hipGetLastError();
   }
   if (dtype == MOE_BF16) {
-    if (bm == 256) return launch_bf16<4, SWIGLU>(a, s);
-    if (bm == 320) return launch_bf16<5, SWIGLU>(a, s);
+    // 256 weight rows per tile (8 waves) when the output width allows it,
+    // else 128 (4 waves)
+    const bool wide = SWIGLU ? a.N % 128 == 0 : a.N % 256 == 0;
+    if (bm == 256) return wide ? launch_bf16<4, 4, SWIGLU>(a, s) : launch_bf16<4, 2, SWIGLU>(a, s);
+    if (bm == 320) return wide ? launch_bf16<5, 4, SWIGLU>(a, s) : launch_bf16<5, 2, SWIGLU>(a, s);
     return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;

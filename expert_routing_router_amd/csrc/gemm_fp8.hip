@@ -183,14 +183,9 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < NA; i++) {
         const int arow = (2 * i + wm) * 32 + l32;
-        // Each partial starts from its own zero (0 * acc, which the compiler can
-        // neither fold nor share between blocks), so C dies at the first MFMA
-        // and the accumulate form with D tied to C is used. With a shared or
-        // constant C the compiler may give the MFMA a destination overlapping
-        // its A operand, and this multi-pass instruction then returns garbage.
         f32x16 p;
 #pragma unroll
-        for (int r = 0; r < 16; r++) p[r] = acc[i][j][r] * a.fzero;
+        for (int r = 0; r < 16; r++) p[r] = 0.f;
 #pragma unroll
         for (int h = 0; h < 2; h++) {
           const int c0 = h * 4 + khalf * 2;
@@ -222,8 +217,10 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
       __syncthreads();
     }
   };
+  // A wave with no active m-block still runs the loop: it loads its share of
+  // every LDS tile and takes part in every barrier.
   switch (__builtin_amdgcn_readfirstlane(mb_active)) {
-    case 0: break;
+    case 0: k_loop(std::integral_constant<int, 0>{}); break;
     case 1: k_loop(std::integral_constant<int, 1>{}); break;
     case 2: k_loop(std::integral_constant<int, 2>{}); break;
     default: k_loop(std::integral_constant<int, MB>{}); break;
@@ -267,7 +264,7 @@ static hipError_t launch_fp8_t(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, bool swiglu, int bm, hipStream_t s) {
-  if (bm == 128) return swiglu ? launch_fp8_t<2, true>(a, s) : launch_fp8_t<2, false>(a, s);
+  if (bm == 192) return swiglu ? launch_fp8_t<3, true>(a, s) : launch_fp8_t<3, false>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -271,7 +271,6 @@ static GemmArgs gemm_args(const void* x, long x_rows, const float* xs, const int
   g.n_seg = n_seg; g.w0 = w0; g.w1 = w0; g.wstride0 = ws0; g.wstride1 = ws0;
   g.ws0 = s0; g.ws1 = s0; g.sstride0 = ss0; g.sstride1 = ss0; g.n_first = n_seg;
   g.out = out; g.N = N; g.K = K; g.rows_bound = rows_bound;
-  g.fzero = 0.0f;
   return g;
 }
 

@@ -53,7 +53,6 @@ struct GemmArgs {
   int N;                      // output columns (I for the SwiGLU GEMM, d for down)
   int K;                      // reduction length
   int rows_bound;             // upper bound on total rows (grid sizing)
-  float fzero;                // 0.0f, opaque to the compiler (fresh MFMA partials start from it)
 };
 int gemm_bm(int dtype, int mean_rows);
 hipError_t launch_gemm_swiglu(const GemmArgs& a, int dtype, int bm, hipStream_t s);
