@@ -237,6 +237,226 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- LDS-DMA path
+// Same tile and wave layout as gemm_bf16_kernel<MB, 4, ...> (8 waves, 64*MB x
+// 256 weight rows), but operands go from global memory straight into LDS with
+// buffer loads that write LDS (no register staging), through a ring of four
+// K=32 stages: three stages are in flight while one is multiplied, so each
+// CU keeps ~108 KB of loads outstanding instead of one K step's worth.
+//
+// A stage holds 64 bytes (4 chunks of 16) per row. One load instruction of a
+// wave fills one 1 KB block = 16 rows; lane l writes block byte 16*l, i.e.
+// row l>>2, slot l&3, and fetches the chunk c = slot ^ ((row >> 2) & 3). The
+// MFMA operand reads (16 lanes = 16 consecutive rows, one chunk) then hit 16
+// distinct 4-bank groups.
+constexpr int DMA_BK = 32;
+constexpr int DMA_STAGES = 4;
+
+template <int MB>
+struct DmaCfg {
+  static constexpr int THREADS = 512;
+  static constexpr int BM = 64 * MB;
+  static constexpr int BN = 256;
+  static constexpr int A_BLOCKS = BM / 16;              // 1 KB blocks per stage
+  static constexpr int B_BLOCKS = BN / 16;
+  static constexpr int A_BYTES = BM * DMA_BK * 2;
+  static constexpr int STAGE = (BM + BN) * DMA_BK * 2;
+  static constexpr int BYTES = DMA_STAGES * STAGE;
+  static constexpr int A_PER_WAVE = (A_BLOCKS + 7) / 8;  // waves below A_BLOCKS % 8 take one more
+  static constexpr int A_EXTRA = A_BLOCKS % 8;
+  static constexpr int B_PER_WAVE = B_BLOCKS / 8;
+  static_assert(B_BLOCKS % 8 == 0, "B blocks split evenly over 8 waves");
+  static_assert(BYTES <= 160 * 1024 - 2048, "LDS budget");
+};
+
+// One 16-byte-per-lane buffer load that writes LDS at m0 + 16 * lane. The
+// instruction has no register result; its completion is tracked by vmcnt,
+// which the K loop waits on explicitly. s_nop covers the m0-write hazard.
+__device__ __forceinline__ void dma_b128(i32x4 rsrc, int voff, int soff, uint32_t m0) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0) : "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, long bytes) {
+  const uint64_t a = (uint64_t)base;
+  const int n = bytes >= 0x7FFFFFFFL ? 0x7FFFFFFF : (int)bytes;
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)(uint32_t)(a >> 32);   // stride 0
+  r[2] = n;
+  r[3] = kRawBufferFlags;
+  return r;
+}
+
+template <int MB, bool SWIGLU>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
+  using C = DmaCfg<MB>;
+  constexpr int BM = C::BM, BN = C::BN, HN = BN / 2;
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int32_t sprefix[512];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+
+  for (int i = tid; i <= a.n_seg; i += C::THREADS) sprefix[i] = a.mtile_prefix[i];
+  __syncthreads();
+  const int n_tiles = SWIGLU ? a.N / HN : a.N / BN;
+  int seg, ntile, mtile;
+  // XCD-contiguous logical ranges, as in gemm_bf16_kernel
+  const int total_tiles = sprefix[a.n_seg] * n_tiles;
+  const int per_xcd = (total_tiles + 7) >> 3;
+  const int lt = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd) return;
+  if (!decode_tile(sprefix, a.n_seg, n_tiles, lt, seg, ntile, mtile)) return;
+
+  const int seg_begin = a.offsets[seg], seg_end = a.offsets[seg + 1];
+  const int row0 = seg_begin + mtile * BM;
+  const int mvalid = min(BM, seg_end - row0);
+  const int K = a.K;
+  const uint16_t* wbase = seg < a.n_first
+      ? (const uint16_t*)a.w0 + (size_t)seg * a.wstride0
+      : (const uint16_t*)a.w1 + (size_t)(seg - a.n_first) * a.wstride1;
+
+  // ---- per-lane global offsets of this wave's blocks (fixed over K)
+  const int brow = lane >> 2;                                  // row within a block
+  const int bchunk = (lane & 3) ^ ((lane >> 4) & 3);           // chunk this lane fetches
+  const i32x4 xr = rsrc_words(a.x, a.x_rows * (long)K * 2);
+  const i32x4 wr = rsrc_words(wbase, (long)(SWIGLU ? 2 * a.N : a.N) * K * 2);
+  int aoff[C::A_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::A_PER_WAVE; i++) {
+    const int r = (wave + 8 * i) * 16 + brow;   // blocks past A_BLOCKS are never issued
+    const int rr = row0 + min(r, mvalid - 1);
+    const int src = a.row_index ? a.row_index[rr] : rr;
+    aoff[i] = r < mvalid ? (src * K + bchunk * 8) * 2 : kOutOfRange;
+  }
+  int boff[C::B_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::B_PER_WAVE; i++) {
+    const int r = (wave + 8 * i) * 16 + brow;   // 0 .. BN-1
+    const int wrow = SWIGLU ? (r < HN ? ntile * HN + r : a.N + ntile * HN + (r - HN)) : ntile * BN + r;
+    boff[i] = (wrow * K + bchunk * 8) * 2;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  constexpr int A_EXTRA = C::A_EXTRA;           // waves below this issue A_PER_WAVE blocks
+  const bool a_full = A_EXTRA == 0 || wave < A_EXTRA;
+  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+    const int soff = kt * DMA_BK * 2;
+    const uint32_t sbase = lds0 + buf * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::A_PER_WAVE; i++)
+      if (i < C::A_PER_WAVE - 1 || a_full)
+        dma_b128(xr, aoff[i], soff, sbase + (wave + 8 * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < C::B_PER_WAVE; i++)
+      dma_b128(wr, boff[i], soff, sbase + C::A_BYTES + (wave + 8 * i) * 1024);
+  };
+
+  f32x16 acc[MB][2];
+#pragma unroll
+  for (int i = 0; i < MB; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+  int mb_active = 0;
+#pragma unroll
+  for (int i = 0; i < MB; i++)
+    if ((2 * i + wm) * 32 < mvalid) mb_active = i + 1;
+
+  // operand read offsets: row = block*32 + l32 has (row >> 2) & 3 == (l32 >> 2) & 3
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int sw = (l32 >> 2) & 3;
+  const int roff0 = l32 * 64 + ((khalf ^ sw) << 4);         // k-substep 0: chunk khalf
+  const int roff1 = l32 * 64 + (((2 + khalf) ^ sw) << 4);   // k-substep 1: chunk 2 + khalf
+  // B rows of this wave: SwiGLU gate rows wn*32.. and up rows HN + wn*32..; else wn*64 + j*32
+  const int bro0 = (SWIGLU ? wn * 32 : wn * 64) * 64;
+  const int bro1 = (SWIGLU ? HN + wn * 32 : wn * 64 + 32) * 64;
+
+  auto compute_na = [&](auto na_tag, int buf) __attribute__((always_inline)) {
+    constexpr int NA = decltype(na_tag)::value;
+    const uint8_t* A = lds + buf * C::STAGE;
+    const uint8_t* B = A + C::A_BYTES;
+    bf16x8 b0[2], b1[2], af[2][NA > 0 ? NA : 1];
+    b0[0] = *(const bf16x8*)(B + bro0 + roff0);
+    b0[1] = *(const bf16x8*)(B + bro1 + roff0);
+#pragma unroll
+    for (int i = 0; i < NA; i++) af[0][i] = *(const bf16x8*)(A + (2 * i + wm) * 2048 + roff0);
+    b1[0] = *(const bf16x8*)(B + bro0 + roff1);
+    b1[1] = *(const bf16x8*)(B + bro1 + roff1);
+#pragma unroll
+    for (int i = 0; i < NA; i++) af[1][i] = *(const bf16x8*)(A + (2 * i + wm) * 2048 + roff1);
+#pragma unroll
+    for (int i = 0; i < NA; i++) {
+      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], b0[0], acc[i][0], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], b0[1], acc[i][1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NA; i++) {
+      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], b1[0], acc[i][0], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], b1[1], acc[i][1], 0, 0, 0);
+    }
+  };
+
+  // Ring protocol for step kt: wait for this wave's loads of stage kt (the two
+  // younger stages may stay outstanding), barrier (every wave's stage-kt data
+  // is in LDS and every wave is done reading stage kt-1), refill stage kt-1's
+  // buffer with step kt+3, multiply stage kt. Loads past the last step re-read
+  // it into a buffer that is never read again, so the count per step is fixed.
+  const int nk = K / DMA_BK;
+  auto k_loop = [&](auto na_tag) __attribute__((always_inline)) {
+    issue(0, 0);
+    issue(min(1, nk - 1), 1);
+    issue(min(2, nk - 1), 2);
+    for (int kt = 0; kt < nk; kt++) {
+      if (a_full) wait_vmcnt<2 * (C::A_PER_WAVE + C::B_PER_WAVE)>();
+      else wait_vmcnt<2 * (C::A_PER_WAVE - 1 + C::B_PER_WAVE)>();
+      __syncthreads();
+      issue(min(kt + 3, nk - 1), (kt + 3) & 3);
+      compute_na(na_tag, kt & 3);
+    }
+    wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
+  };
+  switch (__builtin_amdgcn_readfirstlane(mb_active)) {
+    case 0: k_loop(std::integral_constant<int, 0>{}); break;
+    case 1: k_loop(std::integral_constant<int, 1>{}); break;
+    case 2: k_loop(std::integral_constant<int, 2>{}); break;
+    case 3: k_loop(std::integral_constant<int, (MB >= 3 ? 3 : MB)>{}); break;
+    case 4: k_loop(std::integral_constant<int, (MB >= 4 ? 4 : MB)>{}); break;
+    default: k_loop(std::integral_constant<int, MB>{}); break;
+  }
+
+  uint16_t* out = (uint16_t*)a.out;
+#pragma unroll
+  for (int i = 0; i < MB; i++) {
+    if (i < mb_active) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+        if (row < mvalid) {
+          uint16_t* orow = out + (size_t)(row0 + row) * a.N;
+          if (SWIGLU) {
+            orow[ntile * HN + wn * 32 + l32] = f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
+          } else {
+            const int col = ntile * BN + wn * 64 + l32;
+            orow[col] = f32_to_bf16(acc[i][0][r]);
+            orow[col + 32] = f32_to_bf16(acc[i][1][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fp32 path
 // fp32 experts (the small fp32 layer): MI355X's fp32 vector rate equals its
 // fp32 matrix rate, so a plain VALU kernel is the fp32 path. One thread per
@@ -301,6 +521,20 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int MB, bool SWIGLU>
+static hipError_t launch_bf16_dma(const GemmArgs& a, hipStream_t s) {
+  using C = DmaCfg<MB>;
+  const int n_tiles = SWIGLU ? a.N / (C::BN / 2) : a.N / C::BN;
+  const long mtiles_bound = (long)a.rows_bound / C::BM + a.n_seg;
+  const long grid = (mtiles_bound * n_tiles + 7) / 8 * 8;
+  if (grid <= 0) return hipSuccess;
+  auto k = gemm_bf16_dma_kernel<MB, SWIGLU>;
+  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
+  if (e != hipSuccess) return e;
+  k<<<dim3((unsigned)grid), C::THREADS, C::BYTES, s>>>(a);
+  return hipGetLastError();
+}
+
 template <bool SWIGLU>
 static hipError_t launch_any(const GemmArgs& a, int dtype, int bm, hipStream_t s) {
   if (dtype == MOE_F32) {
@@ -313,8 +547,8 @@ static hipError_t launch_any(const GemmArgs& a, int dtype, int bm, hipStream_t s
     // 256 weight rows per tile (8 waves) when the output width allows it,
     // else 128 (4 waves)
     const bool wide = SWIGLU ? a.N % 128 == 0 : a.N % 256 == 0;
-    if (bm == 256) return wide ? launch_bf16<4, 4, SWIGLU>(a, s) : launch_bf16<4, 2, SWIGLU>(a, s);
-    if (bm == 320) return wide ? launch_bf16<5, 4, SWIGLU>(a, s) : launch_bf16<5, 2, SWIGLU>(a, s);
+    if (bm == 256) return wide ? launch_bf16_dma<4, SWIGLU>(a, s) : launch_bf16<4, 2, SWIGLU>(a, s);
+    if (bm == 320) return wide ? launch_bf16_dma<5, SWIGLU>(a, s) : launch_bf16<5, 2, SWIGLU>(a, s);
     return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
