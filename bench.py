@@ -57,6 +57,35 @@ def algorithmic(cfg):
     return st
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_swiglu_v3_hbm_traffic.txt")
+GEMM_SOURCES = ["expert_routing_router_amd/csrc/gemm_bf16.hip", "expert_routing_router_amd/csrc/common.h"]
+
+
+def measured_traffic(cfg):
+    """HBM bytes per launch of the gate/up GEMM from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's reading), or None when
+    the summary is for another workload or the kernel sources changed since."""
+    import hashlib
+    if cfg.name != "v3" or cfg.T != 8192 or cfg.expert_dtype != "bf16" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    fields = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip().split()[0] if v.strip() else ""
+    if fields.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(cfg, n_sample_experts, log_fn):
     """The oracle (unchanged) on a bounded sample of one step, scaled to tokens/s.
 
@@ -119,6 +148,9 @@ def main():
     ap.add_argument("--T", type=int, default=0, help="override tokens per batch")
     ap.add_argument("--cpu-sample-experts", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--load-trajectory", type=int, default=0,
+                    help="after the timed steps, run this many forward+update steps from the initial "
+                         "bias and report the max/mean expert load of each (every 10th listed)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times) and exit: the "
                          "reference dispatch for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -190,6 +222,20 @@ def main():
         c = layer.counts.float()
         loads.append(float(c.max() / c.mean()))
 
+    trajectory = None
+    if args.load_trajectory:
+        b_t = np_to_device(gen.bias_init(cfg), "f32", "cuda:0")
+        ratios = []
+        for i in range(args.load_trajectory):
+            layer.forward(us[i % nb], b_t, update_bias=True)
+            c = layer.counts.float()
+            ratios.append(float(c.max() / c.mean()))
+        trajectory = {"steps": args.load_trajectory, "tokens": "%d resident batches in turn" % nb,
+                      "max_over_mean_every_10": [round(x, 3) for x in ratios[::10]],
+                      "first": round(ratios[0], 3), "last": round(ratios[-1], 3),
+                      "mean_last_20": round(sum(ratios[-20:]) / len(ratios[-20:]), 3)}
+        log("load trajectory: max/mean %.3f -> %.3f over %d steps" % (ratios[0], ratios[-1], len(ratios)))
+
     alg = algorithmic(cfg)
     peak_tf = PEAK_TFLOPS[cfg.expert_dtype]
     kernels = {}
@@ -213,8 +259,8 @@ def main():
     g1_ms = stage_ms["gemm1"] / max(calls, 1)
     achieved = g1["bytes"] / g1_ms / 1e6
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": "gemm_%s_kernel (grouped gate/up GEMM + SwiGLU, routed + shared)" % cfg.expert_dtype,
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(cfg),
+                "kernel": "grouped gate/up GEMM + SwiGLU over routed and shared rows (gemm_%s kernel)" % ("bf16_dma" if cfg.expert_dtype == "bf16" else cfg.expert_dtype),
                 "bytes_per_launch": g1["bytes"], "avg_ms": round(g1_ms, 4)}
 
     cpu = None
@@ -242,6 +288,7 @@ def main():
         "kernels": kernels,
         "grouped_gemm_mfma_frac": kernels["grouped_gemm"]["mfma_frac"],
         "max_over_mean_load": [round(x, 3) for x in loads],
+        "load_trajectory": trajectory,
         "event_ms_per_step": round(ev_ms / args.steps, 4),
     }
     print(json.dumps(rec), flush=True)

@@ -156,3 +156,37 @@ def check_order_and_gates(idx, gate, s_gpu, idx_ref, gate_ref, key_ref, cfg, s64
     assert np.allclose(g1, g2, rtol=2e-6, atol=0)
     k = np.take_along_axis(key_ref.astype(np.float64), idx, 1)
     assert (k[:, :-1] >= k[:, 1:] - 1e-6 * np.abs(k[:, 1:])).all()
+
+
+def test_bias_trajectory_200_steps_scores_in():
+    """200 forward+update steps of the skewed router (V3 routing shape, 1024 tokens per step):
+    with the oracle's fp32 affinities fed in, the GPU's loads and bias equal the oracle's
+    at every step, bit for bit, so the whole balancing trajectory is reproduced."""
+    cfg = get_config("skew").with_(T=1024)
+    T, N, K = cfg.T, cfg.n_routed, cfg.top_k
+    E = nx.to_f64(gen.centroids(cfg), cfg.router_dtype)
+    desc = M.desc_from_config(cfg)
+    b_ref = gen.bias_init(cfg)
+    b_dev = dev(b_ref, "f32")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    counts = torch.empty(N, dtype=torch.int32, device="cuda")
+    ratio = []
+    for step in range(200):
+        u = nx.to_f64(gen.tokens(cfg, step), cfg.in_dtype)
+        s32 = routing.sigmoid(routing.logits(u, E)).astype(np.float32)
+        r = routing.select(s32, b_ref, K, cfg.n_groups, cfg.topk_groups, cfg.group_topk,
+                           cfg.group_score_biased)
+        M.moe_route(desc, b_dev, idx, gate, counts, scores_in=dev(s32, "f32"))
+        M.moe_update_bias(desc, counts, b_dev)
+        torch.cuda.synchronize()
+        c = host(counts)
+        assert np.array_equal(c, r.counts), step
+        assert np.array_equal(host(idx), r.idx), step
+        b_ref = routing.bias_step(r.counts, b_ref, T, K, cfg.gamma)
+        assert np.array_equal(host(b_dev).view(np.uint32), b_ref.view(np.uint32)), step
+        ratio.append(c.max() / c.mean())
+    log("skew T=1024 max/mean load: step 0 %.2f, 50 %.2f, 100 %.2f, 150 %.2f, 199 %.2f"
+        % tuple(ratio[i] for i in (0, 50, 100, 150, 199)))
+    # the balancing moves every expert's bias by gamma per step towards the mean load
+    assert np.mean(ratio[-20:]) < np.mean(ratio[:20])
