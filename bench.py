@@ -58,7 +58,8 @@ def algorithmic(cfg):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_swiglu_v3_hbm_traffic.txt")
-GEMM_SOURCES = ["expert_routing_router_amd/csrc/gemm_bf16.hip", "expert_routing_router_amd/csrc/common.h"]
+GEMM_SOURCES = ["expert_routing_router_amd/csrc/gemm_bf16.hip", "expert_routing_router_amd/csrc/common.h",
+                "expert_routing_router_amd/csrc/lds_dma.h"]
 
 
 def measured_traffic(cfg):

@@ -21,6 +21,7 @@
 // buffer, 16-byte chunks XOR-swizzled by row so MFMA operand reads are
 // conflict-free) -> v_mfma_f32_32x32x16_bf16.
 #include "common.h"
+#include "lds_dma.h"
 #include "moe_internal.h"
 #include <cmath>
 #include <type_traits>
@@ -269,32 +270,6 @@ struct DmaCfg {
   static_assert(BYTES <= 160 * 1024 - 2048, "LDS budget");
 };
 
-// One 16-byte-per-lane buffer load that writes LDS at m0 + 16 * lane. The
-// instruction has no register result; its completion is tracked by vmcnt,
-// which the K loop waits on explicitly. s_nop covers the m0-write hazard.
-__device__ __forceinline__ void dma_b128(i32x4 rsrc, int voff, int soff, uint32_t m0) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0) : "memory");
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, long bytes) {
-  const uint64_t a = (uint64_t)base;
-  const int n = bytes >= 0x7FFFFFFFL ? 0x7FFFFFFF : (int)bytes;
-  i32x4 r;
-  r[0] = (int)(uint32_t)a;
-  r[1] = (int)(uint32_t)(a >> 32);   // stride 0
-  r[2] = n;
-  r[3] = kRawBufferFlags;
-  return r;
-}
-
 template <int MB, bool SWIGLU>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
   using C = DmaCfg<MB>;
@@ -497,10 +472,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   }
 }
 
-int gemm_bm(int dtype, int mean_rows) {
-  // The FP8 tile keeps its accumulators in VGPRs (the per-block scale fold is
-  // VALU work): 192 rows is the tallest tile that fits without spilling.
-  if (dtype == MOE_FP8_E4M3) return 192;
+int gemm_bm(int dtype, int mean_rows, int dmodel) {
+  // FP8: 256-row tiles of the LDS-DMA kernel when the down GEMM's width is a
+  // multiple of its 256-row weight tile, else the register-staged 192-row kernel.
+  if (dtype == MOE_FP8_E4M3) return dmodel % 256 == 0 ? 256 : 192;
   // one m-tile per expert when the mean load (+4 sigma of a binomial load) fits
   const int need = mean_rows + 4 * (int)std::sqrt((double)(mean_rows > 0 ? mean_rows : 1));
   if (need <= 256) return 256;
