@@ -22,6 +22,7 @@
 // conflict-free) -> v_mfma_f32_32x32x16_bf16.
 #include "common.h"
 #include "lds_dma.h"
+#include "tile_order.h"
 #include "moe_internal.h"
 #include <cmath>
 #include <type_traits>
@@ -52,26 +53,6 @@ struct GemmCfg {
 // 64-bank LDS, and any 8 consecutive rows 8 distinct groups of a 32-bank one.
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
-}
-
-// Finds (segment, n-tile, m-tile) of logical tile L; tiles are ordered by
-// segment, then n-tile, then m-tile, so the m-tiles sharing one weight tile
-// are adjacent in dispatch order.
-__device__ __forceinline__ bool decode_tile(const int32_t* sprefix, int n_seg, int n_tiles, int L,
-                                            int& seg, int& nt, int& mt) {
-  const int total = sprefix[n_seg] * n_tiles;
-  if (L >= total) return false;
-  int lo = 0, hi = n_seg - 1;
-  while (lo < hi) {                       // largest seg with sprefix[seg]*n_tiles <= L
-    const int mid = (lo + hi + 1) >> 1;
-    if (sprefix[mid] * n_tiles <= L) lo = mid; else hi = mid - 1;
-  }
-  seg = lo;
-  const int local = L - sprefix[seg] * n_tiles;
-  const int mte = sprefix[seg + 1] - sprefix[seg];
-  nt = local / mte;
-  mt = local - nt * mte;
-  return true;
 }
 
 template <int MB, int WN, bool SWIGLU>

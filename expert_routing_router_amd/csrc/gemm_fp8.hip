@@ -11,6 +11,7 @@
 // Tiling, ragged segments and the SwiGLU epilogue follow the bf16 kernel.
 #include "common.h"
 #include "lds_dma.h"
+#include "tile_order.h"
 #include "moe_internal.h"
 #include <type_traits>
 
@@ -31,23 +32,6 @@ struct Fp8Lds {
 };
 
 __device__ __forceinline__ int swz8(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
-
-__device__ __forceinline__ bool decode_tile8(const int32_t* sprefix, int n_seg, int n_tiles, int L,
-                                             int& seg, int& nt, int& mt) {
-  const int total = sprefix[n_seg] * n_tiles;
-  if (L >= total) return false;
-  int lo = 0, hi = n_seg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (sprefix[mid] * n_tiles <= L) lo = mid; else hi = mid - 1;
-  }
-  seg = lo;
-  const int local = L - sprefix[seg] * n_tiles;
-  const int mte = sprefix[seg + 1] - sprefix[seg];
-  nt = local / mte;
-  mt = local - nt * mte;
-  return true;
-}
 
 template <int MB, bool SWIGLU>
 __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
@@ -73,7 +57,7 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
   const int per_xcd = (total_tiles + 7) >> 3;
   const int lt = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if ((int)(blockIdx.x >> 3) >= per_xcd) return;
-  if (!decode_tile8(sprefix, a.n_seg, n_tiles, lt, seg, ntile, mtile)) return;
+  if (!decode_tile(sprefix, a.n_seg, n_tiles, lt, seg, ntile, mtile)) return;
 
   const int row0 = a.offsets[seg] + mtile * BM;
   const int mvalid = min(BM, a.offsets[seg + 1] - row0);
@@ -307,7 +291,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
   const int per_xcd = (total_tiles + 7) >> 3;
   const int lt = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if ((int)(blockIdx.x >> 3) >= per_xcd) return;
-  if (!decode_tile8(sprefix, a.n_seg, n_tiles, lt, seg, ntile, mtile)) return;
+  if (!decode_tile(sprefix, a.n_seg, n_tiles, lt, seg, ntile, mtile)) return;
 
   const int row0 = a.offsets[seg] + mtile * BM;
   const int mvalid = min(BM, a.offsets[seg + 1] - row0);

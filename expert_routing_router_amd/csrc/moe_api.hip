@@ -137,8 +137,16 @@ extern "C" int moe_validate(const moe_desc_t* d) {
 // ---------------------------------------------------------------- workspace layout
 struct Ws {
   size_t idx, gate, counts, bitmap, wprefix, offsets, mtile, row_token, slot_row, H, Y;
-  size_t qu, su, qh, sh, offs_s, mtile_s, total;
+  size_t qu, su, qh, sh, offs_s, mtile_s, rscratch, total;
 };
+
+static RouteArgs route_args(const moe_desc_t* d, const void* u, const void* E, const float* b,
+                            const float* scores_in, float* scores_out, int32_t* idx, float* gate, int32_t* counts);
+
+// moe_forward routes large batches in two phases (tiled logits, then selection)
+static bool two_phase_router(const moe_desc_t* d) {
+  return route_two_phase_ok(route_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr));
+}
 
 static bool fused_shared(const moe_desc_t* d) { return d->n_shared == 0 || d->inter == d->inter_shared; }
 
@@ -174,6 +182,7 @@ static Ws layout(const moe_desc_t* d) {
   } else {
     w.qu = w.su = w.qh = w.sh = 0;
   }
+  w.rscratch = two_phase_router(d) ? take(route_two_phase_bytes(d->T, d->n_routed, d->d, d->router_dtype)) : 0;
   w.total = o;
   return w;
 }
@@ -405,7 +414,8 @@ extern "C" int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const vo
   // 1. router
   prof_mark(-1, s);
   RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, nullptr, idx, gate, counts);
-  MOE_TRY(launch_route(ra, route_front(d), s));
+  if (two_phase_router(d)) MOE_TRY(launch_route_two_phase(ra, base + L.rscratch, s));
+  else MOE_TRY(launch_route(ra, route_front(d), s));
   prof_mark(MOE_STAGE_ROUTE, s);
 
   // 2. dispatch layout; shared experts become extra identity segments

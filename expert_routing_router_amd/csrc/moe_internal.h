@@ -15,6 +15,12 @@ struct RouteArgs {
   int in_dtype, router_dtype;
 };
 hipError_t launch_route(const RouteArgs& a, int front, hipStream_t s);
+// Two-phase router (tiled logits kernel into a scores buffer, then selection
+// from it); same results as the fused front ends. Needs route_two_phase_bytes
+// of device scratch.
+bool route_two_phase_ok(const RouteArgs& a);
+size_t route_two_phase_bytes(int T, int N, int d, int router_dtype);
+hipError_t launch_route_two_phase(const RouteArgs& a, void* scratch, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, long n, hipStream_t s);
 
 // ---------------------------------------------------------------- permute

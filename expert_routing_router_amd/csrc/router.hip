@@ -22,6 +22,7 @@
 // smaller mid+lo products go to separate accumulators so the small terms are
 // not rounded against the large running sum.
 #include "common.h"
+#include "lds_dma.h"
 #include "moe_internal.h"
 #include <type_traits>
 
@@ -316,6 +317,210 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
   __syncthreads();
   for (int e = threadIdx.x; e < a.n_routed; e += RT_THREADS)
     if (sh.cnt[e]) atomicAdd(&a.counts[e], sh.cnt[e]);
+}
+
+// ---------------------------------------------------------------- two-phase router
+// For large batches the logits are better tiled over (tokens x experts) than
+// one workgroup per 32 tokens x all experts (which streams the whole centroid
+// matrix through every CU). Phase 1 (logits_kernel) computes the affinities
+// of a 128-token x 64-expert tile and writes them to a scores buffer; phase 2
+// is route_kernel in scores-in mode (the same selection code). Phase 1 does
+// the same arithmetic as front_mfma -- the same 16x16x32 MFMAs on the same
+// operands, fp32 partials over 64-element chunks of d summed in fp64 in chunk
+// order, the split of fp32 centroids into hi/mid/lo bf16 planes, the same
+// sigmoid -- so both routers give bit-identical affinities.
+constexpr int LG_BT = 128;          // tokens per workgroup
+constexpr int LG_BE = 64;           // experts per workgroup
+constexpr int LG_BK = 64;           // bf16 elements per stage row (128 bytes)
+
+template <int NPLANES>
+struct LogitsCfg {
+  static constexpr int U_BYTES = LG_BT * LG_BK * 2;       // 16 KB
+  static constexpr int E_BYTES = LG_BE * LG_BK * 2;       // 8 KB per plane
+  static constexpr int STAGE = U_BYTES + NPLANES * E_BYTES;
+  static constexpr int STAGES = NPLANES == 1 ? 6 : 3;
+  static constexpr int BYTES = STAGES * STAGE;
+  static constexpr int U_PER_WAVE = LG_BT / 8 / 4;         // 1 KB blocks of 8 rows, 4 waves
+  static constexpr int E_PER_WAVE = LG_BE / 8 / 4;
+  static constexpr int LOADS = U_PER_WAVE + NPLANES * E_PER_WAVE;
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+// fp32 centroids -> three bf16 planes [3][N][d] with hi + mid + lo == value exactly
+__global__ void split_planes_kernel(const float* E, uint16_t* planes, long n) {
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+    const float v = E[i];
+    const uint16_t h = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(h);
+    const uint16_t m = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(m);
+    planes[i] = h;
+    planes[n + i] = m;
+    planes[2 * n + i] = f32_to_bf16(r2);
+  }
+}
+
+template <int NPLANES>
+__global__ __launch_bounds__(256, 1) void logits_kernel(const uint16_t* __restrict__ u,
+                                                        const uint16_t* __restrict__ planes, float* scores,
+                                                        int T, int d, int N) {
+  using C = LogitsCfg<NPLANES>;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * LG_BT, e0 = blockIdx.y * LG_BE;
+
+  // ---- loads: one instruction fills 8 rows x 128 bytes; lane l writes row
+  // l>>3, slot l&7 and fetches chunk slot ^ ((row >> 1) & 7)
+  const int brow = lane >> 3;
+  const int bchunk = (lane & 7) ^ ((((wave & 1) << 2) + (lane >> 4)) & 7);   // block parity = wave parity
+  const i32x4 ur = rsrc_words(u, (long)T * d * 2);
+  const i32x4 er = rsrc_words(planes, (long)NPLANES * N * d * 2);
+  int uoff[C::U_PER_WAVE], eoff[NPLANES][C::E_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::U_PER_WAVE; i++) {
+    const int t = t0 + (wave + 4 * i) * 8 + brow;
+    uoff[i] = t < T ? (t * d + bchunk * 8) * 2 : kOutOfRange;
+  }
+#pragma unroll
+  for (int p = 0; p < NPLANES; p++)
+#pragma unroll
+    for (int i = 0; i < C::E_PER_WAVE; i++) {
+      const int e = e0 + (wave + 4 * i) * 8 + brow;
+      eoff[p][i] = ((p * N + e) * d + bchunk * 8) * 2;
+    }
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+    const int koff = kt * LG_BK * 2;
+    const uint32_t sb = lds0 + buf * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::U_PER_WAVE; i++) dma_b128(ur, uoff[i], koff, sb + (wave + 4 * i) * 1024);
+#pragma unroll
+    for (int p = 0; p < NPLANES; p++)
+#pragma unroll
+      for (int i = 0; i < C::E_PER_WAVE; i++)
+        dma_b128(er, eoff[p][i], koff, sb + C::U_BYTES + p * C::E_BYTES + (wave + 4 * i) * 1024);
+  };
+
+  // ---- wave w: tokens 32w .. 32w+31 (two 16-row blocks) x the 64 experts (four blocks)
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int sw = (r16 >> 1) & 7;
+  int roff[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ks++) roff[ks] = r16 * 128 + (((ks * 4 + kg) ^ sw) << 4);
+  double z64[2][4][4];
+#pragma unroll
+  for (int m = 0; m < 2; m++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) z64[m][j][r] = 0.0;
+
+  const int nk = d / LG_BK;
+#pragma unroll
+  for (int p = 0; p < C::STAGES - 1; p++) issue(min(p, nk - 1), p);
+  int buf = 0, nbuf = C::STAGES - 1;
+  for (int kt = 0; kt < nk; kt++) {
+    wait_vmcnt<(C::STAGES - 2) * C::LOADS>();
+    __syncthreads();
+    issue(min(kt + C::STAGES - 1, nk - 1), nbuf);
+    const uint8_t* U = lds + buf * C::STAGE;
+    const uint8_t* Ep = U + C::U_BYTES;
+    f32x4 acc[2][4], acs[2][4];
+#pragma unroll
+    for (int m = 0; m < 2; m++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) acc[m][j] = acs[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+      const bf16x8 a0 = *(const bf16x8*)(U + (wave * 32) * 128 + roff[ks]);
+      const bf16x8 a1 = *(const bf16x8*)(U + (wave * 32 + 16) * 128 + roff[ks]);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (NPLANES == 1) {
+          const bf16x8 B = *(const bf16x8*)(Ep + (j * 16) * 128 + roff[ks]);
+          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, B, acc[0][j], 0, 0, 0);
+          acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, B, acc[1][j], 0, 0, 0);
+        } else {
+          const bf16x8 h = *(const bf16x8*)(Ep + (j * 16) * 128 + roff[ks]);
+          const bf16x8 md = *(const bf16x8*)(Ep + C::E_BYTES + (j * 16) * 128 + roff[ks]);
+          const bf16x8 lo = *(const bf16x8*)(Ep + 2 * C::E_BYTES + (j * 16) * 128 + roff[ks]);
+          acs[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, lo, acs[0][j], 0, 0, 0);
+          acs[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, lo, acs[1][j], 0, 0, 0);
+          acs[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, md, acs[0][j], 0, 0, 0);
+          acs[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, md, acs[1][j], 0, 0, 0);
+          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, h, acc[0][j], 0, 0, 0);
+          acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, h, acc[1][j], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 2; m++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          z64[m][j][r] += (double)acc[m][j][r];
+          if (NPLANES > 1) z64[m][j][r] += (double)acs[m][j][r];
+        }
+    buf = buf + 1 == C::STAGES ? 0 : buf + 1;
+    nbuf = nbuf + 1 == C::STAGES ? 0 : nbuf + 1;
+  }
+  wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
+
+  // D element (4*(lane>>4) + r, lane&15) of each 16x16 block
+#pragma unroll
+  for (int m = 0; m < 2; m++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int t = t0 + wave * 32 + m * 16 + 4 * kg + r;
+      if (t < T) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) scores[(size_t)t * N + e0 + 16 * j + r16] = (float)sigmoid64(z64[m][j][r]);
+      }
+    }
+}
+
+bool route_two_phase_ok(const RouteArgs& a) {
+  return a.in_dtype == MOE_BF16 && (a.router_dtype == MOE_BF16 || a.router_dtype == MOE_F32) &&
+         a.n_routed % LG_BE == 0 && a.d % 128 == 0 && a.T > 0;
+}
+
+size_t route_two_phase_bytes(int T, int N, int d, int router_dtype) {
+  const size_t sc = (((size_t)T * N * 4) + 255) / 256 * 256;
+  const size_t pl = router_dtype == MOE_F32 ? (((size_t)3 * N * d * 2) + 255) / 256 * 256 : 0;
+  return sc + pl;
+}
+
+hipError_t launch_route(const RouteArgs& a, int front, hipStream_t s);
+
+// Phase 1 into `scratch` (scores, then the bf16 planes of fp32 centroids), phase 2 from there.
+hipError_t launch_route_two_phase(const RouteArgs& a, void* scratch, hipStream_t s) {
+  float* scores = (float*)scratch;
+  const size_t sc = (((size_t)a.T * a.n_routed * 4) + 255) / 256 * 256;
+  const dim3 grid(cdiv(a.T, LG_BT), a.n_routed / LG_BE);
+  hipError_t e;
+  if (a.router_dtype == MOE_F32) {
+    uint16_t* planes = (uint16_t*)((uint8_t*)scratch + sc);
+    const long n = (long)a.n_routed * a.d;
+    split_planes_kernel<<<(int)std::min<long>(cdiv<long>(n, 256), 2048), 256, 0, s>>>((const float*)a.E, planes, n);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    auto k = logits_kernel<3>;
+    if ((e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 LogitsCfg<3>::BYTES)) != hipSuccess) return e;
+    k<<<grid, 256, LogitsCfg<3>::BYTES, s>>>((const uint16_t*)a.u, planes, scores, a.T, a.d, a.n_routed);
+  } else {
+    auto k = logits_kernel<1>;
+    if ((e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 LogitsCfg<1>::BYTES)) != hipSuccess) return e;
+    k<<<grid, 256, LogitsCfg<1>::BYTES, s>>>((const uint16_t*)a.u, (const uint16_t*)a.E, scores, a.T, a.d,
+                                             a.n_routed);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  RouteArgs b = a;
+  b.scores_in = scores;
+  b.scores_out = nullptr;
+  return launch_route(b, kFrontScoresIn, s);
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, long n) {

@@ -190,3 +190,28 @@ def test_bias_trajectory_200_steps_scores_in():
         % tuple(ratio[i] for i in (0, 50, 100, 150, 199)))
     # the balancing moves every expert's bias by gamma per step towards the mean load
     assert np.mean(ratio[-20:]) < np.mean(ratio[:20])
+
+
+@pytest.mark.parametrize("name,T", [("v3", None), ("fp8", 1000), ("mid", 4095), ("skew", 2048)])
+def test_two_phase_router_matches_fused(name, T):
+    """moe_forward routes large batches with the tiled two-phase router; its topk_idx, gates and
+    loads must equal moe_route's fused single-kernel router bit for bit (same arithmetic)."""
+    from tests.test_gpu_forward import layer_for
+    cfg = get_config(name)
+    if T is not None:
+        cfg = cfg.with_(T=T)
+    layer = layer_for(cfg)
+    u = dev(gen.tokens(cfg, 3), cfg.in_dtype)
+    b0 = gen.bias_init(cfg) + np.float32(0.004) * (np.arange(cfg.n_routed) % 3 - 1).astype(np.float32)
+    b_fwd = dev(b0, "f32")
+    layer.forward(u, b_fwd, update_bias=False)
+    desc = M.desc_from_config(cfg)
+    idx = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((cfg.T, cfg.top_k), dtype=torch.float32, device="cuda")
+    counts = torch.empty(cfg.n_routed, dtype=torch.int32, device="cuda")
+    M.moe_route(desc, dev(b0, "f32"), idx, gate, counts, u=u, E=layer.E)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(layer.idx), host(idx))
+    assert np.array_equal(host(layer.gate).view(np.uint32), host(gate).view(np.uint32))
+    assert np.array_equal(host(layer.counts), host(counts))
+    log(name, "T=%d two-phase routing == fused routing" % cfg.T)
