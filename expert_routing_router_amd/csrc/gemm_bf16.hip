@@ -304,16 +304,22 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
   constexpr int A_EXTRA = C::A_EXTRA;           // waves below this issue A_PER_WAVE blocks
   const bool a_full = A_EXTRA == 0 || wave < A_EXTRA;
-  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+  // Part P of this wave's stage loads for step kt into buffer buf: its A
+  // blocks first (the last one only on waves that have it), then its B blocks.
+  auto issue_part = [&](auto p_tag, int kt, int buf) __attribute__((always_inline)) {
+    constexpr int P = decltype(p_tag)::value;
     const int soff = kt * DMA_BK * 2;
     const uint32_t sbase = lds0 + buf * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::A_PER_WAVE; i++)
-      if (i < C::A_PER_WAVE - 1 || a_full)
-        dma_b128(xr, aoff[i], soff, sbase + (wave + 8 * i) * 1024);
-#pragma unroll
-    for (int i = 0; i < C::B_PER_WAVE; i++)
-      dma_b128(wr, boff[i], soff, sbase + C::A_BYTES + (wave + 8 * i) * 1024);
+    if constexpr (P < C::A_PER_WAVE) {
+      if (P < C::A_PER_WAVE - 1 || a_full) dma_b128(xr, aoff[P], soff, sbase + (wave + 8 * P) * 1024);
+    } else if constexpr (P < C::A_PER_WAVE + C::B_PER_WAVE) {
+      constexpr int Q = P - C::A_PER_WAVE;
+      dma_b128(wr, boff[Q], soff, sbase + C::A_BYTES + (wave + 8 * Q) * 1024);
+    }
+  };
+  constexpr int NPARTS = C::A_PER_WAVE + C::B_PER_WAVE;
+  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+    static_for<NPARTS>([&](auto p) __attribute__((always_inline)) { issue_part(p, kt, buf); });
   };
 
   f32x16 acc[MB][2];
@@ -338,11 +344,17 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
   const int bro0 = (SWIGLU ? wn * 32 : wn * 64) * 64;
   const int bro1 = (SWIGLU ? HN + wn * 32 : wn * 64 + 32) * 64;
 
-  auto compute_na = [&](auto na_tag, int buf) __attribute__((always_inline)) {
+  // One step: all operand reads of stage `buf`, then the MFMAs in NPARTS
+  // groups with one of the stage loads for step kti (into buffer bufi) in
+  // front of each group. Spreading the loads over the step keeps the
+  // texture unit's queues from filling, which otherwise stalls the issuing
+  // wave (and its MFMAs) right after the barrier.
+  auto compute_na = [&](auto na_tag, int buf, int kti, int bufi) __attribute__((always_inline)) {
     constexpr int NA = decltype(na_tag)::value;
+    constexpr int NA1 = NA > 0 ? NA : 1;
     const uint8_t* A = lds + buf * C::STAGE;
     const uint8_t* B = A + C::A_BYTES;
-    bf16x8 b0[2], b1[2], af[2][NA > 0 ? NA : 1];
+    bf16x8 b0[2], b1[2], af[2][NA1];
     b0[0] = *(const bf16x8*)(B + bro0 + roff0);
     b0[1] = *(const bf16x8*)(B + bro1 + roff0);
 #pragma unroll
@@ -351,16 +363,30 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
     b1[1] = *(const bf16x8*)(B + bro1 + roff1);
 #pragma unroll
     for (int i = 0; i < NA; i++) af[1][i] = *(const bf16x8*)(A + (2 * i + wm) * 2048 + roff1);
-#pragma unroll
-    for (int i = 0; i < NA; i++) {
-      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], b0[0], acc[i][0], 0, 0, 0);
-      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], b0[1], acc[i][1], 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < NA; i++) {
-      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], b1[0], acc[i][0], 0, 0, 0);
-      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], b1[1], acc[i][1], 0, 0, 0);
-    }
+    // 2*NA (k-substep, m-block) pairs of two MFMAs; a load before every PER pairs
+    constexpr int PAIRS = 2 * NA;
+    constexpr int PER = PAIRS > 0 ? (PAIRS + NPARTS - 1) / NPARTS : 1;
+    issue_part(std::integral_constant<int, 0>{}, kti, bufi);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<2 * MB>([&](auto q_tag) __attribute__((always_inline)) {
+      constexpr int q = decltype(q_tag)::value;
+      if constexpr (q < PAIRS) {
+        constexpr int ks = q / NA1, i = q % NA1;
+        const bf16x8* bb = ks == 0 ? b0 : b1;
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bb[0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bb[1], acc[i][1], 0, 0, 0);
+        if constexpr ((q + 1) % PER == 0 && (q + 1) / PER < NPARTS) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_part(std::integral_constant<int, (q + 1) / PER>{}, kti, bufi);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    });
+    // loads left over when few m-blocks are active
+    static_for<NPARTS>([&](auto p_tag) __attribute__((always_inline)) {
+      constexpr int P = decltype(p_tag)::value;
+      if constexpr (P >= 1 && P > PAIRS / PER) issue_part(p_tag, kti, bufi);
+    });
   };
 
   // Ring protocol for step kt: wait for this wave's loads of stage kt (the two
@@ -377,8 +403,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
       if (a_full) wait_vmcnt<2 * (C::A_PER_WAVE + C::B_PER_WAVE)>();
       else wait_vmcnt<2 * (C::A_PER_WAVE - 1 + C::B_PER_WAVE)>();
       __syncthreads();
-      issue(min(kt + 3, nk - 1), (kt + 3) & 3);
-      compute_na(na_tag, kt & 3);
+      compute_na(na_tag, kt & 3, min(kt + 3, nk - 1), (kt + 3) & 3);
     }
     wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
   };

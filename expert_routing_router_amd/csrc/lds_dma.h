@@ -9,6 +9,8 @@
 // be made to wait for all loads in flight.
 #pragma once
 #include "common.h"
+#include <type_traits>
+#include <utility>
 
 namespace moe {
 
@@ -44,6 +46,16 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, long bytes) {
 __device__ __forceinline__ void dma_b32(i32x4 rsrc, int voff, int soff, uint32_t m0) {
   asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0) : "memory");
+}
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // LDS byte address of a shared-memory pointer (the value m0 takes)
