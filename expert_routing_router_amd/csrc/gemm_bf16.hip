@@ -226,34 +226,40 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs a) {
 // K=32 stages: three stages are in flight while one is multiplied, so each
 // CU keeps ~108 KB of loads outstanding instead of one K step's worth.
 //
-// A stage holds 64 bytes (4 chunks of 16) per row. One load instruction of a
-// wave fills one 1 KB block = 16 rows; lane l writes block byte 16*l, i.e.
-// row l>>2, slot l&3, and fetches the chunk c = slot ^ ((row >> 2) & 3). The
-// MFMA operand reads (16 lanes = 16 consecutive rows, one chunk) then hit 16
-// distinct 4-bank groups.
-constexpr int DMA_BK = 32;
-constexpr int DMA_STAGES = 4;
-
-template <int MB>
+// A stage holds RB bytes per row (RB = 64: four K=32 stages; RB = 128: two
+// K=64 stages), CPR = RB/16 chunks of 16 bytes. One load instruction of a
+// wave fills one 1 KB block of RPB = 1024/RB rows; lane l writes block byte
+// 16*l, i.e. row l/CPR, slot l%CPR, and fetches the chunk
+// c = slot ^ ((row >> SH) & (CPR-1)), SH = log2(16/CPR). The MFMA operand
+// reads (16 lanes = 16 consecutive rows, one chunk) then hit 16 distinct
+// 4-bank groups.
+template <int MB, int RB>
 struct DmaCfg {
   static constexpr int THREADS = 512;
   static constexpr int BM = 64 * MB;
   static constexpr int BN = 256;
-  static constexpr int A_BLOCKS = BM / 16;              // 1 KB blocks per stage
-  static constexpr int B_BLOCKS = BN / 16;
-  static constexpr int A_BYTES = BM * DMA_BK * 2;
-  static constexpr int STAGE = (BM + BN) * DMA_BK * 2;
-  static constexpr int BYTES = DMA_STAGES * STAGE;
+  static constexpr int BK = RB / 2;                     // bf16 elements per stage row
+  static constexpr int CPR = RB / 16;
+  static constexpr int RPB = 1024 / RB;
+  static constexpr int SH = RB == 64 ? 2 : 1;
+  static constexpr int SUB = RB / 32;                   // 16-element k-substeps per stage
+  static constexpr int STAGES = RB == 64 ? 4 : 2;
+  static constexpr int A_BLOCKS = BM / RPB;             // 1 KB blocks per stage
+  static constexpr int B_BLOCKS = BN / RPB;
+  static constexpr int A_BYTES = BM * RB;
+  static constexpr int STAGE = (BM + BN) * RB;
+  static constexpr int BYTES = STAGES * STAGE;
   static constexpr int A_PER_WAVE = (A_BLOCKS + 7) / 8;  // waves below A_BLOCKS % 8 take one more
   static constexpr int A_EXTRA = A_BLOCKS % 8;
   static constexpr int B_PER_WAVE = B_BLOCKS / 8;
+  static_assert(RB == 64 || RB == 128, "stage row bytes");
   static_assert(B_BLOCKS % 8 == 0, "B blocks split evenly over 8 waves");
   static_assert(BYTES <= 160 * 1024 - 2048, "LDS budget");
 };
 
-template <int MB, bool SWIGLU>
+template <int MB, bool SWIGLU, int RB>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
-  using C = DmaCfg<MB>;
+  using C = DmaCfg<MB, RB>;
   constexpr int BM = C::BM, BN = C::BN, HN = BN / 2;
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int32_t sprefix[512];
@@ -281,15 +287,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
       ? (const uint16_t*)a.w0 + (size_t)seg * a.wstride0
       : (const uint16_t*)a.w1 + (size_t)(seg - a.n_first) * a.wstride1;
 
-  // ---- per-lane global offsets of this wave's blocks (fixed over K)
-  const int brow = lane >> 2;                                  // row within a block
-  const int bchunk = (lane & 3) ^ ((lane >> 4) & 3);           // chunk this lane fetches
+  // ---- per-lane global offsets of this wave's blocks (fixed over K). Block
+  // wave + 8i starts at row RPB*(wave + 8i); the +8i part leaves the swizzle unchanged.
+  const int brow = lane / C::CPR;                              // row within a block
+  const int bchunk = (lane % C::CPR) ^ (((C::RPB * wave + brow) >> C::SH) & (C::CPR - 1));
   const i32x4 xr = rsrc_words(a.x, a.x_rows * (long)K * 2);
   const i32x4 wr = rsrc_words(wbase, (long)(SWIGLU ? 2 * a.N : a.N) * K * 2);
   int aoff[C::A_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::A_PER_WAVE; i++) {
-    const int r = (wave + 8 * i) * 16 + brow;   // blocks past A_BLOCKS are never issued
+    const int r = (wave + 8 * i) * C::RPB + brow;   // blocks past A_BLOCKS are never issued
     const int rr = row0 + min(r, mvalid - 1);
     const int src = a.row_index ? a.row_index[rr] : rr;
     aoff[i] = r < mvalid ? (src * K + bchunk * 8) * 2 : kOutOfRange;
@@ -297,18 +304,18 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
   int boff[C::B_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::B_PER_WAVE; i++) {
-    const int r = (wave + 8 * i) * 16 + brow;   // 0 .. BN-1
+    const int r = (wave + 8 * i) * C::RPB + brow;   // 0 .. BN-1
     const int wrow = SWIGLU ? (r < HN ? ntile * HN + r : a.N + ntile * HN + (r - HN)) : ntile * BN + r;
     boff[i] = (wrow * K + bchunk * 8) * 2;
   }
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  const uint32_t lds0 = lds_addr(lds);
   constexpr int A_EXTRA = C::A_EXTRA;           // waves below this issue A_PER_WAVE blocks
   const bool a_full = A_EXTRA == 0 || wave < A_EXTRA;
   // Part P of this wave's stage loads for step kt into buffer buf: its A
   // blocks first (the last one only on waves that have it), then its B blocks.
   auto issue_part = [&](auto p_tag, int kt, int buf) __attribute__((always_inline)) {
     constexpr int P = decltype(p_tag)::value;
-    const int soff = kt * DMA_BK * 2;
+    const int soff = kt * RB;
     const uint32_t sbase = lds0 + buf * C::STAGE;
     if constexpr (P < C::A_PER_WAVE) {
       if (P < C::A_PER_WAVE - 1 || a_full) dma_b128(xr, aoff[P], soff, sbase + (wave + 8 * P) * 1024);
@@ -335,49 +342,52 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
   for (int i = 0; i < MB; i++)
     if ((2 * i + wm) * 32 < mvalid) mb_active = i + 1;
 
-  // operand read offsets: row = block*32 + l32 has (row >> 2) & 3 == (l32 >> 2) & 3
+  // operand read offsets: row = block*32 + l32 has the swizzle of row l32
   const int l32 = lane & 31, khalf = lane >> 5;
-  const int sw = (l32 >> 2) & 3;
-  const int roff0 = l32 * 64 + ((khalf ^ sw) << 4);         // k-substep 0: chunk khalf
-  const int roff1 = l32 * 64 + (((2 + khalf) ^ sw) << 4);   // k-substep 1: chunk 2 + khalf
+  const int sw = (l32 >> C::SH) & (C::CPR - 1);
+  int roff[C::SUB];                                  // k-substep ks: chunk 2*ks + khalf
+#pragma unroll
+  for (int ks = 0; ks < C::SUB; ks++) roff[ks] = l32 * RB + (((2 * ks + khalf) ^ sw) << 4);
   // B rows of this wave: SwiGLU gate rows wn*32.. and up rows HN + wn*32..; else wn*64 + j*32
-  const int bro0 = (SWIGLU ? wn * 32 : wn * 64) * 64;
-  const int bro1 = (SWIGLU ? HN + wn * 32 : wn * 64 + 32) * 64;
+  const int bro0 = (SWIGLU ? wn * 32 : wn * 64) * RB;
+  const int bro1 = (SWIGLU ? HN + wn * 32 : wn * 64 + 32) * RB;
 
-  // One step: all operand reads of stage `buf`, then the MFMAs in NPARTS
-  // groups with one of the stage loads for step kti (into buffer bufi) in
-  // front of each group. Spreading the loads over the step keeps the
-  // texture unit's queues from filling, which otherwise stalls the issuing
-  // wave (and its MFMAs) right after the barrier.
-  auto compute_na = [&](auto na_tag, int buf, int kti, int bufi) __attribute__((always_inline)) {
+  // Two k-substeps (h, h+1) of stage `buf`: all their operand reads, then the
+  // MFMAs in groups with one of the stage loads P0..P1-1 for step kti (into
+  // buffer bufi) in front of each group. Spreading the loads over the step
+  // keeps the texture unit's queues from filling, which otherwise stalls the
+  // issuing wave (and its MFMAs) right after the barrier.
+  auto compute_half = [&](auto na_tag, auto h_tag, auto p0_tag, auto p1_tag, int buf, int kti, int bufi)
+      __attribute__((always_inline)) {
     constexpr int NA = decltype(na_tag)::value;
     constexpr int NA1 = NA > 0 ? NA : 1;
+    constexpr int H = decltype(h_tag)::value;
+    constexpr int P0 = decltype(p0_tag)::value, P1 = decltype(p1_tag)::value;
     const uint8_t* A = lds + buf * C::STAGE;
     const uint8_t* B = A + C::A_BYTES;
-    bf16x8 b0[2], b1[2], af[2][NA1];
-    b0[0] = *(const bf16x8*)(B + bro0 + roff0);
-    b0[1] = *(const bf16x8*)(B + bro1 + roff0);
+    bf16x8 bf[2][2], af[2][NA1];
 #pragma unroll
-    for (int i = 0; i < NA; i++) af[0][i] = *(const bf16x8*)(A + (2 * i + wm) * 2048 + roff0);
-    b1[0] = *(const bf16x8*)(B + bro0 + roff1);
-    b1[1] = *(const bf16x8*)(B + bro1 + roff1);
+    for (int s = 0; s < 2; s++) {
+      bf[s][0] = *(const bf16x8*)(B + bro0 + roff[H + s]);
+      bf[s][1] = *(const bf16x8*)(B + bro1 + roff[H + s]);
 #pragma unroll
-    for (int i = 0; i < NA; i++) af[1][i] = *(const bf16x8*)(A + (2 * i + wm) * 2048 + roff1);
+      for (int i = 0; i < NA; i++) af[s][i] = *(const bf16x8*)(A + (2 * i + wm) * 32 * RB + roff[H + s]);
+    }
     // 2*NA (k-substep, m-block) pairs of two MFMAs; a load before every PER pairs
+    constexpr int NP = P1 - P0;
     constexpr int PAIRS = 2 * NA;
-    constexpr int PER = PAIRS > 0 ? (PAIRS + NPARTS - 1) / NPARTS : 1;
-    issue_part(std::integral_constant<int, 0>{}, kti, bufi);
+    constexpr int PER = PAIRS > 0 && NP > 0 ? (PAIRS + NP - 1) / NP : 1;
+    if constexpr (NP > 0) issue_part(std::integral_constant<int, P0>{}, kti, bufi);
     __builtin_amdgcn_sched_barrier(0);
     static_for<2 * MB>([&](auto q_tag) __attribute__((always_inline)) {
       constexpr int q = decltype(q_tag)::value;
       if constexpr (q < PAIRS) {
-        constexpr int ks = q / NA1, i = q % NA1;
-        const bf16x8* bb = ks == 0 ? b0 : b1;
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bb[0], acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bb[1], acc[i][1], 0, 0, 0);
-        if constexpr ((q + 1) % PER == 0 && (q + 1) / PER < NPARTS) {
+        constexpr int s = q / NA1, i = q % NA1;
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bf[s][0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bf[s][1], acc[i][1], 0, 0, 0);
+        if constexpr ((q + 1) % PER == 0 && (q + 1) / PER < NP) {
           __builtin_amdgcn_sched_barrier(0);
-          issue_part(std::integral_constant<int, (q + 1) / PER>{}, kti, bufi);
+          issue_part(std::integral_constant<int, P0 + (q + 1) / PER>{}, kti, bufi);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -385,25 +395,36 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
     // loads left over when few m-blocks are active
     static_for<NPARTS>([&](auto p_tag) __attribute__((always_inline)) {
       constexpr int P = decltype(p_tag)::value;
-      if constexpr (P >= 1 && P > PAIRS / PER) issue_part(p_tag, kti, bufi);
+      if constexpr (P > P0 && P < P1 && P - P0 > PAIRS / PER) issue_part(p_tag, kti, bufi);
+    });
+  };
+  // one stage = SUB/2 halves; the loads split evenly between them
+  auto compute_na = [&](auto na_tag, int buf, int kti, int bufi) __attribute__((always_inline)) {
+    constexpr int HALVES = C::SUB / 2;
+    static_for<HALVES>([&](auto hh) __attribute__((always_inline)) {
+      constexpr int X = decltype(hh)::value;
+      compute_half(na_tag, std::integral_constant<int, 2 * X>{},
+                   std::integral_constant<int, NPARTS * X / HALVES>{},
+                   std::integral_constant<int, NPARTS * (X + 1) / HALVES>{}, buf, kti, bufi);
     });
   };
 
-  // Ring protocol for step kt: wait for this wave's loads of stage kt (the two
-  // younger stages may stay outstanding), barrier (every wave's stage-kt data
-  // is in LDS and every wave is done reading stage kt-1), refill stage kt-1's
-  // buffer with step kt+3, multiply stage kt. Loads past the last step re-read
-  // it into a buffer that is never read again, so the count per step is fixed.
-  const int nk = K / DMA_BK;
+  // Ring protocol for step kt: wait for this wave's loads of stage kt (the
+  // STAGES-2 younger stages may stay outstanding), barrier (every wave's
+  // stage-kt data is in LDS and every wave is done reading stage kt-1), then
+  // multiply stage kt while refilling stage kt-1's buffer with step
+  // kt+STAGES-1. Loads past the last step re-read it into a buffer that is
+  // never read again, so the count per step is fixed.
+  constexpr int S = C::STAGES;
+  const int nk = K / C::BK;
   auto k_loop = [&](auto na_tag) __attribute__((always_inline)) {
-    issue(0, 0);
-    issue(min(1, nk - 1), 1);
-    issue(min(2, nk - 1), 2);
+#pragma unroll
+    for (int p = 0; p < S - 1; p++) issue(min(p, nk - 1), p);
     for (int kt = 0; kt < nk; kt++) {
-      if (a_full) wait_vmcnt<2 * (C::A_PER_WAVE + C::B_PER_WAVE)>();
-      else wait_vmcnt<2 * (C::A_PER_WAVE - 1 + C::B_PER_WAVE)>();
+      if (a_full) wait_vmcnt<(S - 2) * NPARTS>();
+      else wait_vmcnt<(S - 2) * (NPARTS - 1)>();
       __syncthreads();
-      compute_na(na_tag, kt & 3, min(kt + 3, nk - 1), (kt + 3) & 3);
+      compute_na(na_tag, kt % S, min(kt + S - 1, nk - 1), (kt + S - 1) % S);
     }
     wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
   };
@@ -502,14 +523,18 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+#ifndef GEMM_DMA_RB
+#define GEMM_DMA_RB 64
+#endif
 template <int MB, bool SWIGLU>
 static hipError_t launch_bf16_dma(const GemmArgs& a, hipStream_t s) {
-  using C = DmaCfg<MB>;
+  constexpr int RB = GEMM_DMA_RB;
+  using C = DmaCfg<MB, RB>;
   const int n_tiles = SWIGLU ? a.N / (C::BN / 2) : a.N / C::BN;
   const long mtiles_bound = (long)a.rows_bound / C::BM + a.n_seg;
   const long grid = (mtiles_bound * n_tiles + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  auto k = gemm_bf16_dma_kernel<MB, SWIGLU>;
+  auto k = gemm_bf16_dma_kernel<MB, SWIGLU, RB>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
   if (e != hipSuccess) return e;
   k<<<dim3((unsigned)grid), C::THREADS, C::BYTES, s>>>(a);
