@@ -32,15 +32,18 @@ extern "C" __device__ unsigned int __ockl_wfred_min_u32(unsigned int);
 namespace moe {
 
 constexpr int RT_BT = 32;
+constexpr int RT_BT_SEL = 8;
 constexpr int RT_THREADS = 256;
 constexpr int RT_NMAX = 256;
 constexpr int RT_QMAX = 8;
 
-struct RouterLds {
-  float s[RT_BT][RT_NMAX];
+template <int BT>
+struct RouterLdsT {
+  float s[BT][RT_NMAX];
   float b[RT_NMAX];
   int cnt[RT_NMAX];
 };
+using RouterLds = RouterLdsT<RT_BT>;      // the fused front ends work on 32 tokens
 
 __device__ __forceinline__ double sigmoid64(double z) {
   if (z >= 0.0) return 1.0 / (1.0 + exp(-z));
@@ -213,7 +216,8 @@ __device__ void front_f64(const RouteArgs& a, RouterLds& sh, int t0, int nt) {
 // selection round is two wave reductions (device-library, DPP based): the
 // largest ordered key, then the lowest expert index holding it -- the total
 // order (key desc, index asc); -0 and +0 share one ordered key.
-__device__ void select_tokens(const RouteArgs& a, RouterLds& sh, int t0, int nt) {
+template <int BT>
+__device__ void select_tokens(const RouteArgs& a, RouterLdsT<BT>& sh, int t0, int nt) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int N = a.n_routed, K = a.top_k, G = a.n_groups, M = a.topk_groups, q = a.group_topk;
   const int S = N / G;
@@ -285,23 +289,24 @@ __device__ void select_tokens(const RouteArgs& a, RouterLds& sh, int t0, int nt)
   }
 }
 
-template <int FRONT, bool U_BF16, bool E_BF16>
+template <int FRONT, bool U_BF16, bool E_BF16, int BT = RT_BT>
 __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
-  __shared__ RouterLds sh;
-  const int t0 = blockIdx.x * RT_BT;
-  const int nt = min(RT_BT, a.T - t0);
+  static_assert(FRONT == kFrontScoresIn || BT == RT_BT, "the fused front ends work on 32 tokens");
+  __shared__ RouterLdsT<BT> sh;
+  const int t0 = blockIdx.x * BT;
+  const int nt = min(BT, a.T - t0);
   for (int e = threadIdx.x; e < a.n_routed; e += RT_THREADS) {
     sh.b[e] = a.b[e];
     sh.cnt[e] = 0;
   }
-  if (FRONT == kFrontScoresIn) {
+  if constexpr (FRONT == kFrontScoresIn) {
     for (int p = threadIdx.x; p < nt * a.n_routed; p += RT_THREADS) {
       const int t = p / a.n_routed, e = p - t * a.n_routed;
       sh.s[t][e] = a.scores_in[(size_t)(t0 + t) * a.n_routed + e];
     }
-  } else if (FRONT == kFrontMfma) {
+  } else if constexpr (FRONT == kFrontMfma) {
     front_mfma<false>(a, sh, t0);
-  } else if (FRONT == kFrontMfmaSplitE) {
+  } else if constexpr (FRONT == kFrontMfmaSplitE) {
     front_mfma<true>(a, sh, t0);
   } else {
     front_f64<U_BF16, E_BF16>(a, sh, t0, nt);
@@ -541,7 +546,10 @@ hipError_t launch_route(const RouteArgs& a, int front, hipStream_t s) {
   const dim3 grid(cdiv(a.T, RT_BT));
   const bool ub = a.in_dtype == MOE_BF16;
   switch (front) {
-    case kFrontScoresIn: route_kernel<kFrontScoresIn, false, false><<<grid, RT_THREADS, 0, s>>>(a); break;
+    case kFrontScoresIn:
+      // selection only: 8 tokens per workgroup (2 per wave) for more waves in flight
+      route_kernel<kFrontScoresIn, false, false, RT_BT_SEL><<<dim3(cdiv(a.T, RT_BT_SEL)), RT_THREADS, 0, s>>>(a);
+      break;
     case kFrontMfma: route_kernel<kFrontMfma, true, true><<<grid, RT_THREADS, 0, s>>>(a); break;
     case kFrontMfmaSplitE: route_kernel<kFrontMfmaSplitE, true, false><<<grid, RT_THREADS, 0, s>>>(a); break;
     default: {
