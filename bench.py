@@ -237,6 +237,34 @@ def main():
                       "mean_last_20": round(sum(ratios[-20:]) / len(ratios[-20:]), 3)}
         log("load trajectory: max/mean %.3f -> %.3f over %d steps" % (ratios[0], ratios[-1], len(ratios)))
 
+    # the sequence-wise balance loss (forward value) from this layer's router outputs:
+    # timed on its own, it is not part of the forward step
+    seq_balance = None
+    if cfg.T > 0:
+        seq_len = 4096 if cfg.T % 4096 == 0 else cfg.T
+        desc = M.desc_from_config(cfg)
+        sc = torch.empty((cfg.T, cfg.n_routed), dtype=torch.float32, device="cuda:0")
+        ri = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device="cuda:0")
+        rg = torch.empty((cfg.T, cfg.top_k), dtype=torch.float32, device="cuda:0")
+        rc = torch.empty(cfg.n_routed, dtype=torch.int32, device="cuda:0")
+        M.moe_route(desc, b, ri, rg, rc, u=us[0], E=layer.E, scores_out=sc)
+        bl = torch.empty(cfg.T // seq_len, dtype=torch.float32, device="cuda:0")
+        bws = torch.empty(M.moe_seq_balance_workspace_bytes(desc, seq_len), dtype=torch.uint8, device="cuda:0")
+        M.moe_seq_balance_loss(desc, seq_len, 1e-4, sc, ri, bl, bws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            M.moe_seq_balance_loss(desc, seq_len, 1e-4, sc, ri, bl, bws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sb_ms = e0.elapsed_time(e1) / 20
+        sb_bytes = cfg.T * cfg.n_routed * 4 + cfg.T * cfg.top_k * 4
+        seq_balance = {"ms": round(sb_ms, 4), "GB/s": round(sb_bytes / sb_ms / 1e6, 1),
+                       "hbm_frac": round(sb_bytes / sb_ms / 1e6 / PEAK_HBM_GBS, 4), "seq_len": seq_len,
+                       "loss_over_alpha": [round(float(x) / 1e-4, 6) for x in bl.cpu()]}
+        log("seq balance loss: %.4f ms for %d sequences" % (sb_ms, cfg.T // seq_len))
+
     alg = algorithmic(cfg)
     peak_tf = PEAK_TFLOPS[cfg.expert_dtype]
     kernels = {}
@@ -251,6 +279,8 @@ def main():
             k["TFLOP/s"] = round(tf, 1)
             k["mfma_frac"] = round(tf / (peak_tf if name.startswith("gemm") else PEAK_TFLOPS["bf16"]), 4)
         kernels[name] = k
+    if seq_balance:
+        kernels["seq_balance_loss"] = seq_balance
     g_ms = (stage_ms["gemm1"] + stage_ms["gemm2"]) / max(calls, 1)
     g_tf = (alg["gemm1"]["flops"] + alg["gemm2"]["flops"]) / g_ms / 1e9
     kernels["grouped_gemm"] = {"ms": round(g_ms, 4), "TFLOP/s": round(g_tf, 1),

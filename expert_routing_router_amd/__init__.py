@@ -14,5 +14,6 @@ from ._lib import (  # noqa: F401
     lib, header_symbols, make_desc, desc_from_config, make_weights,
     moe_validate, moe_workspace_bytes, moe_expert_ffn_workspace_bytes,
     moe_route, moe_permute, moe_expert_ffn, moe_combine, moe_update_bias, moe_forward,
-    moe_quantize_fp8, moe_profile_enable, moe_profile_read, STAGES,
+    moe_quantize_fp8, moe_seq_balance_workspace_bytes, moe_seq_balance_loss,
+    moe_profile_enable, moe_profile_read, STAGES,
 )

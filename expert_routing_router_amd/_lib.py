@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
             "moe_forward": ([D, ctypes.POINTER(MoeWeights), P, P, P, ctypes.POINTER(MoeRouteOut),
                              I32, P, SZ, P], I32),
             "moe_quantize_fp8": ([I32, P, I32, I32, I32, P, P, P], I32),
+            "moe_seq_balance_workspace_bytes": ([D, I32], SZ),
+            "moe_seq_balance_loss": ([D, I32, ctypes.c_float, P, P, P, P, P, P, SZ, P], I32),
             "moe_profile_enable": ([I32], I32),
             "moe_profile_read": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), I32], I32),
         }
@@ -207,6 +209,17 @@ def moe_quantize_fp8(kind, src, rows, cols, q, scale, stream=None):
     _check("moe_quantize_fp8", lib().moe_quantize_fp8(
         kind, _ptr(src, "src"), sdt, rows, cols, _ptr(q, "q"), _ptr(scale, "scale"),
         _stream(stream)))
+
+
+def moe_seq_balance_workspace_bytes(desc, seq_len) -> int:
+    return lib().moe_seq_balance_workspace_bytes(ctypes.byref(desc), seq_len)
+
+
+def moe_seq_balance_loss(desc, seq_len, alpha, scores, topk_idx, loss, ws, f=None, P=None, stream=None):
+    _check("moe_seq_balance_loss", lib().moe_seq_balance_loss(
+        ctypes.byref(desc), seq_len, alpha, _ptr(scores, "scores"), _ptr(topk_idx, "topk_idx"),
+        _ptr(f, "f", False), _ptr(P, "P", False), _ptr(loss, "loss"), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)))
 
 
 STAGES = ("route", "permute", "quant_x", "gemm1", "gemm2", "combine", "bias")

@@ -369,6 +369,25 @@ extern "C" int moe_update_bias(const moe_desc_t* d, const int32_t* counts, float
                                        (hipStream_t)stream));
 }
 
+extern "C" size_t moe_seq_balance_workspace_bytes(const moe_desc_t* d, int32_t seq_len) {
+  if (moe_validate(d) != MOE_OK || seq_len < 1 || d->T % seq_len) return 0;
+  return seq_balance_ws_bytes(d->T, d->n_routed, seq_len);
+}
+
+extern "C" int moe_seq_balance_loss(const moe_desc_t* d, int32_t seq_len, float alpha, const float* scores,
+                                    const int32_t* topk_idx, float* f, float* P, float* loss, void* ws,
+                                    size_t ws_bytes, moe_stream_t stream) {
+  int st = moe_validate(d);
+  if (st) return st;
+  if (seq_len < 1 || d->T % seq_len) return MOE_EINVAL;
+  if (!aligned(scores) || !aligned(topk_idx) || !aligned(loss) || !aligned(ws)) return MOE_EINVAL;
+  if (!aligned_or_null(f) || !aligned_or_null(P)) return MOE_EINVAL;
+  if (d->T == 0) return MOE_OK;
+  if (ws_bytes < seq_balance_ws_bytes(d->T, d->n_routed, seq_len)) return MOE_EWORKSPACE;
+  return hip_status(launch_seq_balance(scores, topk_idx, d->T, d->n_routed, d->top_k, seq_len, alpha, f, P, loss,
+                                       ws, (hipStream_t)stream));
+}
+
 __global__ void iota_kernel(int32_t* p, int n, int step) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i <= n) p[i] = i * step;

@@ -74,6 +74,11 @@ struct CombineArgs {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_update_bias(const int32_t* counts, float* b, int n_routed, long total,
                               float gamma, hipStream_t s);
+
+// sequence-wise balance loss (forward value)
+size_t seq_balance_ws_bytes(int T, int N, int seq_len);
+hipError_t launch_seq_balance(const float* s, const int32_t* idx, int T, int N, int K, int seq_len, float alpha,
+                              float* f, float* P, float* loss, void* ws, hipStream_t st);
 hipError_t launch_quant_act(const void* src, int src_dtype, long rows, int cols,
                             const int32_t* row_index, uint8_t* q, float* scale, hipStream_t s);
 hipError_t launch_quant_w(const void* src, int src_dtype, long rows, int cols, uint8_t* q,

@@ -175,6 +175,24 @@ int moe_combine(const moe_desc_t* desc, const void* u, const void* y, const void
 int moe_update_bias(const moe_desc_t* desc, const int32_t* counts, float* b,
                     moe_stream_t stream);
 
+/* Complementary sequence-wise balance loss, forward value (pwwt.cn note
+ * section 1.2; alpha = 0.0001 on the xyznot.com guides, section 2). The T
+ * tokens are T/seq_len consecutive sequences; for sequence q
+ *   f_i = #{(t,k) in q : topk_idx[t,k] = i} / (K * seq_len)
+ *   P_i = mean over t in q of scores[t,i] / sum_j scores[t,j]
+ *         (1/N_r for a token whose affinities sum to 0)
+ *   loss[q] = alpha * sum_i f_i * P_i
+ * (the page's formula is missing; these normalisations are the reading taken).
+ *   scores [T, N_r] fp32: the router's affinities (moe_route's scores_out);
+ *   topk_idx [T, K] int32: its selections. f, P [T/seq_len, N_r] fp32 (each
+ *   nullable), loss [T/seq_len] fp32. Sums are fp64 in a fixed order.
+ *   ws: moe_seq_balance_workspace_bytes(desc, seq_len) bytes (0 on bad args).
+ * MOE_EINVAL when seq_len < 1 or T % seq_len != 0. */
+size_t moe_seq_balance_workspace_bytes(const moe_desc_t* desc, int32_t seq_len);
+int moe_seq_balance_loss(const moe_desc_t* desc, int32_t seq_len, float alpha, const float* scores,
+                         const int32_t* topk_idx, float* f, float* P, float* loss, void* ws,
+                         size_t ws_bytes, moe_stream_t stream);
+
 /* Whole layer: route -> permute -> grouped experts (routed + shared) ->
  * combine -> (update_bias != 0) bias update. b is read by the router and, if
  * update_bias, updated in place after the loads are known.

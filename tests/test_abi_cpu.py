@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = L.header_symbols()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     raw = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -150,3 +150,16 @@ def test_binding_requires_device_tensors(lib):
     d = _v3()
     with pytest.raises(ValueError):
         M.moe_update_bias(d, torch.zeros(256, dtype=torch.int32), torch.zeros(256))
+
+
+def test_seq_balance_arg_errors(lib):
+    """seq_len must divide T; workspace size 0 on bad arguments (checked before any launch)."""
+    d = M.make_desc(T=64, d=256, n_routed=16, top_k=4, n_groups=4, topk_groups=2)
+    assert M.moe_seq_balance_workspace_bytes(d, 16) > 0
+    assert M.moe_seq_balance_workspace_bytes(d, 0) == 0
+    assert M.moe_seq_balance_workspace_bytes(d, 48) == 0
+    null = ctypes.c_void_p(16)
+    st = lib.moe_seq_balance_loss(ctypes.byref(d), 48, 1e-4, null, null, None, None, null, null, 1 << 20, None)
+    assert st == M.MOE_EINVAL
+    st = lib.moe_seq_balance_loss(ctypes.byref(d), 0, 1e-4, null, null, None, None, null, null, 1 << 20, None)
+    assert st == M.MOE_EINVAL
