@@ -45,6 +45,10 @@ class MoeWeights(ctypes.Structure):
         "w13_shared_scale", "w2_shared_scale")]
 
 
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("du", "dE", "dw13", "dw2", "dw13_shared", "dw2_shared")]
+
+
 class MoeRouteOut(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_gate", ctypes.c_void_p), ("counts", ctypes.c_void_p)]
 
@@ -77,6 +81,10 @@ def lib() -> ctypes.CDLL:
                              I32, P, SZ, P], I32),
             "moe_quantize_fp8": ([I32, P, I32, I32, I32, P, P, P], I32),
             "moe_seq_balance_workspace_bytes": ([D, I32], SZ),
+            "moe_transpose_expert_weights": ([D, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeights), P], I32),
+            "moe_backward_workspace_bytes": ([D], SZ),
+            "moe_backward": ([D, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeights), P, P, P,
+                              ctypes.POINTER(MoeGrads), P, SZ, P], I32),
             "moe_seq_balance_loss": ([D, I32, ctypes.c_float, P, P, P, P, P, P, SZ, P], I32),
             "moe_profile_enable": ([I32], I32),
             "moe_profile_read": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), I32], I32),
@@ -220,6 +228,28 @@ def moe_seq_balance_loss(desc, seq_len, alpha, scores, topk_idx, loss, ws, f=Non
         ctypes.byref(desc), seq_len, alpha, _ptr(scores, "scores"), _ptr(topk_idx, "topk_idx"),
         _ptr(f, "f", False), _ptr(P, "P", False), _ptr(loss, "loss"), _ptr(ws, "ws"),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_transpose_expert_weights(desc, weights: MoeWeights, wt: MoeWeights, stream=None):
+    _check("moe_transpose_expert_weights", lib().moe_transpose_expert_weights(
+        ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(wt), _stream(stream)))
+
+
+def moe_backward_workspace_bytes(desc) -> int:
+    return lib().moe_backward_workspace_bytes(ctypes.byref(desc))
+
+
+def make_grads(du, dE, dw13, dw2, dw13_shared=None, dw2_shared=None) -> MoeGrads:
+    return MoeGrads(*[_ptr(t, n, n in ("du", "dE", "dw13", "dw2")) for t, n in (
+        (du, "du"), (dE, "dE"), (dw13, "dw13"), (dw2, "dw2"), (dw13_shared, "dw13_shared"),
+        (dw2_shared, "dw2_shared"))])
+
+
+def moe_backward(desc, weights: MoeWeights, wt: MoeWeights, u, b, dout, grads: MoeGrads, ws, stream=None):
+    _check("moe_backward", lib().moe_backward(
+        ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(wt), _ptr(u, "u"), _ptr(b, "b"),
+        _ptr(dout, "dout"), ctypes.byref(grads), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream(stream)))
 
 
 STAGES = ("route", "permute", "quant_x", "gemm1", "gemm2", "combine", "bias")

@@ -1,0 +1,364 @@
+// Backward pass of the DeepSeekMoE layer (bf16 experts), for the routing the
+// forward chose.
+//
+// Forward (output equation of the xyznot.com DeepSeek-V3 guides, "Metodo"
+// section 2): out_t = u_t + sum_s FFN_s(u_t) + sum_k g_{t,k} FFN_{idx_k}(u_t),
+// g = s_sel / sum(s_sel), s = Sigmoid(u E^T), FFN(x) = W2 (SiLU(W1 x) * W3 x).
+// The selection and the bias are piecewise constant (the bias only routes:
+// pwwt.cn note 1.1.2-1.1.3), so with dout = d(loss)/d(out):
+//   dY_{t,k}   = g_{t,k} dout_t              (routed rows), dout_t (shared rows)
+//   dg_{t,k}   = <dout_t, Y_{t,k}>
+//   dH = dY W2,  dA = dH * B * sig(A) * (1 + A (1 - sig(A))),  dB = dH * SiLU(A)
+//   dX = [dA dB] W13,  dW2 = dY^T H,  dW13 = [dA dB]^T X       (per expert)
+//   ds_{t,k}   = (dg_{t,k} - sum_j g_{t,j} dg_{t,j}) / sum_j s_{t,j}
+//   dz_{t,k}   = ds_{t,k} s_{t,k} (1 - s_{t,k})
+//   du_t = dout_t + sum_s dX_s,t + sum_k dX_{t,k} + sum_k dz_{t,k} e_{idx_k}
+//   dE_i = sum over tokens that selected i of dz_{t,k} u_t
+// This file holds the element-wise pieces, the per-expert weight-gradient
+// GEMM and the weight transposes; the dense GEMMs (A|B, Y, dH, dX) reuse the
+// forward's grouped GEMM kernels with transposed weight copies.
+#include "common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+__device__ __forceinline__ void load_bf16x8(const uint16_t* p, float* v) {
+  const i32x4 q = *(const i32x4*)p;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    v[2 * i] = __uint_as_float(((uint32_t)q[i]) << 16);
+    v[2 * i + 1] = __uint_as_float(((uint32_t)q[i]) & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void store_bf16x8(uint16_t* p, const float* v) {
+  i32x4 q;
+#pragma unroll
+  for (int i = 0; i < 4; i++) q[i] = (int)pack_bf16x2(v[2 * i], v[2 * i + 1]);
+  *(i32x4*)p = q;
+}
+__device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
+
+// H = SiLU(A) * B from AB = [A | B] (rows of 2I), bf16 in and out, fp32 math
+__global__ void swiglu_fwd_kernel(const uint16_t* __restrict__ ab, uint16_t* __restrict__ h, long rows, int I) {
+  const long n8 = rows * (I / 8);
+  for (long p = (long)blockIdx.x * blockDim.x + threadIdx.x; p < n8; p += (long)gridDim.x * blockDim.x) {
+    const long r = p / (I / 8);
+    const int c = (int)(p - r * (I / 8)) * 8;
+    float a[8], b[8], o[8];
+    load_bf16x8(ab + r * 2 * I + c, a);
+    load_bf16x8(ab + r * 2 * I + I + c, b);
+#pragma unroll
+    for (int i = 0; i < 8; i++) o[i] = a[i] * sigmoidf_(a[i]) * b[i];
+    store_bf16x8(h + r * I + c, o);
+  }
+}
+
+// dA, dB from dH and AB: dA = dH * B * sig(A) * (1 + A (1 - sig(A))), dB = dH * SiLU(A)
+__global__ void swiglu_bwd_kernel(const uint16_t* __restrict__ dh, const uint16_t* __restrict__ ab,
+                                  uint16_t* __restrict__ dab, long rows, int I) {
+  const long n8 = rows * (I / 8);
+  for (long p = (long)blockIdx.x * blockDim.x + threadIdx.x; p < n8; p += (long)gridDim.x * blockDim.x) {
+    const long r = p / (I / 8);
+    const int c = (int)(p - r * (I / 8)) * 8;
+    float a[8], b[8], g[8], da[8], db[8];
+    load_bf16x8(ab + r * 2 * I + c, a);
+    load_bf16x8(ab + r * 2 * I + I + c, b);
+    load_bf16x8(dh + r * I + c, g);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float sg = sigmoidf_(a[i]);
+      da[i] = g[i] * b[i] * sg * (1.0f + a[i] * (1.0f - sg));
+      db[i] = g[i] * a[i] * sg;
+    }
+    store_bf16x8(dab + r * 2 * I + c, da);
+    store_bf16x8(dab + r * 2 * I + I + c, db);
+  }
+}
+
+// One workgroup per token: the K gate gradients dg = <dout_t, Y_{t,k}> (fp32),
+// and the rows of dY: g * dout for its routed rows, dout for its shared rows.
+__global__ __launch_bounds__(256) void dgate_dy_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict__ y,
+                                                       const int32_t* __restrict__ slot_row, const float* __restrict__ gate,
+                                                       int d, int K, int n_shared, long shared_base, long shared_stride,
+                                                       float* __restrict__ dg, uint16_t* __restrict__ dy) {
+  __shared__ float red[64][4];
+  const int t = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint16_t* drow = dout + (size_t)t * d;
+  for (int k = 0; k < K; k++) {
+    const long row = slot_row[(size_t)t * K + k];
+    const float g = gate[(size_t)t * K + k];
+    float acc = 0.f;
+    for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+      float a[8], b[8], o[8];
+      load_bf16x8(drow + c, a);
+      load_bf16x8(y + row * d + c, b);
+#pragma unroll
+      for (int i = 0; i < 8; i++) { acc = fmaf(a[i], b[i], acc); o[i] = g * a[i]; }
+      store_bf16x8(dy + row * d + c, o);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) red[k & 63][w] = acc;
+  }
+  for (int s = 0; s < n_shared; s++) {
+    const long row = shared_base + (long)s * shared_stride + t;
+    for (int c = threadIdx.x * 8; c < d; c += 256 * 8)
+      *(i32x4*)(dy + row * d + c) = *(const i32x4*)(drow + c);
+  }
+  __syncthreads();
+  if (threadIdx.x < K) {
+    const int k = threadIdx.x;
+    dg[(size_t)t * K + k] = ((red[k][0] + red[k][1]) + red[k][2]) + red[k][3];
+  }
+}
+
+// Per token: dz_{t,k} = (dg_k - sum_j g_j dg_j) / sum_j s_j * s_k (1 - s_k), in fp64
+__global__ void dz_kernel(const float* __restrict__ scores, const int32_t* __restrict__ idx,
+                          const float* __restrict__ dg, int T, int N, int K, float* __restrict__ dz) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  double S = 0.0;
+  for (int k = 0; k < K; k++) S += (double)scores[(size_t)t * N + idx[(size_t)t * K + k]];
+  double gdg = 0.0;
+  for (int k = 0; k < K; k++) {
+    const double s = scores[(size_t)t * N + idx[(size_t)t * K + k]];
+    gdg += (S > 0.0 ? s / S : 1.0 / K) * (double)dg[(size_t)t * K + k];
+  }
+  for (int k = 0; k < K; k++) {
+    const double s = scores[(size_t)t * N + idx[(size_t)t * K + k]];
+    const double ds = S > 0.0 ? ((double)dg[(size_t)t * K + k] - gdg) / S : 0.0;
+    dz[(size_t)t * K + k] = (float)(ds * s * (1.0 - s));
+  }
+}
+
+// One workgroup per token: du_t = dout_t + sum_s dX_s,t + sum_k dX_{t,k} + sum_k dz_{t,k} e_{idx_k}
+template <bool E_BF16>
+__global__ __launch_bounds__(256) void du_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict__ dx,
+                                                 const int32_t* __restrict__ slot_row, const int32_t* __restrict__ idx,
+                                                 const float* __restrict__ dz, const void* __restrict__ E, int d, int K,
+                                                 int n_shared, long shared_base, long shared_stride,
+                                                 float* __restrict__ du) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    float acc[8], v[8];
+    load_bf16x8(dout + (size_t)t * d + c, acc);
+    for (int s = 0; s < n_shared; s++) {
+      load_bf16x8(dx + (shared_base + (long)s * shared_stride + t) * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[i] += v[i];
+    }
+    for (int k = 0; k < K; k++) {
+      load_bf16x8(dx + (size_t)slot_row[(size_t)t * K + k] * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[i] += v[i];
+    }
+    for (int k = 0; k < K; k++) {
+      const float z = dz[(size_t)t * K + k];
+      const size_t er = (size_t)idx[(size_t)t * K + k] * d + c;
+      if (E_BF16) {
+        load_bf16x8((const uint16_t*)E + er, v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = ((const float*)E)[er + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[i] = fmaf(z, v[i], acc[i]);
+    }
+    float* o = du + (size_t)t * d + c;
+    *(f32x4*)o = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4*)(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  }
+}
+
+// grid (N_r, ceil(d/2048)): dE_i = sum over expert i's rows (ascending token)
+// of dz_{t,k} u_t, fp32; k is where i sits in the token's selection.
+__global__ __launch_bounds__(256) void de_kernel(const uint16_t* __restrict__ u, const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ row_token, const int32_t* __restrict__ idx,
+                                                 const float* __restrict__ dz, int d, int K, float* __restrict__ dE) {
+  const int i = blockIdx.x;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (c >= d) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = offsets[i]; r < offsets[i + 1]; r++) {
+    const int t = row_token[r];
+    int k = 0;
+    while (k < K - 1 && idx[(size_t)t * K + k] != i) k++;
+    const float z = dz[(size_t)t * K + k];
+    float v[8];
+    load_bf16x8(u + (size_t)t * d + c, v);
+#pragma unroll
+    for (int j = 0; j < 8; j++) acc[j] = fmaf(z, v[j], acc[j]);
+  }
+  float* o = dE + (size_t)i * d + c;
+  *(f32x4*)o = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  *(f32x4*)(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+}
+
+// ---------------------------------------------------------------- weight gradients
+// C_e[m][n] = sum over segment e's rows r of P[r][m] * Q[q(r)][n]  (fp32 out)
+// P [R][M] bf16 (the permuted rows), Q rows bf16 (gathered through q_row when
+// not null). One workgroup (4 waves, 2x2) per 128x128 block of C; the rows go
+// through LDS in chunks of 16, transposed so each m (or n) holds its 16 r
+// values contiguously (16-byte MFMA operand reads); the next chunk is loaded
+// into registers while the current one is multiplied. Every block of C is one
+// workgroup's full sum: no atomics, a fixed order.
+constexpr int WG_T = 128;          // block edge
+constexpr int WG_R = 16;           // rows per chunk (one MFMA k-step)
+constexpr int WG_PITCH = 24;       // bf16 elements per LDS row (16 used + 8 pad: conflict-free reads)
+
+__global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a) {
+  __shared__ __align__(16) uint16_t sp[2][WG_T][WG_PITCH];
+  __shared__ __align__(16) uint16_t sq[2][WG_T][WG_PITCH];
+  const int seg = blockIdx.x, m0 = blockIdx.y * WG_T, n0 = blockIdx.z * WG_T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int rb = a.offsets[seg], re = a.offsets[seg + 1];
+  float* out = seg < a.n_first ? a.out0 + (size_t)seg * a.ostride0 : a.out1 + (size_t)(seg - a.n_first) * a.ostride1;
+
+  // loader: lane -> row r = lane & 15, 8 columns at 8 * (4*wave + lane/16)
+  const int lr = lane & 15, lc = 8 * (4 * wave + (lane >> 4));
+  i32x4 rp, rq;
+  auto gload = [&](int r0) __attribute__((always_inline)) {
+    const int r = r0 + lr;
+    if (r < re) {
+      rp = *(const i32x4*)(a.P + (size_t)r * a.M + m0 + lc);
+      const long qr = a.q_row ? a.q_row[r] : r;
+      rq = *(const i32x4*)(a.Q + (size_t)qr * a.Nn + n0 + lc);
+    } else {
+      rp = i32x4{0, 0, 0, 0};
+      rq = i32x4{0, 0, 0, 0};
+    }
+  };
+  auto sstore = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint32_t p = (uint32_t)rp[j], q = (uint32_t)rq[j];
+      sp[buf][lc + 2 * j][lr] = (uint16_t)(p & 0xFFFF);
+      sp[buf][lc + 2 * j + 1][lr] = (uint16_t)(p >> 16);
+      sq[buf][lc + 2 * j][lr] = (uint16_t)(q & 0xFFFF);
+      sq[buf][lc + 2 * j + 1][lr] = (uint16_t)(q >> 16);
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int nchunk = (re - rb + WG_R - 1) / WG_R;
+  if (nchunk > 0) {
+    gload(rb);
+    sstore(0);
+    __syncthreads();
+    for (int c = 0; c < nchunk; c++) {
+      const int buf = c & 1;
+      if (c + 1 < nchunk) gload(rb + (c + 1) * WG_R);
+      bf16x8 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; i++) af[i] = *(const bf16x8*)&sp[buf][wm * 64 + i * 32 + l32][kh * 8];
+#pragma unroll
+      for (int j = 0; j < 2; j++) bf[j] = *(const bf16x8*)&sq[buf][wn * 64 + j * 32 + l32][kh * 8];
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      if (c + 1 < nchunk) sstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  // D element (8*(r>>2) + 4*(lane>>5) + (r&3), lane&31)
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+        const int n = n0 + wn * 64 + j * 32 + l32;
+        out[(size_t)m * a.Nn + n] = acc[i][j][r];
+      }
+}
+
+// ---------------------------------------------------------------- transposes
+// dst[b][c][r] = src[b][r][c] for bf16 [batch][rows][cols], 64x64 tiles via LDS
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                             int rows, int cols) {
+  __shared__ uint16_t tile[64][65];
+  const size_t base = (size_t)blockIdx.z * rows * cols;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i >> 6, c = i & 63;
+    if (r0 + r < rows && c0 + c < cols) tile[r][c] = src[base + (size_t)(r0 + r) * cols + c0 + c];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int c = i >> 6, r = i & 63;
+    if (r0 + r < rows && c0 + c < cols) dst[base + (size_t)(c0 + c) * rows + r0 + r] = tile[r][c];
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+static dim3 grid_1d(long n, int per_block) {
+  return dim3((unsigned)std::min<long>(cdiv<long>(n, per_block), 8192));
+}
+
+hipError_t launch_swiglu_fwd(const void* ab, void* h, long rows, int I, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  swiglu_fwd_kernel<<<grid_1d(rows * (I / 8), 256), 256, 0, s>>>((const uint16_t*)ab, (uint16_t*)h, rows, I);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const void* dh, const void* ab, void* dab, long rows, int I, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  swiglu_bwd_kernel<<<grid_1d(rows * (I / 8), 256), 256, 0, s>>>((const uint16_t*)dh, (const uint16_t*)ab,
+                                                                  (uint16_t*)dab, rows, I);
+  return hipGetLastError();
+}
+
+hipError_t launch_dgate_dy(const void* dout, const void* y, const int32_t* slot_row, const float* gate, int T, int d,
+                           int K, int n_shared, long shared_base, long shared_stride, float* dg, void* dy,
+                           hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  dgate_dy_kernel<<<T, 256, 0, s>>>((const uint16_t*)dout, (const uint16_t*)y, slot_row, gate, d, K, n_shared,
+                                    shared_base, shared_stride, dg, (uint16_t*)dy);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const float* scores, const int32_t* idx, const float* dg, const void* dout,
+                             const void* dx, const int32_t* slot_row, const void* E, int e_dtype, const void* u,
+                             const int32_t* offsets, const int32_t* row_token, int T, int N, int d, int K,
+                             int n_shared, long shared_base, long shared_stride, float* dz, float* du, float* dE,
+                             hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  dz_kernel<<<cdiv(T, 256), 256, 0, s>>>(scores, idx, dg, T, N, K, dz);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (e_dtype == MOE_BF16)
+    du_kernel<true><<<T, 256, 0, s>>>((const uint16_t*)dout, (const uint16_t*)dx, slot_row, idx, dz, E, d, K,
+                                      n_shared, shared_base, shared_stride, du);
+  else
+    du_kernel<false><<<T, 256, 0, s>>>((const uint16_t*)dout, (const uint16_t*)dx, slot_row, idx, dz, E, d, K,
+                                       n_shared, shared_base, shared_stride, du);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  de_kernel<<<dim3(N, cdiv(d, 2048)), 256, 0, s>>>((const uint16_t*)u, offsets, row_token, idx, dz, d, K, dE);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
+  if (a.n_seg <= 0) return hipSuccess;
+  wgrad_kernel<<<dim3(a.n_seg, a.M / WG_T, a.Nn / WG_T), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const void* src, void* dst, int batch, int rows, int cols, hipStream_t s) {
+  if (batch <= 0 || rows <= 0 || cols <= 0) return hipSuccess;
+  transpose_bf16_kernel<<<dim3(cdiv(cols, 64), cdiv(rows, 64), batch), 256, 0, s>>>(
+      (const uint16_t*)src, (uint16_t*)dst, rows, cols);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -518,3 +518,152 @@ extern "C" int moe_quantize_fp8(int32_t kind, const void* src, int32_t src_dtype
   if (kind == MOE_QUANT_ACT_1x128) return hip_status(launch_quant_act(src, src_dtype, rows, cols, nullptr, q, scale, s));
   return hip_status(launch_quant_w(src, src_dtype, rows, cols, q, scale, s));
 }
+
+// ---------------------------------------------------------------- backward
+// Supported: bf16 u and experts, I (and I_s) a multiple of 128, shared
+// experts of the routed experts' size (or none), T > 0 handled, T == 0 no-op.
+static int backward_shape_ok(const moe_desc_t* d) {
+  if (d->in_dtype != MOE_BF16 || d->expert_dtype != MOE_BF16) return MOE_ENOTSUP;
+  if (d->inter % 128) return MOE_ENOTSUP;
+  if (d->n_shared && d->inter_shared != d->inter) return MOE_ENOTSUP;
+  return MOE_OK;
+}
+
+struct BwdWs {
+  size_t idx, gate, counts, scores, bitmap, wprefix, offsets, mtile, row_token, slot_row;
+  size_t ab, h, y, dy, dh, dab, dg, dz, total;
+};
+
+static BwdWs bwd_layout(const moe_desc_t* d) {
+  BwdWs w;
+  const size_t T = d->T, K = d->top_k, N = d->n_routed, Ns = d->n_shared, I = d->inter, D = d->d;
+  const size_t W = (T + 63) / 64, n_seg = N + Ns, R = T * K + Ns * T;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += al256(bytes); return at; };
+  w.idx = take(T * K * 4);
+  w.gate = take(T * K * 4);
+  w.counts = take(N * 4);
+  w.scores = take(T * N * 4);
+  w.bitmap = take(W * N * 8);
+  w.wprefix = take(W * N * 4);
+  w.offsets = take((n_seg + 1) * 4);
+  w.mtile = take((n_seg + 1) * 4);
+  w.row_token = take(R * 4);
+  w.slot_row = take(T * K * 4);
+  w.ab = take(R * 2 * I * 2);
+  w.h = take(R * I * 2);
+  w.y = take(R * D * 2);          // Y, then dX
+  w.dy = take(R * D * 2);
+  w.dh = take(R * I * 2);
+  w.dab = take(R * 2 * I * 2);
+  w.dg = take(T * K * 4);
+  w.dz = take(T * K * 4);
+  w.total = o;
+  return w;
+}
+
+extern "C" size_t moe_backward_workspace_bytes(const moe_desc_t* d) {
+  if (moe_validate(d) != MOE_OK || backward_shape_ok(d) != MOE_OK) return 0;
+  return bwd_layout(d).total;
+}
+
+extern "C" int moe_transpose_expert_weights(const moe_desc_t* d, const moe_weights_t* w, moe_weights_t* wt,
+                                            moe_stream_t stream) {
+  int st = moe_validate(d);
+  if (st) return st;
+  if ((st = backward_shape_ok(d))) return st;
+  if (!w || !wt || !aligned(w->w13) || !aligned(w->w2) || !aligned(wt->w13) || !aligned(wt->w2)) return MOE_EINVAL;
+  if (d->n_shared && (!aligned(w->w13_shared) || !aligned(w->w2_shared) || !aligned(wt->w13_shared) ||
+                      !aligned(wt->w2_shared)))
+    return MOE_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  const int I = d->inter, D = d->d;
+  MOE_TRY(launch_transpose_bf16(w->w13, (void*)wt->w13, d->n_routed, 2 * I, D, s));
+  MOE_TRY(launch_transpose_bf16(w->w2, (void*)wt->w2, d->n_routed, D, I, s));
+  if (d->n_shared) {
+    MOE_TRY(launch_transpose_bf16(w->w13_shared, (void*)wt->w13_shared, d->n_shared, 2 * I, D, s));
+    MOE_TRY(launch_transpose_bf16(w->w2_shared, (void*)wt->w2_shared, d->n_shared, D, I, s));
+  }
+  return MOE_OK;
+}
+
+extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const moe_weights_t* wt, const void* u,
+                            const float* b, const void* dout, moe_grads_t* g, void* ws, size_t ws_bytes,
+                            moe_stream_t stream) {
+  int st = moe_validate(d);
+  if (st) return st;
+  if ((st = backward_shape_ok(d))) return st;
+  if (!w || !wt || !g) return MOE_EINVAL;
+  if (!aligned(u) || !aligned(b) || !aligned(dout) || !aligned(ws) || !aligned(w->centroids)) return MOE_EINVAL;
+  if (!aligned(w->w13) || !aligned(w->w2) || !aligned(wt->w13) || !aligned(wt->w2)) return MOE_EINVAL;
+  if (!aligned(g->du) || !aligned(g->dE) || !aligned(g->dw13) || !aligned(g->dw2)) return MOE_EINVAL;
+  if (d->n_shared && (!aligned(w->w13_shared) || !aligned(w->w2_shared) || !aligned(wt->w13_shared) ||
+                      !aligned(wt->w2_shared) || !aligned(g->dw13_shared) || !aligned(g->dw2_shared)))
+    return MOE_EINVAL;
+  const BwdWs L = bwd_layout(d);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (d->T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* base = (uint8_t*)ws;
+  const int T = d->T, K = d->top_k, N = d->n_routed, Ns = d->n_shared, I = d->inter, D = d->d;
+  const long TK = (long)T * K, R = TK + (long)Ns * T;
+  const int n_seg = N + Ns;
+  int32_t* idx = (int32_t*)(base + L.idx);
+  float* gate = (float*)(base + L.gate);
+  int32_t* counts = (int32_t*)(base + L.counts);
+  float* scores = (float*)(base + L.scores);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* mtile = (int32_t*)(base + L.mtile);
+  int32_t* row_token = (int32_t*)(base + L.row_token);
+  int32_t* slot_row = (int32_t*)(base + L.slot_row);
+  void* AB = base + L.ab;
+  void* H = base + L.h;
+  void* Y = base + L.y;
+  void* dY = base + L.dy;
+  void* dH = base + L.dh;
+  void* dAB = base + L.dab;
+  float* dg = (float*)(base + L.dg);
+  float* dz = (float*)(base + L.dz);
+
+  // forward recompute: the same routing and dispatch as moe_forward (the fused
+  // router gives bit-identical affinities and selections), then A|B, H, Y
+  RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, scores, idx, gate, counts);
+  MOE_TRY(launch_route(ra, route_front(d), s));
+  const int bm = gemm_bm(d->expert_dtype, (int)(TK / N), d->d);
+  PermuteArgs p;
+  p.idx = idx; p.T = T; p.K = K; p.n_routed = N;
+  p.bitmap = (uint64_t*)(base + L.bitmap); p.wprefix = (int32_t*)(base + L.wprefix);
+  p.counts_ws = nullptr; p.offsets = offsets; p.row_token = row_token; p.slot_row = slot_row;
+  p.counts_out = nullptr; p.n_extra_seg = Ns; p.mtile_prefix = mtile; p.bm = bm;
+  MOE_TRY(launch_permute(p, s));
+  auto grouped = [&](const void* x, long x_rows, const int32_t* ridx, const void* w0, const void* w1, long wstride,
+                     void* out, int Nout, int Kred) -> hipError_t {
+    GemmArgs ga = gemm_args(x, x_rows, nullptr, ridx, offsets, mtile, n_seg, w0, nullptr, wstride, 0, out, Nout,
+                            Kred, (int)R);
+    ga.w1 = Ns ? w1 : w0;
+    ga.n_first = N;
+    return launch_gemm_down(ga, MOE_BF16, bm, s);
+  };
+  const long s13 = 2L * I * D, s2 = (long)D * I;
+  MOE_TRY(grouped(u, T, row_token, w->w13, w->w13_shared, s13, AB, 2 * I, D));      // [A|B] = X W13^T
+  MOE_TRY(launch_swiglu_fwd(AB, H, R, I, s));                                         // H = SiLU(A) B
+  MOE_TRY(grouped(H, R, nullptr, w->w2, w->w2_shared, s2, Y, D, I));                // Y = H W2^T
+
+  // backward
+  MOE_TRY(launch_dgate_dy(dout, Y, slot_row, gate, T, D, K, Ns, TK, T, dg, dY, s));   // dg, dY
+  MOE_TRY(grouped(dY, R, nullptr, wt->w2, wt->w2_shared, s2, dH, I, D));             // dH = dY W2
+  MOE_TRY(launch_swiglu_bwd(dH, AB, dAB, R, I, s));                                   // dA | dB
+  void* dX = Y;                                                                       // Y is no longer needed
+  MOE_TRY(grouped(dAB, R, nullptr, wt->w13, wt->w13_shared, s13, dX, D, 2 * I));     // dX = [dA dB] W13
+  MOE_TRY(launch_router_bwd(scores, idx, dg, dout, dX, slot_row, w->centroids, d->router_dtype, u, offsets,
+                            row_token, T, N, D, K, Ns, TK, T, dz, g->du, g->dE, s));  // dz, du, dE
+  WgradArgs wa;
+  wa.offsets = offsets; wa.n_seg = n_seg; wa.n_first = N;
+  wa.P = (const uint16_t*)dY; wa.Q = (const uint16_t*)H; wa.q_row = nullptr; wa.M = D; wa.Nn = I;
+  wa.out0 = g->dw2; wa.ostride0 = s2; wa.out1 = Ns ? g->dw2_shared : g->dw2; wa.ostride1 = s2;
+  MOE_TRY(launch_wgrad(wa, s));                                                       // dW2 = dY^T H
+  wa.P = (const uint16_t*)dAB; wa.Q = (const uint16_t*)u; wa.q_row = row_token; wa.M = 2 * I; wa.Nn = D;
+  wa.out0 = g->dw13; wa.ostride0 = s13; wa.out1 = Ns ? g->dw13_shared : g->dw13; wa.ostride1 = s13;
+  MOE_TRY(launch_wgrad(wa, s));                                                       // dW13 = [dA dB]^T X
+  return MOE_OK;
+}

@@ -75,6 +75,29 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_update_bias(const int32_t* counts, float* b, int n_routed, long total,
                               float gamma, hipStream_t s);
 
+// ---------------------------------------------------------------- backward
+struct WgradArgs {
+  const uint16_t* P;          // [R, M] bf16 permuted rows
+  const uint16_t* Q;          // rows [*, Nn] bf16
+  const int32_t* q_row;       // nullable: Q row of permuted row r
+  const int32_t* offsets;     // [n_seg+1]
+  int n_seg, M, Nn;           // M, Nn multiples of 128
+  float* out0; float* out1; long ostride0, ostride1;   // [M, Nn] per segment
+  int n_first;                // segments below: out0, others: out1
+};
+hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
+hipError_t launch_swiglu_fwd(const void* ab, void* h, long rows, int I, hipStream_t s);
+hipError_t launch_swiglu_bwd(const void* dh, const void* ab, void* dab, long rows, int I, hipStream_t s);
+hipError_t launch_dgate_dy(const void* dout, const void* y, const int32_t* slot_row, const float* gate, int T, int d,
+                           int K, int n_shared, long shared_base, long shared_stride, float* dg, void* dy,
+                           hipStream_t s);
+hipError_t launch_router_bwd(const float* scores, const int32_t* idx, const float* dg, const void* dout,
+                             const void* dx, const int32_t* slot_row, const void* E, int e_dtype, const void* u,
+                             const int32_t* offsets, const int32_t* row_token, int T, int N, int d, int K,
+                             int n_shared, long shared_base, long shared_stride, float* dz, float* du, float* dE,
+                             hipStream_t s);
+hipError_t launch_transpose_bf16(const void* src, void* dst, int batch, int rows, int cols, hipStream_t s);
+
 // sequence-wise balance loss (forward value)
 size_t seq_balance_ws_bytes(int T, int N, int seq_len);
 hipError_t launch_seq_balance(const float* s, const int32_t* idx, int T, int N, int K, int seq_len, float alpha,

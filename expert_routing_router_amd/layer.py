@@ -97,3 +97,36 @@ class MoELayer:
         L.moe_forward(self.desc, self.weights, u, b, self.out, self.ws, update_bias,
                       self.idx, self.gate, self.counts, stream=stream)
         return self.out
+
+    def backward(self, u: torch.Tensor, b: torch.Tensor, dout: torch.Tensor, stream=None):
+        """Gradients of forward(u, b) for the upstream gradient dout [T, d] (bf16), for the routing
+        the forward chooses with this b: a dict of fp32 device tensors du [T, d], dE [N_r, d],
+        dw13 [N_r, 2I, d], dw2 [N_r, d, I] (and dw13s, dw2s for the shared experts). The
+        transposed weight copies and the gradient buffers are allocated on the first call."""
+        cfg, dev = self.cfg, self.device
+        if getattr(self, "_wt", None) is None:
+            I, d, N, ns = cfg.inter, cfg.d, cfg.n_routed, max(cfg.n_shared, 1)
+            bf = torch.bfloat16
+            self._w13t = torch.empty((N, d, 2 * I), dtype=bf, device=dev)
+            self._w2t = torch.empty((N, I, d), dtype=bf, device=dev)
+            self._w13st = torch.empty((ns, d, 2 * I), dtype=bf, device=dev)
+            self._w2st = torch.empty((ns, I, d), dtype=bf, device=dev)
+            sh = cfg.n_shared > 0
+            self._wt = L.make_weights(None, self._w13t, self._w2t, self._w13st if sh else None,
+                                      self._w2st if sh else None)
+            L.moe_transpose_expert_weights(self.desc, self.weights, self._wt, stream=stream)
+            f32 = torch.float32
+            self.grads = {
+                "du": torch.empty((cfg.T, d), dtype=f32, device=dev),
+                "dE": torch.empty((N, d), dtype=f32, device=dev),
+                "dw13": torch.empty((N, 2 * I, d), dtype=f32, device=dev),
+                "dw2": torch.empty((N, d, I), dtype=f32, device=dev),
+                "dw13s": torch.empty((ns, 2 * I, d), dtype=f32, device=dev),
+                "dw2s": torch.empty((ns, d, I), dtype=f32, device=dev),
+            }
+            g = self.grads
+            self._grads = L.make_grads(g["du"], g["dE"], g["dw13"], g["dw2"], g["dw13s"] if sh else None,
+                                       g["dw2s"] if sh else None)
+            self._bws = torch.empty(L.moe_backward_workspace_bytes(self.desc), dtype=torch.uint8, device=dev)
+        L.moe_backward(self.desc, self.weights, self._wt, u, b, dout, self._grads, self._bws, stream=stream)
+        return self.grads

@@ -175,6 +175,41 @@ int moe_combine(const moe_desc_t* desc, const void* u, const void* y, const void
 int moe_update_bias(const moe_desc_t* desc, const int32_t* counts, float* b,
                     moe_stream_t stream);
 
+/* Gradients of the layer (moe_backward). fp32, caller-owned, row-major:
+ *   du [T, d]; dE [N_r, d]; dw13 [N_r, 2I, d]; dw2 [N_r, d, I];
+ *   dw13_shared [N_s, 2I, d], dw2_shared [N_s, d, I] (unused when N_s = 0). */
+typedef struct moe_grads {
+  float* du;
+  float* dE;
+  float* dw13;
+  float* dw2;
+  float* dw13_shared;
+  float* dw2_shared;
+} moe_grads_t;
+
+/* Transposed expert weights for moe_backward (bf16 layers): fills
+ * wt->w13 [N_r, d, 2I] and wt->w2 [N_r, I, d] (and the shared ones) from the
+ * weights in w. Other members of wt are ignored. */
+int moe_transpose_expert_weights(const moe_desc_t* desc, const moe_weights_t* w, moe_weights_t* wt,
+                                 moe_stream_t stream);
+
+/* Backward of moe_forward for the routing it chooses (same u, b, weights):
+ * given dout = dL/dout [T, d] (bf16), writes dL/du, dL/dE and the expert
+ * weight gradients. The selection and the bias are piecewise constant (b only
+ * routes: pwwt.cn note 1.1.2-1.1.3), so gradients flow through the gates'
+ * dependence on the affinities, g = s_sel / sum(s_sel), and the SwiGLU
+ * experts (output equation of the xyznot.com guides, section 2):
+ *   dg = <dout, Y>, dY = g dout, dH = dY W2, dA|dB from SwiGLU, dX = [dA dB] W13,
+ *   ds = (dg - sum g dg) / sum s, dz = ds s (1 - s), dE = dz^T u.
+ * The forward is recomputed inside (bf16 intermediates, fp32 accumulation).
+ * Supported: bf16 u and experts, I % 128 == 0, N_s == 0 or I_s == I;
+ * MOE_ENOTSUP otherwise. wt: moe_transpose_expert_weights of w.
+ * ws: moe_backward_workspace_bytes(desc) bytes (0 when unsupported). */
+size_t moe_backward_workspace_bytes(const moe_desc_t* desc);
+int moe_backward(const moe_desc_t* desc, const moe_weights_t* w, const moe_weights_t* wt, const void* u,
+                 const float* b, const void* dout, moe_grads_t* grads, void* ws, size_t ws_bytes,
+                 moe_stream_t stream);
+
 /* Complementary sequence-wise balance loss, forward value (pwwt.cn note
  * section 1.2; alpha = 0.0001 on the xyznot.com guides, section 2). The T
  * tokens are T/seq_len consecutive sequences; for sequence q

@@ -1,0 +1,108 @@
+"""Backward pass (moe_backward) on the GPU against oracle.backward (fp64 autograd
+of the layer for the routing the forward chooses).
+
+The GPU keeps bf16 intermediates (A|B, H, Y, dY, dH, dA|dB, dX) with fp32
+accumulation, like the forward; each is one bf16 rounding (relative 2^-9) of
+a quantity that then enters sums of hundreds of terms, so the bar is the
+forward's bf16 bar: relative L2 error <= 1e-2 for du, the expert weight
+gradients and dE. Routing is first checked to be the oracle's (same sets).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from expert_routing_router_amd.layer import MoELayer
+from oracle import backward, numerics as nx, routing
+from tests.gpu_util import dev, host, log, rel_l2
+from workloads import gen, get_config
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(name):
+    if name == "small":
+        return get_config("v3").with_(T=1024, d=512, n_routed=32, top_k=4, n_groups=4, topk_groups=2,
+                                      group_topk=2, n_shared=1, inter=256, inter_shared=256)
+    if name == "ragged":
+        return get_config("mid").with_(T=777, d=256, n_routed=64, top_k=6, n_shared=2, inter=384,
+                                       inter_shared=384)
+    return get_config(name)
+
+
+def _dout(cfg, seed=11):
+    rng = np.random.default_rng(seed)
+    return gen.f32_to_bf16_bits(rng.standard_normal((cfg.T, cfg.d)).astype(np.float32))
+
+
+def _run(cfg, step=0):
+    layer = MoELayer(cfg, gen)
+    u = gen.tokens(cfg, step)
+    b = gen.bias_init(cfg) + np.float32(0.003) * ((np.arange(cfg.n_routed) % 5) - 2).astype(np.float32)
+    dout = _dout(cfg)
+    b_dev = dev(b, "f32")
+    layer.forward(dev(u, cfg.in_dtype), b_dev, update_bias=False)
+    g = layer.backward(dev(u, cfg.in_dtype), b_dev, dev(dout, "bf16"))
+    torch.cuda.synchronize()
+    return layer, u, b, dout, g
+
+
+def _oracle_inputs(cfg, u, b):
+    u64 = nx.to_f64(u, cfg.in_dtype)
+    E64 = nx.to_f64(gen.centroids(cfg), cfg.router_dtype)
+    r, _, _ = routing.route_tokens(u64, E64, b, cfg)
+    return u64, E64, r
+
+
+def _weights(cfg, experts):
+    w13 = {e: nx.to_f64(gen.expert_w13(cfg, e), "bf16") for e in experts}
+    w2 = {e: nx.to_f64(gen.expert_w2(cfg, e), "bf16") for e in experts}
+    w13s = [nx.to_f64(gen.shared_w13(cfg, s), "bf16") for s in range(cfg.n_shared)]
+    w2s = [nx.to_f64(gen.shared_w2(cfg, s), "bf16") for s in range(cfg.n_shared)]
+    return w13, w2, w13s, w2s
+
+
+@pytest.mark.parametrize("name", ["small", "ragged"])
+def test_backward_full(name):
+    cfg = _cfg(name)
+    layer, u, b, dout, g = _run(cfg)
+    u64, E64, r = _oracle_inputs(cfg, u, b)
+    idx_gpu = host(layer.idx)
+    assert np.array_equal(np.sort(idx_gpu, 1), np.sort(r.idx, 1)), "routing differs from the oracle's"
+    w13, w2, w13s, w2s = _weights(cfg, range(cfg.n_routed))
+    ref = backward.layer_grads(u64, E64, r.idx, nx.bf16_to_f64(dout), w13, w2, w13s, w2s)
+    used = sorted(ref["dw13"])
+    errs = {
+        "du": rel_l2(host(g["du"]), ref["du"]),
+        "dE": rel_l2(host(g["dE"]), ref["dE"]),
+        "dw13": rel_l2(host(g["dw13"])[used], np.stack([ref["dw13"][e] for e in used])),
+        "dw2": rel_l2(host(g["dw2"])[used], np.stack([ref["dw2"][e] for e in used])),
+    }
+    if cfg.n_shared:
+        errs["dw13s"] = rel_l2(host(g["dw13s"])[:cfg.n_shared], np.stack(ref["dw13s"]))
+        errs["dw2s"] = rel_l2(host(g["dw2s"])[:cfg.n_shared], np.stack(ref["dw2s"]))
+    log(name, " ".join("%s %.2e" % kv for kv in errs.items()))
+    for k, v in errs.items():
+        assert v <= 1e-2, (k, v)
+    # an expert no token chose gets an exactly zero gradient
+    unused = sorted(set(range(cfg.n_routed)) - set(used))
+    for e in unused:
+        assert not host(g["dw2"][e]).any() and not host(g["dw13"][e]).any()
+
+
+def test_backward_v3_sampled_tokens():
+    """V3 shape: du of sampled tokens (a token's du depends on its own path only)."""
+    cfg = get_config("v3")
+    layer, u, b, dout, g = _run(cfg)
+    u64, E64, r = _oracle_inputs(cfg, u, b)
+    idx_gpu = host(layer.idx)
+    same = (np.sort(idx_gpu, 1) == np.sort(r.idx, 1)).all(axis=1)
+    tokens = [t for t in np.random.default_rng(3).choice(cfg.T, 8, replace=False) if same[t]][:3]
+    experts = sorted(set(r.idx[tokens].reshape(-1).tolist()))
+    w13, w2, w13s, w2s = _weights(cfg, experts)
+    ref = backward.layer_grads(u64[tokens], E64, r.idx[tokens], nx.bf16_to_f64(dout[tokens]), w13, w2, w13s, w2s,
+                              experts=[])
+    err = rel_l2(host(g["du"])[tokens], ref["du"])
+    log("v3 sampled du over %d tokens: rel-L2 %.2e" % (len(tokens), err))
+    assert err <= 1e-2
+    assert np.isfinite(host(g["dw13"][:4])).all() and np.isfinite(host(g["dE"])).all()
