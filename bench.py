@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--T", type=int, default=0, help="override tokens per batch")
     ap.add_argument("--cpu-sample-experts", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", type=int, default=5,
+                    help="also time this many moe_backward calls (bf16 layers; reported beside the step; 0: skip)")
     ap.add_argument("--load-trajectory", type=int, default=0,
                     help="after the timed steps, run this many forward+update steps from the initial "
                          "bias and report the max/mean expert load of each (every 10th listed)")
@@ -265,6 +267,35 @@ def main():
                        "loss_over_alpha": [round(float(x) / 1e-4, 6) for x in bl.cpu()]}
         log("seq balance loss: %.4f ms for %d sequences" % (sb_ms, cfg.T // seq_len))
 
+    bwd = None
+    if args.backward and cfg.expert_dtype == "bf16" and cfg.in_dtype == "bf16":
+        rng = torch.Generator(device="cuda:0").manual_seed(5)
+        dout = torch.randn((cfg.T, cfg.d), generator=rng, device="cuda:0").to(torch.bfloat16)
+        t0 = time.time()
+        layer.backward(us[0], b, dout)           # first call: transposed weights, buffers
+        torch.cuda.synchronize()
+        log("backward set-up + first call %.1fs" % (time.time() - t0))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.backward):
+            layer.backward(us[i % nb], b, dout)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = e0.elapsed_time(e1) / args.backward
+        R = cfg.T * cfg.top_k + cfg.n_shared * cfg.T
+        w13 = (cfg.n_routed + cfg.n_shared) * 2 * cfg.inter * cfg.d
+        w2 = (cfg.n_routed + cfg.n_shared) * cfg.inter * cfg.d
+        # forward recompute (A|B, Y) + dH + dX + dW2 + dW13: six products of the experts' shape
+        flops = 3.0 * 2.0 * R * cfg.d * 3 * cfg.inter
+        # weights read twice (W, W^T), fp32 weight gradients written once, u / dout / du
+        byts = 2 * 2 * (w13 + w2) + 4 * (w13 + w2) + cfg.T * cfg.d * (2 + 2 + 4)
+        bwd = {"ms": round(bwd_ms, 3), "tokens_per_s": round(cfg.T / bwd_ms * 1e3, 1),
+               "TFLOP/s": round(flops / bwd_ms / 1e9, 1), "mfma_frac": round(flops / bwd_ms / 1e9 / 2500.0, 4),
+               "GB/s": round(byts / bwd_ms / 1e6, 1), "hbm_frac": round(byts / bwd_ms / 1e6 / PEAK_HBM_GBS, 4),
+               "algorithmic_flops": flops, "algorithmic_bytes": byts, "calls": args.backward}
+        log("backward: %.3f ms/call (%.0f TFLOP/s, %.0f GB/s algorithmic)" % (bwd_ms, flops / bwd_ms / 1e9,
+                                                                           byts / bwd_ms / 1e6))
+
     alg = algorithmic(cfg)
     peak_tf = PEAK_TFLOPS[cfg.expert_dtype]
     kernels = {}
@@ -320,6 +351,7 @@ def main():
         "grouped_gemm_mfma_frac": kernels["grouped_gemm"]["mfma_frac"],
         "max_over_mean_load": [round(x, 3) for x in loads],
         "load_trajectory": trajectory,
+        "backward": bwd,
         "event_ms_per_step": round(ev_ms / args.steps, 4),
     }
     print(json.dumps(rec), flush=True)

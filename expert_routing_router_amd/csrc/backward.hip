@@ -197,47 +197,78 @@ __global__ __launch_bounds__(256) void de_kernel(const uint16_t* __restrict__ u,
 // ---------------------------------------------------------------- weight gradients
 // C_e[m][n] = sum over segment e's rows r of P[r][m] * Q[q(r)][n]  (fp32 out)
 // P [R][M] bf16 (the permuted rows), Q rows bf16 (gathered through q_row when
-// not null). One workgroup (4 waves, 2x2) per 128x128 block of C; the rows go
-// through LDS in chunks of 16, transposed so each m (or n) holds its 16 r
-// values contiguously (16-byte MFMA operand reads); the next chunk is loaded
-// into registers while the current one is multiplied. Every block of C is one
+// not null). One workgroup (4 waves, 2x2 of 64x64) per 128x128 block of C;
+// the segment's rows go through LDS in chunks of 64. The MFMA operands need 8
+// consecutive rows per lane, the rows in memory hold consecutive columns, so
+// each thread loads an 8x8 (rows x columns) micro-tile of P or Q, transposes
+// it in registers and writes 8 columns x 16 bytes to LDS. The next chunk is
+// loaded while the current one is multiplied. Every block of C is one
 // workgroup's full sum: no atomics, a fixed order.
 constexpr int WG_T = 128;          // block edge
-constexpr int WG_R = 16;           // rows per chunk (one MFMA k-step)
-constexpr int WG_PITCH = 24;       // bf16 elements per LDS row (16 used + 8 pad: conflict-free reads)
+constexpr int WG_R = 64;           // rows per chunk (four MFMA k-steps)
+constexpr int WG_PITCH = 72;       // bf16 per LDS row (64 used + 8 pad: conflict-free operand reads)
+
+// columns j of 8 rows (one i32x4 of 8 bf16 per row) -> 8 bf16 of column j, rows in order
+__device__ __forceinline__ i32x4 column_of(const i32x4* v, int j) {
+  i32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const uint32_t x = (uint32_t)v[2 * q][j >> 1], y = (uint32_t)v[2 * q + 1][j >> 1];
+    o[q] = (int)((j & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16)));
+  }
+  return o;
+}
 
 __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a) {
-  __shared__ __align__(16) uint16_t sp[2][WG_T][WG_PITCH];
-  __shared__ __align__(16) uint16_t sq[2][WG_T][WG_PITCH];
-  const int seg = blockIdx.x, m0 = blockIdx.y * WG_T, n0 = blockIdx.z * WG_T;
+  __shared__ __align__(16) uint16_t lds[2][2][WG_T][WG_PITCH];     // [operand][buffer][column][row]
+  // Blocks go in super-tiles of 8x8 blocks of one segment; super-tile k runs on
+  // XCD k % 8 (workgroup i runs on XCD i % 8) as 64 consecutive workgroups
+  // there, which then share 8 column slices of P and 8 of Q in that XCD's L2.
+  // Dealing super-tiles round-robin keeps segments of very different row
+  // counts spread over all XCDs.
+  const int nb = a.Nn / WG_T, mb = a.M / WG_T;
+  const int snb = (nb + 7) / 8, smb = (mb + 7) / 8;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int st = xcd + 8 * (j >> 6), w = j & 63;
+  const int seg = st / (smb * snb);
+  if (seg >= a.n_seg) return;
+  const int srem = st - seg * smb * snb;
+  const int mblk = (srem / snb) * 8 + (w >> 3), nblk = (srem % snb) * 8 + (w & 7);
+  if (mblk >= mb || nblk >= nb) return;
+  const int m0 = mblk * WG_T, n0 = nblk * WG_T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int rb = a.offsets[seg], re = a.offsets[seg + 1];
   float* out = seg < a.n_first ? a.out0 + (size_t)seg * a.ostride0 : a.out1 + (size_t)(seg - a.n_first) * a.ostride1;
+  const int nchunk = (re - rb + WG_R - 1) / WG_R;
 
-  // loader: lane -> row r = lane & 15, 8 columns at 8 * (4*wave + lane/16)
-  const int lr = lane & 15, lc = 8 * (4 * wave + (lane >> 4));
-  i32x4 rp, rq;
-  auto gload = [&](int r0) __attribute__((always_inline)) {
-    const int r = r0 + lr;
-    if (r < re) {
-      rp = *(const i32x4*)(a.P + (size_t)r * a.M + m0 + lc);
-      const long qr = a.q_row ? a.q_row[r] : r;
-      rq = *(const i32x4*)(a.Q + (size_t)qr * a.Nn + n0 + lc);
-    } else {
-      rp = i32x4{0, 0, 0, 0};
-      rq = i32x4{0, 0, 0, 0};
+  // loader: threads 0..127 take P, 128..255 Q; micro-tile (8 rows at 8*rt, 8 columns at 8*ct)
+  const int op = tid >> 7, ct = tid & 15, rt = (tid >> 4) & 7;
+  const int ncols = op ? a.Nn : a.M;
+  const int c0 = (op ? n0 : m0) + 8 * ct;
+  const __amdgpu_buffer_rsrc_t src = op ? make_rsrc(a.Q, (long)a.q_rows * a.Nn * 2)
+                                        : make_rsrc(a.P, (long)re * a.M * 2);
+  i32x4 v[8];
+  // source rows of a chunk, fetched one chunk ahead of their use (the Q rows
+  // may be gathered through q_row)
+  int srow[8];
+  auto rows_of = [&](int r0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int r = r0 + 8 * rt + i;
+      srow[i] = r < re ? (op && a.q_row ? a.q_row[r] : r) : -1;
+    }
+  };
+  auto gload = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int off = srow[i] >= 0 ? (int)(((long)srow[i] * ncols + c0) * 2) : kOutOfRange;
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(src, off, 0, 0);
     }
   };
   auto sstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const uint32_t p = (uint32_t)rp[j], q = (uint32_t)rq[j];
-      sp[buf][lc + 2 * j][lr] = (uint16_t)(p & 0xFFFF);
-      sp[buf][lc + 2 * j + 1][lr] = (uint16_t)(p >> 16);
-      sq[buf][lc + 2 * j][lr] = (uint16_t)(q & 0xFFFF);
-      sq[buf][lc + 2 * j + 1][lr] = (uint16_t)(q >> 16);
-    }
+    for (int j = 0; j < 8; j++) *(i32x4*)&lds[op][buf][8 * ct + j][8 * rt] = column_of(v, j);
   };
 
   f32x16 acc[2][2];
@@ -248,24 +279,31 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
   const int l32 = lane & 31, kh = lane >> 5;
-  const int nchunk = (re - rb + WG_R - 1) / WG_R;
   if (nchunk > 0) {
-    gload(rb);
+    rows_of(rb);
+    gload();
+    rows_of(rb + WG_R);
     sstore(0);
     __syncthreads();
     for (int c = 0; c < nchunk; c++) {
       const int buf = c & 1;
-      if (c + 1 < nchunk) gload(rb + (c + 1) * WG_R);
-      bf16x8 af[2], bf[2];
+      if (c + 1 < nchunk) {
+        gload();
+        rows_of(rb + (c + 2) * WG_R);
+      }
 #pragma unroll
-      for (int i = 0; i < 2; i++) af[i] = *(const bf16x8*)&sp[buf][wm * 64 + i * 32 + l32][kh * 8];
+      for (int ks = 0; ks < WG_R / 16; ks++) {
+        bf16x8 af[2], bf[2];
 #pragma unroll
-      for (int j = 0; j < 2; j++) bf[j] = *(const bf16x8*)&sq[buf][wn * 64 + j * 32 + l32][kh * 8];
+        for (int i = 0; i < 2; i++) af[i] = *(const bf16x8*)&lds[0][buf][wm * 64 + i * 32 + l32][ks * 16 + kh * 8];
 #pragma unroll
-      for (int i = 0; i < 2; i++)
+        for (int j = 0; j < 2; j++) bf[j] = *(const bf16x8*)&lds[1][buf][wn * 64 + j * 32 + l32][ks * 16 + kh * 8];
 #pragma unroll
-        for (int j = 0; j < 2; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+          for (int j = 0; j < 2; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      }
       if (c + 1 < nchunk) sstore(buf ^ 1);
       __syncthreads();
     }
@@ -350,7 +388,9 @@ hipError_t launch_router_bwd(const float* scores, const int32_t* idx, const floa
 
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
   if (a.n_seg <= 0) return hipSuccess;
-  wgrad_kernel<<<dim3(a.n_seg, a.M / WG_T, a.Nn / WG_T), 256, 0, s>>>(a);
+  const long supers = (long)a.n_seg * ((a.M / WG_T + 7) / 8) * ((a.Nn / WG_T + 7) / 8);
+  const long blocks = (supers + 7) / 8 * 8 * 64;
+  wgrad_kernel<<<dim3((unsigned)blocks), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -659,10 +659,11 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
                             row_token, T, N, D, K, Ns, TK, T, dz, g->du, g->dE, s));  // dz, du, dE
   WgradArgs wa;
   wa.offsets = offsets; wa.n_seg = n_seg; wa.n_first = N;
-  wa.P = (const uint16_t*)dY; wa.Q = (const uint16_t*)H; wa.q_row = nullptr; wa.M = D; wa.Nn = I;
+  wa.P = (const uint16_t*)dY; wa.Q = (const uint16_t*)H; wa.q_row = nullptr; wa.q_rows = R; wa.M = D; wa.Nn = I;
   wa.out0 = g->dw2; wa.ostride0 = s2; wa.out1 = Ns ? g->dw2_shared : g->dw2; wa.ostride1 = s2;
   MOE_TRY(launch_wgrad(wa, s));                                                       // dW2 = dY^T H
-  wa.P = (const uint16_t*)dAB; wa.Q = (const uint16_t*)u; wa.q_row = row_token; wa.M = 2 * I; wa.Nn = D;
+  wa.P = (const uint16_t*)dAB; wa.Q = (const uint16_t*)u; wa.q_row = row_token; wa.q_rows = T; wa.M = 2 * I;
+  wa.Nn = D;
   wa.out0 = g->dw13; wa.ostride0 = s13; wa.out1 = Ns ? g->dw13_shared : g->dw13; wa.ostride1 = s13;
   MOE_TRY(launch_wgrad(wa, s));                                                       // dW13 = [dA dB]^T X
   return MOE_OK;

@@ -80,6 +80,7 @@ struct WgradArgs {
   const uint16_t* P;          // [R, M] bf16 permuted rows
   const uint16_t* Q;          // rows [*, Nn] bf16
   const int32_t* q_row;       // nullable: Q row of permuted row r
+  long q_rows;                // rows of Q (range of the buffer loads)
   const int32_t* offsets;     // [n_seg+1]
   int n_seg, M, Nn;           // M, Nn multiples of 128
   float* out0; float* out1; long ostride0, ostride1;   // [M, Nn] per segment
