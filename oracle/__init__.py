@@ -26,4 +26,4 @@ printed reference on the pages; they are pinned by special cases (dense
 SwiGLU, zero weights, linearity in W2) only.
 """
 
-from . import numerics, routing, ffn, permute, brute, balance, backward  # noqa: F401
+from . import numerics, routing, ffn, permute, brute, balance, backward, capacity  # noqa: F401
