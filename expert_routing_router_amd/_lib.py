@@ -86,6 +86,10 @@ def lib() -> ctypes.CDLL:
             "moe_backward": ([D, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeights), P, P, P,
                               ctypes.POINTER(MoeGrads), P, SZ, P], I32),
             "moe_seq_balance_loss": ([D, I32, ctypes.c_float, P, P, P, P, P, P, SZ, P], I32),
+            "moe_capacity_workspace_bytes": ([D], SZ),
+            "moe_capacity_mask": ([D, I32, P, P, P, P, P, SZ, P], I32),
+            "moe_forward_capacity": ([D, ctypes.POINTER(MoeWeights), P, P, P, ctypes.POINTER(MoeRouteOut),
+                                      I32, I32, P, P, P, SZ, P], I32),
             "moe_profile_enable": ([I32], I32),
             "moe_profile_read": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), I32], I32),
         }
@@ -209,6 +213,29 @@ def moe_forward(desc, weights: MoeWeights, u, b, out, ws, update_bias=True, topk
     _check("moe_forward", lib().moe_forward(
         ctypes.byref(desc), ctypes.byref(weights), _ptr(u, "u"), _ptr(b, "b"), _ptr(out, "out"),
         ctypes.byref(dbg) if dbg is not None else None, int(bool(update_bias)), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_capacity_workspace_bytes(desc) -> int:
+    return lib().moe_capacity_workspace_bytes(ctypes.byref(desc))
+
+
+def moe_capacity_mask(desc, capacity, scores, topk_idx, keep, ws, n_dropped=None, stream=None):
+    _check("moe_capacity_mask", lib().moe_capacity_mask(
+        ctypes.byref(desc), capacity, _ptr(scores, "scores"), _ptr(topk_idx, "topk_idx"), _ptr(keep, "keep"),
+        _ptr(n_dropped, "n_dropped", False), _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_forward_capacity(desc, weights: MoeWeights, u, b, out, ws, capacity, update_bias=True, keep=None,
+                         n_dropped=None, topk_idx=None, topk_gate=None, counts=None, stream=None):
+    dbg = None
+    if topk_idx is not None or topk_gate is not None or counts is not None:
+        dbg = MoeRouteOut(_ptr(topk_idx, "topk_idx", False), _ptr(topk_gate, "topk_gate", False),
+                          _ptr(counts, "counts", False))
+    _check("moe_forward_capacity", lib().moe_forward_capacity(
+        ctypes.byref(desc), ctypes.byref(weights), _ptr(u, "u"), _ptr(b, "b"), _ptr(out, "out"),
+        ctypes.byref(dbg) if dbg is not None else None, int(bool(update_bias)), capacity,
+        _ptr(keep, "keep", False), _ptr(n_dropped, "n_dropped", False), _ptr(ws, "ws"),
         ws.numel() * ws.element_size(), _stream(stream)))
 
 

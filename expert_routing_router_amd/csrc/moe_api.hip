@@ -138,6 +138,7 @@ extern "C" int moe_validate(const moe_desc_t* d) {
 struct Ws {
   size_t idx, gate, counts, bitmap, wprefix, offsets, mtile, row_token, slot_row, H, Y;
   size_t qu, su, qh, sh, offs_s, mtile_s, rscratch, total;
+  size_t keep, dropped, scores;   // capacity-limited forward only
 };
 
 static RouteArgs route_args(const moe_desc_t* d, const void* u, const void* E, const float* b,
@@ -150,7 +151,7 @@ static bool two_phase_router(const moe_desc_t* d) {
 
 static bool fused_shared(const moe_desc_t* d) { return d->n_shared == 0 || d->inter == d->inter_shared; }
 
-static Ws layout(const moe_desc_t* d) {
+static Ws layout(const moe_desc_t* d, bool capacity = false) {
   Ws w;
   const size_t T = d->T, K = d->top_k, N = d->n_routed, Ns = d->n_shared;
   const size_t W = (T + 63) / 64;
@@ -183,6 +184,13 @@ static Ws layout(const moe_desc_t* d) {
     w.qu = w.su = w.qh = w.sh = 0;
   }
   w.rscratch = two_phase_router(d) ? take(route_two_phase_bytes(d->T, d->n_routed, d->d, d->router_dtype)) : 0;
+  w.keep = w.dropped = w.scores = 0;
+  if (capacity) {
+    w.keep = take(T * K * 4);
+    w.dropped = take(4);
+    // the two-phase router leaves the affinities at the start of its scratch
+    w.scores = two_phase_router(d) ? w.rscratch : take(T * N * 4);
+  }
   w.total = o;
   return w;
 }
@@ -393,9 +401,11 @@ __global__ void iota_kernel(int32_t* p, int n, int step) {
   if (i <= n) p[i] = i * step;
 }
 
-extern "C" int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* u, float* b, void* out,
-                           moe_route_out_t* dbg, int32_t update_bias, void* ws, size_t ws_bytes,
-                           moe_stream_t stream) {
+// cap < 0: no capacity limit (the layer as the method defines it); cap >= 0: each expert keeps at
+// most cap selections (the dropping baseline), keep_out/n_dropped report what was kept.
+static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void* u, float* b, void* out,
+                        moe_route_out_t* dbg, int32_t update_bias, void* ws, size_t ws_bytes, hipStream_t s,
+                        int cap, int32_t* keep_out, int32_t* n_dropped) {
   int st = moe_validate(d);
   if (st) return st;
   if (!w || !aligned(u) || !aligned(b) || !aligned(out) || !aligned(ws)) return MOE_EINVAL;
@@ -409,11 +419,13 @@ extern "C" int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const vo
   if (dbg && (!aligned_or_null(dbg->topk_idx) || !aligned_or_null(dbg->topk_gate) ||
               !aligned_or_null(dbg->counts)))
     return MOE_EINVAL;
-  const Ws L = layout(d);
+  const bool capped = cap >= 0;
+  if (!aligned_or_null(keep_out) || !aligned_or_null(n_dropped)) return MOE_EINVAL;
+  const Ws L = layout(d, capped);
   if (ws_bytes < L.total) return MOE_EWORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
   if (d->T == 0) {
     if (dbg && dbg->counts) MOE_TRY(launch_fill_i32(dbg->counts, 0, d->n_routed, s));
+    if (n_dropped) MOE_TRY(launch_fill_i32(n_dropped, 0, 1, s));
     return MOE_OK;
   }
   uint8_t* base = (uint8_t*)ws;
@@ -432,24 +444,42 @@ extern "C" int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const vo
 
   // 1. router
   prof_mark(-1, s);
+  float* scores = capped ? (float*)(base + L.scores) : nullptr;
   RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, nullptr, idx, gate, counts);
-  if (two_phase_router(d)) MOE_TRY(launch_route_two_phase(ra, base + L.rscratch, s));
-  else MOE_TRY(launch_route(ra, route_front(d), s));
+  if (two_phase_router(d)) {
+    MOE_TRY(launch_route_two_phase(ra, base + L.rscratch, s));
+  } else {
+    ra.scores_out = scores;
+    MOE_TRY(launch_route(ra, route_front(d), s));
+  }
   prof_mark(MOE_STAGE_ROUTE, s);
 
   // 2. dispatch layout; shared experts become extra identity segments
-  const bool fused = fused_shared(d);
   const long TK = (long)T * K;
   const int bm = gemm_bm(d->expert_dtype, (int)(TK / N), d->d);
   PermuteArgs p;
   p.idx = idx; p.T = T; p.K = K; p.n_routed = N;
   p.bitmap = (uint64_t*)(base + L.bitmap); p.wprefix = (int32_t*)(base + L.wprefix);
   p.counts_ws = nullptr; p.offsets = offsets; p.row_token = row_token; p.slot_row = slot_row;
-  p.counts_out = nullptr; p.n_extra_seg = Ns;
+  p.counts_out = nullptr;
+  int32_t* keep = nullptr;
+  if (capped) {
+    // no-drop layout first (rows of each expert in token order), then the kept subset
+    p.n_extra_seg = 0; p.mtile_prefix = nullptr; p.bm = 0;
+    MOE_TRY(launch_permute(p, s));
+    keep = keep_out ? keep_out : (int32_t*)(base + L.keep);
+    MOE_TRY(launch_capacity(offsets, row_token, idx, scores, T, N, K, cap, keep,
+                            n_dropped ? n_dropped : (int32_t*)(base + L.dropped), s));
+    p.keep = keep;
+  }
+  p.n_extra_seg = Ns;
   p.mtile_prefix = d->expert_dtype == MOE_F32 ? nullptr : mtile;
   p.bm = bm;
   MOE_TRY(launch_permute(p, s));
   prof_mark(MOE_STAGE_PERMUTE, s);
+  // with dropping, the shared experts' rows sit at a fixed place (row T*K on) only in the
+  // separate shared pass, so that pass is used
+  const bool fused = fused_shared(d) && !capped;
 
   // 3. FP8: quantise u once per 1x128 tile
   const void* x = u;
@@ -476,6 +506,8 @@ extern "C" int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const vo
     int st2 = run_ffn(d, d->inter, x, T, xs, row_token, offsets, mtile, N, (int)TK, w->w13, w->w13_scale, w->w13,
                       w->w13_scale, w->w2, w->w2_scale, w->w2, w->w2_scale, N, H, qh, shs, Y, bm, s);
     if (st2) return st2;
+  }
+  if (!fused && Ns > 0) {
     int32_t* offs_s = (int32_t*)(base + L.offs_s);
     int32_t* mtile_s = (int32_t*)(base + L.mtile_s);
     iota_kernel<<<cdiv(Ns + 1, 64), 64, 0, s>>>(offs_s, Ns, T);
@@ -486,7 +518,7 @@ extern "C" int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const vo
     uint8_t* Ys = Y + (size_t)TK * d->d * yy;
     uint8_t* qhs = f8 ? qh + (size_t)TK * d->inter : nullptr;
     float* shss = f8 ? shs + (size_t)TK * (d->inter / 128) : nullptr;
-    st2 = run_ffn(d, d->inter_shared, x, T, xs, row_token + TK, offs_s, mtile_s, Ns, Ns * T, w->w13_shared,
+    int st2 = run_ffn(d, d->inter_shared, x, T, xs, row_token + TK, offs_s, mtile_s, Ns, Ns * T, w->w13_shared,
                   w->w13_shared_scale, w->w13_shared, w->w13_shared_scale, w->w2_shared, w->w2_shared_scale,
                   w->w2_shared, w->w2_shared_scale, Ns, Hs, qhs, shss, Ys, bms, s);
     if (st2) return st2;
@@ -505,6 +537,50 @@ extern "C" int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const vo
   if (update_bias) MOE_TRY(launch_update_bias(counts, b, N, TK, d->gamma, s));
   prof_mark(MOE_STAGE_BIAS, s);
   return MOE_OK;
+}
+
+extern "C" int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* u, float* b, void* out,
+                           moe_route_out_t* dbg, int32_t update_bias, void* ws, size_t ws_bytes,
+                           moe_stream_t stream) {
+  return forward_impl(d, w, u, b, out, dbg, update_bias, ws, ws_bytes, (hipStream_t)stream, -1, nullptr, nullptr);
+}
+
+extern "C" size_t moe_capacity_workspace_bytes(const moe_desc_t* d) {
+  if (moe_validate(d) != MOE_OK) return 0;
+  return layout(d, true).total;
+}
+
+extern "C" int moe_forward_capacity(const moe_desc_t* d, const moe_weights_t* w, const void* u, float* b,
+                                    void* out, moe_route_out_t* dbg, int32_t update_bias, int32_t capacity,
+                                    int32_t* keep, int32_t* n_dropped, void* ws, size_t ws_bytes,
+                                    moe_stream_t stream) {
+  if (capacity < 0) return MOE_EINVAL;
+  return forward_impl(d, w, u, b, out, dbg, update_bias, ws, ws_bytes, (hipStream_t)stream, capacity, keep,
+                      n_dropped);
+}
+
+extern "C" int moe_capacity_mask(const moe_desc_t* d, int32_t capacity, const float* scores,
+                                 const int32_t* topk_idx, int32_t* keep, int32_t* n_dropped, void* ws,
+                                 size_t ws_bytes, moe_stream_t stream) {
+  int st = moe_validate(d);
+  if (st) return st;
+  if (capacity < 0) return MOE_EINVAL;
+  if (!aligned(scores) || !aligned(topk_idx) || !aligned(keep) || !aligned_or_null(n_dropped) || !aligned(ws))
+    return MOE_EINVAL;
+  const Ws L = layout(d);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (d->T == 0) return n_dropped ? hip_status(launch_fill_i32(n_dropped, 0, 1, s)) : MOE_OK;
+  uint8_t* base = (uint8_t*)ws;
+  PermuteArgs p;
+  p.idx = topk_idx; p.T = d->T; p.K = d->top_k; p.n_routed = d->n_routed;
+  p.bitmap = (uint64_t*)(base + L.bitmap); p.wprefix = (int32_t*)(base + L.wprefix);
+  p.counts_ws = nullptr; p.offsets = (int32_t*)(base + L.offsets); p.row_token = (int32_t*)(base + L.row_token);
+  p.slot_row = (int32_t*)(base + L.slot_row); p.counts_out = nullptr;
+  p.n_extra_seg = 0; p.mtile_prefix = nullptr; p.bm = 0;
+  MOE_TRY(launch_permute(p, s));
+  return hip_status(launch_capacity(p.offsets, p.row_token, topk_idx, scores, d->T, d->n_routed, d->top_k,
+                                    capacity, keep, n_dropped, s));
 }
 
 extern "C" int moe_quantize_fp8(int32_t kind, const void* src, int32_t src_dtype, int32_t rows, int32_t cols,

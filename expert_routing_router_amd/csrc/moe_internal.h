@@ -35,8 +35,13 @@ struct PermuteArgs {
   int n_extra_seg;        // shared-expert segments appended after the routed rows (identity rows)
   int32_t* mtile_prefix;  // nullable [n_seg+1]: prefix of ceil(n_e/bm)
   int bm;
+  const int32_t* keep = nullptr;   // nullable [T*K]: 0 = dropped selection (slot_row -1, no row)
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// capacity limit: keep [T*K] (1 kept, 0 dropped) from the no-drop layout; dropped: total count
+hipError_t launch_capacity(const int32_t* offsets, const int32_t* row_token, const int32_t* idx,
+                           const float* scores, int T, int N, int K, int cap, int32_t* keep, int32_t* dropped,
+                           hipStream_t s);
 hipError_t launch_gather_rows(const void* src, const int32_t* row_token, void* dst,
                               long rows, int row_bytes, hipStream_t s);
 hipError_t launch_mtile_prefix(const int32_t* offsets, int n_seg, int bm, int32_t* out,

@@ -21,7 +21,8 @@ namespace moe {
 constexpr int PM_NMAX = 256;
 
 __global__ __launch_bounds__(256) void bitmap_kernel(const int32_t* __restrict__ idx, int T, int K,
-                                                     int N, uint64_t* __restrict__ bitmap) {
+                                                     int N, const int32_t* __restrict__ keep,
+                                                     uint64_t* __restrict__ bitmap) {
   __shared__ uint64_t words[4][PM_NMAX];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int e = lane; e < N; e += 64) words[wave][e] = 0ull;
@@ -30,7 +31,8 @@ __global__ __launch_bounds__(256) void bitmap_kernel(const int32_t* __restrict__
   const int t = w * 64 + lane;
   if (t < T)
     for (int k = 0; k < K; k++)
-      atomicOr((unsigned long long*)&words[wave][idx[(size_t)t * K + k]], 1ull << lane);
+      if (!keep || keep[(size_t)t * K + k])
+        atomicOr((unsigned long long*)&words[wave][idx[(size_t)t * K + k]], 1ull << lane);
   __syncthreads();
   const int W = cdiv(T, 64);
   if (w < W)
@@ -119,12 +121,15 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
                                                       const uint64_t* __restrict__ bitmap,
                                                       const int32_t* __restrict__ wprefix,
                                                       const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ keep,
                                                       int32_t* __restrict__ row_token,
                                                       int32_t* __restrict__ slot_row) {
   const long TK = (long)T * K;
   const long total = TK + (long)n_extra * T;
   for (long p = (long)blockIdx.x * blockDim.x + threadIdx.x; p < total; p += (long)gridDim.x * blockDim.x) {
-    if (p < TK) {
+    if (p < TK && keep && !keep[p]) {
+      slot_row[p] = -1;                     // dropped selection: no row
+    } else if (p < TK) {
       const int t = (int)(p / K);
       const int e = idx[p];
       const int w = t >> 6, bit = t & 63;
@@ -163,13 +168,13 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restr
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   const int W = cdiv(a.T, 64);
-  bitmap_kernel<<<cdiv(W, 4), 256, 0, s>>>(a.idx, a.T, a.K, a.n_routed, a.bitmap);
+  bitmap_kernel<<<cdiv(W, 4), 256, 0, s>>>(a.idx, a.T, a.K, a.n_routed, a.keep, a.bitmap);
   scan_kernel<<<1, 256, 0, s>>>(a.bitmap, a.T, a.K, a.n_routed, a.n_extra_seg, a.wprefix, a.offsets,
                                 a.counts_out, a.mtile_prefix, a.bm);
   const long total = (long)a.T * a.K + (long)a.n_extra_seg * a.T;
   const int blocks = (int)std::min<long>(cdiv<long>(total, 256), 2048);
   scatter_kernel<<<blocks, 256, 0, s>>>(a.idx, a.T, a.K, a.n_routed, a.n_extra_seg, a.bitmap,
-                                        a.wprefix, a.offsets, a.row_token, a.slot_row);
+                                        a.wprefix, a.offsets, a.keep, a.row_token, a.slot_row);
   return hipGetLastError();
 }
 

@@ -98,6 +98,18 @@ class MoELayer:
                       self.idx, self.gate, self.counts, stream=stream)
         return self.out
 
+    def forward_capacity(self, u: torch.Tensor, b: torch.Tensor, capacity: int, update_bias=True, stream=None):
+        """forward() with each expert capped at `capacity` selections (the token-dropping baseline);
+        self.keep [T, K] int32 and self.n_dropped [1] say what was kept."""
+        if getattr(self, "_cap_ws", None) is None:
+            dev = self.device
+            self._cap_ws = torch.empty(L.moe_capacity_workspace_bytes(self.desc), dtype=torch.uint8, device=dev)
+            self.keep = torch.empty((self.cfg.T, self.cfg.top_k), dtype=torch.int32, device=dev)
+            self.n_dropped = torch.empty(1, dtype=torch.int32, device=dev)
+        L.moe_forward_capacity(self.desc, self.weights, u, b, self.out, self._cap_ws, capacity, update_bias,
+                               self.keep, self.n_dropped, self.idx, self.gate, self.counts, stream=stream)
+        return self.out
+
     def backward(self, u: torch.Tensor, b: torch.Tensor, dout: torch.Tensor, stream=None):
         """Gradients of forward(u, b) for the upstream gradient dout [T, d] (bf16), for the routing
         the forward chooses with this b: a dict of fp32 device tensors du [T, d], dE [N_r, d],

@@ -236,6 +236,36 @@ int moe_forward(const moe_desc_t* desc, const moe_weights_t* w, const void* u, f
                 void* out, moe_route_out_t* dbg, int32_t update_bias, void* ws,
                 size_t ws_bytes, moe_stream_t stream);
 
+/* Capacity-limited dispatch with token dropping: the DeepSeek-V2-style
+ * baseline that DeepSeek-V3 does without (pwwt.cn note on the report,
+ * section 1.4: V2 caps what a device receives and drops the lowest-affinity
+ * tokens, which then skip the layer's experts; V3 drops none). On one GPU the
+ * cap is per expert:
+ *   keep [T*K] int32 (row-major over (t, k), 1 = kept, 0 = dropped): an
+ *   expert with more than `capacity` selections keeps the `capacity` with the
+ *   largest affinity scores[t, e] (ties: lower t) and drops the rest; every
+ *   selection of an expert at or under the cap is kept. The caller picks
+ *   capacity, e.g. ceil(cf * T * K / N_r) for a capacity factor cf; capacity
+ *   0 drops every routed selection. n_dropped [1] (nullable): total dropped.
+ *
+ * moe_capacity_mask: the mask alone, from given affinities scores [T, N_r]
+ *   fp32 and selections topk_idx [T, K]. ws: moe_workspace_bytes(desc).
+ * moe_forward_capacity: moe_forward with the cap applied between routing and
+ *   the experts. A dropped selection skips its expert and adds nothing to the
+ *   token's output; the token's other gates are not renormalised. The bias
+ *   update (update_bias != 0) uses the router's loads before dropping. keep
+ *   nullable (workspace-internal when null). ws:
+ *   moe_capacity_workspace_bytes(desc) (0 on bad desc).
+ * Both: MOE_EINVAL for capacity < 0 or misaligned pointers. */
+size_t moe_capacity_workspace_bytes(const moe_desc_t* desc);
+int moe_capacity_mask(const moe_desc_t* desc, int32_t capacity, const float* scores,
+                      const int32_t* topk_idx, int32_t* keep, int32_t* n_dropped, void* ws,
+                      size_t ws_bytes, moe_stream_t stream);
+int moe_forward_capacity(const moe_desc_t* desc, const moe_weights_t* w, const void* u, float* b,
+                         void* out, moe_route_out_t* dbg, int32_t update_bias, int32_t capacity,
+                         int32_t* keep, int32_t* n_dropped, void* ws, size_t ws_bytes,
+                         moe_stream_t stream);
+
 /* FP8 quantiser (xyznot.com guides, FP8 key idea; pwwt.cn note section 3):
  *   scale = fl32(amax/448) per 1x128 tile (ACT) or 128x128 block (W), 1 when
  *   amax = 0; q = E4M3(fl32(x/scale)), round to nearest even, saturated.

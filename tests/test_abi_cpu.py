@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = L.header_symbols()
-    assert len(names) == 20, names
+    assert len(names) == 23, names
     raw = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -163,3 +163,22 @@ def test_seq_balance_arg_errors(lib):
     assert st == M.MOE_EINVAL
     st = lib.moe_seq_balance_loss(ctypes.byref(d), 0, 1e-4, null, null, None, None, null, null, 1 << 20, None)
     assert st == M.MOE_EINVAL
+
+
+def test_capacity_arg_errors(lib):
+    """Capacity-limited dispatch: negative capacity, misaligned pointers and a short workspace are
+    refused before any launch; the capped forward needs more workspace than moe_forward."""
+    d = _v3()
+    need, need_cap = M.moe_workspace_bytes(d), M.moe_capacity_workspace_bytes(d)
+    assert need_cap > need
+    mask = lambda cap, ws_bytes, scores=A: lib.moe_capacity_mask(
+        ctypes.byref(d), cap, scores, A, A, None, A, ws_bytes, None)
+    assert mask(-1, need) == M.MOE_EINVAL
+    assert mask(10, need, MIS) == M.MOE_EINVAL
+    assert mask(10, need - 256) == M.MOE_EWORKSPACE
+    w = M.MoeWeights(A, A, A, A, A, None, None, None, None)
+    fc = lambda cap, ws_bytes, keep=None: lib.moe_forward_capacity(
+        ctypes.byref(d), ctypes.byref(w), A, A, A, None, 1, cap, keep, None, A, ws_bytes, None)
+    assert fc(-1, need_cap) == M.MOE_EINVAL
+    assert fc(256, need) == M.MOE_EWORKSPACE
+    assert fc(256, need_cap, MIS) == M.MOE_EINVAL
