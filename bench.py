@@ -13,6 +13,7 @@ progress goes to stderr.
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -98,6 +99,12 @@ def cpu_baseline(cfg, n_sample_experts, log_fn):
     import numpy as np
     from oracle import ffn, numerics as nx, routing
     from workloads import gen
+    cpu_model = "?"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "?")
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
         info = threadpool_info()
@@ -135,9 +142,10 @@ def cpu_baseline(cfg, n_sample_experts, log_fn):
     return {"value": cfg.T / per_fwd, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": "one %d-token step: routing of all tokens; SwiGLU of experts 0..%d over their %d "
                       "routed rows, scaled by %d/%d; shared expert over %d tokens, scaled by %d; fp64 numpy "
-                      "(BLAS %s); measured %.1f s of CPU work"
+                      "(BLAS %s, %d threads; %s, %d cores available); measured %.1f s of CPU work"
                       % (cfg.T, len(sample) - 1, rows_done, cfg.n_routed, len(sample), Tsub,
-                         cfg.T // Tsub, blas, t_route + t_routed + t_shared)}
+                         cfg.T // Tsub, blas, cores, cpu_model, len(os.sched_getaffinity(0)),
+                         t_route + t_routed + t_shared)}
 
 
 def main():
@@ -154,6 +162,10 @@ def main():
     ap.add_argument("--load-trajectory", type=int, default=0,
                     help="after the timed steps, run this many forward+update steps from the initial "
                          "bias and report the max/mean expert load of each (every 10th listed)")
+    ap.add_argument("--capacity-factors", default="1.0,1.25",
+                    help="also time the token-dropping baseline (per-expert capacity ceil(cf*T*K/N_r)) at "
+                         "these factors, with the initial bias and with the bias after 100 balancing steps "
+                         "(empty: skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times) and exit: the "
                          "reference dispatch for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -202,14 +214,21 @@ def main():
     M.moe_profile_read(reset=True)
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
+        step_ev[i].record(stream)
         layer.forward(us[i % nb], b, update_bias=True)
+    step_ev[args.steps].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+    per_step = sorted(step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps))
+
+    def pct(q):
+        return per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
     stage_ms, calls = M.moe_profile_read(reset=True)
     M.moe_profile_enable(False)
     ev_ms = ev0.elapsed_time(ev1)
@@ -238,6 +257,37 @@ def main():
                       "first": round(ratios[0], 3), "last": round(ratios[-1], 3),
                       "mean_last_20": round(sum(ratios[-20:]) / len(ratios[-20:]), 3)}
         log("load trajectory: max/mean %.3f -> %.3f over %d steps" % (ratios[0], ratios[-1], len(ratios)))
+
+    # the token-dropping baseline: the same step with each expert capped; reported beside the step
+    capacity = None
+    cfs = [float(x) for x in args.capacity_factors.split(",") if x.strip()]
+    if cfs and cfg.T > 0:
+        b_bal = np_to_device(gen.bias_init(cfg), "f32", "cuda:0")
+        for i in range(100):
+            layer.forward(us[i % nb], b_bal, update_bias=True)
+        biases = {"initial": np_to_device(gen.bias_init(cfg), "f32", "cuda:0"), "balanced_100": b_bal}
+        capacity = []
+        for cf in cfs:
+            cap = int(math.ceil(cf * cfg.T * cfg.top_k / cfg.n_routed))
+            row = {"cf": cf, "capacity": cap}
+            for bname, bb in biases.items():
+                layer.forward_capacity(us[0], bb, cap, update_bias=False)
+                torch.cuda.synchronize()
+                nd = []
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                n_cap = 5
+                e0.record(stream)
+                for i in range(n_cap):
+                    layer.forward_capacity(us[i % nb], bb, cap, update_bias=False)
+                    nd.append(layer.n_dropped.clone())
+                e1.record(stream)
+                torch.cuda.synchronize()
+                frac = sum(int(x.item()) for x in nd) / (n_cap * cfg.T * cfg.top_k)
+                row[bname] = {"ms": round(e0.elapsed_time(e1) / n_cap, 4), "dropped_frac": round(frac, 5)}
+            capacity.append(row)
+            log("capacity cf %.2f: %s" % (cf, row))
+        capacity = {"no_drop_ms_per_step": round(ev_ms / args.steps, 4), "runs": capacity,
+                    "note": "forward without bias update, 5 calls each over the resident batches"}
 
     # the sequence-wise balance loss (forward value) from this layer's router outputs:
     # timed on its own, it is not part of the forward step
@@ -296,6 +346,31 @@ def main():
         log("backward: %.3f ms/call (%.0f TFLOP/s, %.0f GB/s algorithmic)" % (bwd_ms, flops / bwd_ms / 1e9,
                                                                            byts / bwd_ms / 1e6))
 
+    # the machine's ceilings, measured here: a streaming read and an MFMA-only loop
+    cal_buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda:0")
+    cal_sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    M.moe_calibrate_read(cal_buf, cal_sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        M.moe_calibrate_read(cal_buf, cal_sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    read_gbs = 3 * cal_buf.numel() / e0.elapsed_time(e1) / 1e6
+    del cal_buf
+    iters = 4000
+    fsink = torch.zeros(4, dtype=torch.float32, device="cuda:0")
+    M.moe_calibrate_mfma_bf16(100, fsink)
+    e0.record(stream)
+    M.moe_calibrate_mfma_bf16(iters, fsink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mfma_tf = M.MOE_CAL_MFMA_WAVES * iters * 8 * 32768.0 / e0.elapsed_time(e1) / 1e9
+    measured = {"hbm_read_GBps": round(read_gbs, 1), "mfma_bf16_TFLOPs": round(mfma_tf, 1),
+                "how": "moe_calibrate_read: 3 streaming reads of 4 GiB; moe_calibrate_mfma_bf16: "
+                       "8192 waves x 4000 x 8 independent 32x32x16 bf16 MFMAs"}
+    log("measured ceilings: HBM read %.0f GB/s, bf16 MFMA %.0f TFLOP/s" % (read_gbs, mfma_tf))
+
     alg = algorithmic(cfg)
     peak_tf = PEAK_TFLOPS[cfg.expert_dtype]
     kernels = {}
@@ -316,6 +391,11 @@ def main():
     g_tf = (alg["gemm1"]["flops"] + alg["gemm2"]["flops"]) / g_ms / 1e9
     kernels["grouped_gemm"] = {"ms": round(g_ms, 4), "TFLOP/s": round(g_tf, 1),
                                "mfma_frac": round(g_tf / peak_tf, 4)}
+    if cfg.expert_dtype == "bf16":
+        kernels["grouped_gemm"]["mfma_frac_of_measured"] = round(g_tf / mfma_tf, 4)
+    for k in kernels.values():
+        if "GB/s" in k:
+            k["hbm_frac_of_measured"] = round(k["GB/s"] / read_gbs, 4)
 
     g1 = alg["gemm1"]
     g1_ms = stage_ms["gemm1"] / max(calls, 1)
@@ -323,7 +403,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(cfg),
                 "kernel": "grouped gate/up GEMM + SwiGLU over routed and shared rows (gemm_%s kernel)" % ("bf16_dma" if cfg.expert_dtype == "bf16" else cfg.expert_dtype),
-                "bytes_per_launch": g1["bytes"], "avg_ms": round(g1_ms, 4)}
+                "bytes_per_launch": g1["bytes"], "avg_ms": round(g1_ms, 4),
+                "measured_peak": round(read_gbs, 1), "frac_of_measured": round(achieved / read_gbs, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -352,7 +433,10 @@ def main():
         "max_over_mean_load": [round(x, 3) for x in loads],
         "load_trajectory": trajectory,
         "backward": bwd,
+        "capacity_baseline": capacity,
         "event_ms_per_step": round(ev_ms / args.steps, 4),
+        "step_ms": {"median": round(pct(0.5), 4), "p10": round(pct(0.1), 4), "p90": round(pct(0.9), 4)},
+        "measured_ceilings": measured,
     }
     print(json.dumps(rec), flush=True)
 

@@ -18,4 +18,5 @@ from ._lib import (  # noqa: F401
     moe_transpose_expert_weights, moe_backward_workspace_bytes, moe_backward, make_grads,
     moe_capacity_workspace_bytes, moe_capacity_mask, moe_forward_capacity,
     moe_profile_enable, moe_profile_read, STAGES,
+    moe_calibrate_read, moe_calibrate_mfma_bf16, MOE_CAL_MFMA_WAVES,
 )

@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
             "moe_capacity_mask": ([D, I32, P, P, P, P, P, SZ, P], I32),
             "moe_forward_capacity": ([D, ctypes.POINTER(MoeWeights), P, P, P, ctypes.POINTER(MoeRouteOut),
                                       I32, I32, P, P, P, SZ, P], I32),
+            "moe_calibrate_read": ([P, SZ, P, P], I32),
+            "moe_calibrate_mfma_bf16": ([I32, P, P], I32),
             "moe_profile_enable": ([I32], I32),
             "moe_profile_read": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), I32], I32),
         }
@@ -277,6 +279,18 @@ def moe_backward(desc, weights: MoeWeights, wt: MoeWeights, u, b, dout, grads: M
         ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(wt), _ptr(u, "u"), _ptr(b, "b"),
         _ptr(dout, "dout"), ctypes.byref(grads), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+MOE_CAL_MFMA_WAVES = 8192
+
+
+def moe_calibrate_read(buf, sink, stream=None):
+    _check("moe_calibrate_read", lib().moe_calibrate_read(
+        _ptr(buf, "buf"), buf.numel() * buf.element_size(), _ptr(sink, "sink"), _stream(stream)))
+
+
+def moe_calibrate_mfma_bf16(iters, sink, stream=None):
+    _check("moe_calibrate_mfma_bf16", lib().moe_calibrate_mfma_bf16(iters, _ptr(sink, "sink"), _stream(stream)))
 
 
 STAGES = ("route", "permute", "quant_x", "gemm1", "gemm2", "combine", "bias")

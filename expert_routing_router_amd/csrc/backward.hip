@@ -18,6 +18,7 @@
 // GEMM and the weight transposes; the dense GEMMs (A|B, Y, dH, dX) reuse the
 // forward's grouped GEMM kernels with transposed weight copies.
 #include "common.h"
+#include "lds_dma.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -321,6 +322,217 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a) {
       }
 }
 
+// ---------------------------------------------------------------- weight gradients, large shapes
+// When M and Nn are multiples of 256 the products run as grouped GEMMs whose
+// contraction runs along memory: P and Q are first transposed, segment by
+// segment, into PT [M][pitch] and QT [Nn][pitch] with each segment's rows
+// padded with zeros to a multiple of 64 (kofs[e] = where segment e starts),
+// then C_e = PT_e QT_e^T with the forward GEMM's operand path: 256x256 tiles,
+// 8 waves, LDS-DMA ring of four K=32 stages. The kernel is persistent (256
+// workgroups, one per CU), so one tile's fp32 stores drain while the next
+// tile's loads and MFMAs run.
+constexpr int WT_PAD = 64;
+
+// kofs[e] = sum over e' < e of roundup(n_e', 64); kofs[n_seg] = padded total
+__global__ __launch_bounds__(64) void wg_kofs_kernel(const int32_t* __restrict__ offsets, int n_seg,
+                                                     int32_t* __restrict__ kofs) {
+  __shared__ int32_t so[512];
+  for (int i = threadIdx.x; i <= n_seg; i += 64) so[i] = offsets[i];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int e = 0; e < n_seg; e++) {
+      kofs[e] = acc;
+      acc += (so[e + 1] - so[e] + WT_PAD - 1) / WT_PAD * WT_PAD;
+    }
+    kofs[n_seg] = acc;
+  }
+}
+
+// dst[c][kofs[e] + j] = src[row(offsets[e] + j)][c] for j < n_e, 0 for the padding;
+// row(r) = q_row ? q_row[r] : r. grid (cols / 256, upper bound on padded positions / 64),
+// 256 threads; thread (rt, ct) moves the 8x8 micro-tile of positions p0 + 8 rt .. and
+// columns c0 + 8 ct .., transposed in registers.
+__global__ __launch_bounds__(256) void seg_transpose_kernel(const uint16_t* __restrict__ src,
+                                                            const int32_t* __restrict__ q_row,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ kofs, int n_seg, int cols,
+                                                            long pitch, uint16_t* __restrict__ dst) {
+  const int p0 = blockIdx.y * WT_PAD;
+  if (p0 >= kofs[n_seg]) return;
+  // the segment holding p0: the last e with kofs[e] <= p0 (empty segments before it share its kofs)
+  int lo = 0, hi = n_seg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (kofs[mid] <= p0) lo = mid; else hi = mid - 1;
+  }
+  const int j0 = p0 - kofs[lo], rb = offsets[lo], n = offsets[lo + 1] - rb;
+  const int rt = threadIdx.x & 7, ct = threadIdx.x >> 3;
+  const int c0 = blockIdx.x * 256 + ct * 8;
+  i32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int j = j0 + 8 * rt + i;
+    if (j < n) {
+      const int r = rb + j;
+      const long sr = q_row ? q_row[r] : r;
+      v[i] = *(const i32x4*)(src + sr * cols + c0);
+    } else {
+      v[i] = i32x4{0, 0, 0, 0};
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < 8; jj++) *(i32x4*)(dst + (size_t)(c0 + jj) * pitch + p0 + 8 * rt) = column_of(v, jj);
+}
+
+struct WgDma {
+  static constexpr int THREADS = 512, BM = 256, BN = 256, RB = 64, BK = 32, CPR = 4, RPB = 16, STAGES = 4;
+  static constexpr int A_BYTES = BM * RB, STAGE = (BM + BN) * RB, BYTES = STAGES * STAGE;
+  static constexpr int PER_OP = BM / RPB / 8;         // 1 KB blocks of each operand per wave per stage
+  static constexpr int NPARTS = 2 * PER_OP;
+  static constexpr int GRID = 256;                    // 32 workgroups per XCD
+  static constexpr int SUPER = GRID / 8;              // tiles per super-tile
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+struct WgradDmaArgs {
+  const uint16_t* PT; const uint16_t* QT; long pitch; const int32_t* kofs;
+  int n_seg, M, Nn, sm, sn;                           // super-tile of sm x sn tiles (sm * sn = 32)
+  float* out0; float* out1; long ostride0, ostride1; int n_first;
+};
+
+__global__ __launch_bounds__(512, 1) void wgrad_dma_kernel(WgradDmaArgs a) {
+  using C = WgDma;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  // Workgroup i runs on XCD i % 8. Super-tile st (sm x sn tiles of one segment) goes to
+  // XCD st % 8, whose 32 workgroups take one tile each, so the tiles running together on an
+  // XCD share their operand rows in its L2; super-tiles are dealt round-robin so segments of
+  // very different lengths spread over all XCDs.
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int MT = a.M / C::BM, NT = a.Nn / C::BN;
+  const int smt = (MT + a.sm - 1) / a.sm, snt = (NT + a.sn - 1) / a.sn;
+  const int per_seg = smt * snt, n_super = a.n_seg * per_seg;
+  const uint32_t lds0 = lds_addr(lds);
+  const int brow = lane / C::CPR;
+  const int bchunk = (lane % C::CPR) ^ ((brow >> 2) & 3);
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int sw = (l32 >> 2) & 3;
+  int roff[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ks++) roff[ks] = l32 * C::RB + (((2 * ks + khalf) ^ sw) << 4);
+  const i32x4 pr = rsrc_words(a.PT, (long)a.M * a.pitch * 2);
+  const i32x4 qr = rsrc_words(a.QT, (long)a.Nn * a.pitch * 2);
+
+  for (int sidx = 0;; sidx++) {
+    const int st = xcd + 8 * sidx;
+    if (st >= n_super) break;
+    const int seg = st / per_seg, srem = st - seg * per_seg;
+    const int mt = (srem / snt) * a.sm + q / a.sn, nt = (srem % snt) * a.sn + q % a.sn;
+    if (mt >= MT || nt >= NT) continue;
+    const int k0 = a.kofs[seg];
+    const int nk = (a.kofs[seg + 1] - k0) / C::BK;
+    int aoff[C::PER_OP], boff[C::PER_OP];
+#pragma unroll
+    for (int i = 0; i < C::PER_OP; i++) {
+      const int r = (wave + 8 * i) * C::RPB + brow;
+      aoff[i] = (int)(((long)(mt * C::BM + r) * a.pitch + k0 + bchunk * 8) * 2);
+      boff[i] = (int)(((long)(nt * C::BN + r) * a.pitch + k0 + bchunk * 8) * 2);
+    }
+    auto issue_part = [&](auto p_tag, int kt, int buf) __attribute__((always_inline)) {
+      constexpr int P = decltype(p_tag)::value;
+      const uint32_t sbase = lds0 + buf * C::STAGE;
+      if constexpr (P < C::PER_OP)
+        dma_b128(pr, aoff[P], kt * C::RB, sbase + (wave + 8 * P) * 1024);
+      else
+        dma_b128(qr, boff[P - C::PER_OP], kt * C::RB, sbase + C::A_BYTES + (wave + 8 * (P - C::PER_OP)) * 1024);
+    };
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+    __syncthreads();   // every wave is done reading the previous tile's stages
+    if (nk > 0) {
+      constexpr int S = C::STAGES;
+#pragma unroll
+      for (int p = 0; p < S - 1; p++)
+        static_for<C::NPARTS>([&](auto pp) __attribute__((always_inline)) { issue_part(pp, min(p, nk - 1), p); });
+      for (int kt = 0; kt < nk; kt++) {
+        wait_vmcnt<(S - 2) * C::NPARTS>();
+        __syncthreads();
+        const int buf = kt % S, kti = min(kt + S - 1, nk - 1), bufi = (kt + S - 1) % S;
+        const uint8_t* A = lds + buf * C::STAGE;
+        const uint8_t* B = A + C::A_BYTES;
+        bf16x8 af[2][4], bf[2][2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+#pragma unroll
+          for (int i = 0; i < 4; i++) af[ks][i] = *(const bf16x8*)(A + (2 * i + wm) * 32 * C::RB + roff[ks]);
+#pragma unroll
+          for (int j = 0; j < 2; j++) bf[ks][j] = *(const bf16x8*)(B + (wn * 64 + j * 32) * C::RB + roff[ks]);
+        }
+        // 16 MFMAs in four groups, one refill load in front of each group
+        static_for<4>([&](auto g_tag) __attribute__((always_inline)) {
+          constexpr int g = decltype(g_tag)::value, ks = g >> 1, i0 = (g & 1) * 2;
+          issue_part(std::integral_constant<int, g>{}, kti, bufi);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = i0; i < i0 + 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bf[ks][j], acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+      wait_vmcnt<0>();   // no LDS write may land after the tile's reads
+    }
+    float* out = seg < a.n_first ? a.out0 + (size_t)seg * a.ostride0
+                                 : a.out1 + (size_t)(seg - a.n_first) * a.ostride1;
+    // D element (8*(r>>2) + 4*(lane>>5) + (r&3), lane&31) of each 32x32 block
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int m = mt * C::BM + (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+          const int n = nt * C::BN + wn * 64 + j * 32 + l32;
+          out[(size_t)m * a.Nn + n] = acc[i][j][r];
+        }
+  }
+}
+
+long wgrad_pitch(long rows, int n_seg) { return (rows + (long)WT_PAD * n_seg + WT_PAD - 1) / WT_PAD * WT_PAD; }
+
+static hipError_t launch_wgrad_dma(const WgradArgs& a, hipStream_t s) {
+  hipError_t e;
+  wg_kofs_kernel<<<1, 64, 0, s>>>(a.offsets, a.n_seg, a.kofs);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 gp(a.M / 256, (unsigned)(a.pitch / WT_PAD)), gq(a.Nn / 256, (unsigned)(a.pitch / WT_PAD));
+  seg_transpose_kernel<<<gp, 256, 0, s>>>(a.P, nullptr, a.offsets, a.kofs, a.n_seg, a.M, a.pitch, a.pt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  seg_transpose_kernel<<<gq, 256, 0, s>>>(a.Q, a.q_row, a.offsets, a.kofs, a.n_seg, a.Nn, a.pitch, a.qt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  WgradDmaArgs g;
+  g.PT = a.pt; g.QT = a.qt; g.pitch = a.pitch; g.kofs = a.kofs;
+  g.n_seg = a.n_seg; g.M = a.M; g.Nn = a.Nn;
+  const int NT = a.Nn / 256;
+  g.sn = NT % 8 == 0 ? 8 : NT % 4 == 0 ? 4 : NT >= 8 ? 8 : (NT >= 4 ? 4 : (NT >= 2 ? 2 : 1));
+  g.sm = WgDma::SUPER / g.sn;
+  g.out0 = a.out0; g.out1 = a.out1; g.ostride0 = a.ostride0; g.ostride1 = a.ostride1; g.n_first = a.n_first;
+  auto k = wgrad_dma_kernel;
+  if ((e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, WgDma::BYTES)) !=
+      hipSuccess)
+    return e;
+  k<<<WgDma::GRID, WgDma::THREADS, WgDma::BYTES, s>>>(g);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- transposes
 // dst[b][c][r] = src[b][r][c] for bf16 [batch][rows][cols], 64x64 tiles via LDS
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
@@ -388,6 +600,7 @@ hipError_t launch_router_bwd(const float* scores, const int32_t* idx, const floa
 
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
   if (a.n_seg <= 0) return hipSuccess;
+  if (a.pt && a.qt && a.kofs && a.M % 256 == 0 && a.Nn % 256 == 0) return launch_wgrad_dma(a, s);
   const long supers = (long)a.n_seg * ((a.M / WG_T + 7) / 8) * ((a.Nn / WG_T + 7) / 8);
   const long blocks = (supers + 7) / 8 * 8 * 64;
   wgrad_kernel<<<dim3((unsigned)blocks), 256, 0, s>>>(a);

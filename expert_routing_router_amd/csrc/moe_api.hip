@@ -86,6 +86,19 @@ static size_t esize(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1;
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 extern "C" int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+static_assert(kCalMfmaWaves == MOE_CAL_MFMA_WAVES, "calibration grid and header disagree");
+
+extern "C" int moe_calibrate_read(const void* buf, size_t bytes, int32_t* sink, moe_stream_t stream) {
+  if (!aligned(buf) || !aligned(sink) || bytes % 16) return MOE_EINVAL;
+  if (bytes == 0) return MOE_OK;
+  return hip_status(launch_cal_read(buf, bytes, sink, (hipStream_t)stream));
+}
+
+extern "C" int moe_calibrate_mfma_bf16(int32_t iters, float* sink, moe_stream_t stream) {
+  if (iters < 1 || !aligned(sink)) return MOE_EINVAL;
+  return hip_status(launch_cal_mfma(iters, sink, (hipStream_t)stream));
+}
 extern "C" int moe_last_hip_error(void) { return g_last_hip; }
 extern "C" const char* moe_strerror(int st) {
   switch (st) {
@@ -607,7 +620,8 @@ static int backward_shape_ok(const moe_desc_t* d) {
 
 struct BwdWs {
   size_t idx, gate, counts, scores, bitmap, wprefix, offsets, mtile, row_token, slot_row;
-  size_t ab, h, y, dy, dh, dab, dg, dz, total;
+  size_t ab, h, y, dy, dh, dab, dg, dz, pt, qt, kofs, total;
+  long pitch;
 };
 
 static BwdWs bwd_layout(const moe_desc_t* d) {
@@ -634,6 +648,12 @@ static BwdWs bwd_layout(const moe_desc_t* d) {
   w.dab = take(R * 2 * I * 2);
   w.dg = take(T * K * 4);
   w.dz = take(T * K * 4);
+  // transposed, padded operands of the weight-gradient GEMMs (d a multiple of 256)
+  w.pitch = D % 256 == 0 ? wgrad_pitch((long)R, (int)n_seg) : 0;
+  const size_t wide = D > 2 * I ? D : 2 * I;
+  w.pt = w.pitch ? take(wide * (size_t)w.pitch * 2) : 0;
+  w.qt = w.pitch ? take(wide * (size_t)w.pitch * 2) : 0;
+  w.kofs = w.pitch ? take((n_seg + 1) * 4) : 0;
   w.total = o;
   return w;
 }
@@ -735,6 +755,10 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
                             row_token, T, N, D, K, Ns, TK, T, dz, g->du, g->dE, s));  // dz, du, dE
   WgradArgs wa;
   wa.offsets = offsets; wa.n_seg = n_seg; wa.n_first = N;
+  if (L.pitch) {
+    wa.pt = (uint16_t*)(base + L.pt); wa.qt = (uint16_t*)(base + L.qt); wa.kofs = (int32_t*)(base + L.kofs);
+    wa.pitch = L.pitch;
+  }
   wa.P = (const uint16_t*)dY; wa.Q = (const uint16_t*)H; wa.q_row = nullptr; wa.q_rows = R; wa.M = D; wa.Nn = I;
   wa.out0 = g->dw2; wa.ostride0 = s2; wa.out1 = Ns ? g->dw2_shared : g->dw2; wa.ostride1 = s2;
   MOE_TRY(launch_wgrad(wa, s));                                                       // dW2 = dY^T H

@@ -38,6 +38,10 @@ struct PermuteArgs {
   const int32_t* keep = nullptr;   // nullable [T*K]: 0 = dropped selection (slot_row -1, no row)
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// diagnostics: streaming read of `bytes` (multiple of 16); kCalMfmaWaves waves of iters x 8 bf16 MFMAs
+constexpr int kCalMfmaWaves = 8192;
+hipError_t launch_cal_read(const void* buf, size_t bytes, int32_t* sink, hipStream_t s);
+hipError_t launch_cal_mfma(int iters, float* sink, hipStream_t s);
 // capacity limit: keep [T*K] (1 kept, 0 dropped) from the no-drop layout; dropped: total count
 hipError_t launch_capacity(const int32_t* offsets, const int32_t* row_token, const int32_t* idx,
                            const float* scores, int T, int N, int K, int cap, int32_t* keep, int32_t* dropped,
@@ -90,7 +94,11 @@ struct WgradArgs {
   int n_seg, M, Nn;           // M, Nn multiples of 128
   float* out0; float* out1; long ostride0, ostride1;   // [M, Nn] per segment
   int n_first;                // segments below: out0, others: out1
+  // nullable scratch for the transposed-operand path (M, Nn multiples of 256): pt [M][pitch],
+  // qt [Nn][pitch] bf16, kofs [n_seg+1]; pitch = wgrad_pitch(rows of P, n_seg)
+  uint16_t* pt = nullptr; uint16_t* qt = nullptr; int32_t* kofs = nullptr; long pitch = 0;
 };
+long wgrad_pitch(long rows, int n_seg);
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
 hipError_t launch_swiglu_fwd(const void* ab, void* h, long rows, int I, hipStream_t s);
 hipError_t launch_swiglu_bwd(const void* dh, const void* ab, void* dab, long rows, int I, hipStream_t s);

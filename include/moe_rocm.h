@@ -294,6 +294,20 @@ int moe_quantize_fp8(int32_t kind, const void* src, int32_t src_dtype, int32_t r
 int moe_profile_enable(int on);
 int moe_profile_read(double* ms, int64_t* calls, int reset);
 
+/* Calibration (diagnostics, for benchmarks): the ceilings a roofline fraction
+ * can be quoted against besides the published peaks.
+ * moe_calibrate_read: one streaming read of buf [bytes] (bytes % 16 == 0,
+ *   16-byte aligned), non-temporal 16-byte loads over a 4096-workgroup grid;
+ *   sink (16-byte aligned int32, device) is written only in a case that does
+ *   not occur in practice. Time it with events on `stream`: bytes / time.
+ * moe_calibrate_mfma_bf16: MOE_CAL_MFMA_WAVES waves each issue iters x 8
+ *   independent v_mfma_f32_32x32x16_bf16 (32768 flops each), no memory
+ *   traffic: MOE_CAL_MFMA_WAVES * iters * 8 * 32768 flops per call.
+ * Both: MOE_EINVAL on bad arguments. */
+#define MOE_CAL_MFMA_WAVES 8192
+int moe_calibrate_read(const void* buf, size_t bytes, int32_t* sink, moe_stream_t stream);
+int moe_calibrate_mfma_bf16(int32_t iters, float* sink, moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

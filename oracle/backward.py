@@ -65,3 +65,17 @@ def layer_grads(u64, e64, idx, dout64, w13, w2, w13s=(), w2s=(), experts=None):
         "dw13": {e: W13[e].grad.numpy() for e in want}, "dw2": {e: W2[e].grad.numpy() for e in want},
         "dw13s": [w.grad.numpy() for w in W13s], "dw2s": [w.grad.numpy() for w in W2s],
     }
+
+
+def expert_weight_grads(u_rows64, gate_rows64, dout_rows64, w13_64, w2_64):
+    """One routed expert's weight gradients: the rows that chose it (u [n, d]), their gates
+    g [n] and upstream gradients dout [n, d]. The expert enters out only through g * FFN(u),
+    so these equal layer_grads' dw13[e], dw2[e] (pinned against it) without the other
+    experts. Returns (dw13 [2I, d], dw2 [d, I]) fp64."""
+    u = torch.tensor(u_rows64, dtype=torch.float64)
+    W13 = torch.tensor(w13_64, dtype=torch.float64, requires_grad=True)
+    W2 = torch.tensor(w2_64, dtype=torch.float64, requires_grad=True)
+    g = torch.tensor(np.asarray(gate_rows64, dtype=np.float64))[:, None]
+    out = g * _swiglu(u, W13, W2)
+    (out * torch.tensor(dout_rows64, dtype=torch.float64)).sum().backward()
+    return W13.grad.numpy(), W2.grad.numpy()

@@ -80,3 +80,22 @@ def test_gradient_is_linear_in_dout():
     g2 = backward.layer_grads(u, E, idx, -2.5 * dout, w13, w2, w13s, w2s)
     for k in ("du", "dE"):
         assert np.allclose(g2[k], -2.5 * g1[k], rtol=1e-12, atol=1e-14)
+
+
+def test_expert_weight_grads_match_finite_differences():
+    """expert_weight_grads on the rows that chose expert e, with their gates, gives the
+    layer's dW13_e, dW2_e: checked against finite differences of the whole layer objective."""
+    u, E, idx, w13, w2, w13s, w2s, dout = _problem(5, T=9)
+    f = lambda: _objective(u, E, idx, w13, w2, w13s, w2s, dout)
+    s = routing.sigmoid(routing.logits(u, E))
+    sel = np.take_along_axis(s, idx, 1)
+    g = sel / sel.sum(axis=1, keepdims=True)
+    rng = np.random.default_rng(7)
+    for e in sorted(set(idx.reshape(-1).tolist()))[:3]:
+        rows, ks = np.nonzero(idx == e)
+        d13, d2 = backward.expert_weight_grads(u[rows], g[rows, ks], dout[rows], w13[e], w2[e])
+        for arr, gr in ((w13[e], d13), (w2[e], d2)):
+            for _ in range(5):
+                pos = tuple(int(rng.integers(0, n)) for n in arr.shape)
+                num = _fd(f, arr, pos)
+                assert abs(num - gr[pos]) <= 1e-6 * max(1.0, abs(num)), (e, pos, num, gr[pos])
