@@ -90,12 +90,13 @@ __device__ void front_mfma(const RouteArgs& a, RouterLds& sh, int t0) {
   const int ta0 = min(t0 + r16, a.T - 1), ta1 = min(t0 + 16 + r16, a.T - 1);
   const uint16_t* pa0 = u + (size_t)ta0 * a.d + kg * 8;
   const uint16_t* pa1 = u + (size_t)ta1 * a.d + kg * 8;
-  // B rows of this wave's blocks (blocks past nblk re-read block `wave`: loads stay in bounds)
+  // B rows of this wave's blocks; slots past nb (a wave with fewer blocks, or none when
+  // N_r < 64) re-read block 0, which always exists, so every load stays inside E
   const uint16_t* pb16[4];
   const float* pb32[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    const int blk = j < nb ? wave + 4 * j : wave;
+    const int blk = j < nb ? wave + 4 * j : 0;
     const size_t row = (size_t)((blk << 4) + r16) * a.d + kg * 8;
     pb16[j] = (const uint16_t*)a.E + row;
     pb32[j] = (const float*)a.E + row;
