@@ -172,3 +172,25 @@ def test_capacity_above_every_load_matches_forward():
     err = rel_l2(host(layer.out), host(plain))
     log("cap >= T: rel diff to moe_forward %.3e, bit-exact %s" % (err, torch.equal(layer.out, plain)))
     assert err <= 1e-6
+
+
+def test_forward_capacity_fp8_sampled():
+    """The FP8 V3-shape layer at capacity factor 1 (the capped forward takes the separate
+    shared-expert pass there too): mask as above, sampled outputs against oracle B (the same
+    E4M3 recipe on the CPU) with the dropped gates zeroed, at the FP8 bar."""
+    cfg = get_config("fp8")
+    layer = layer_for(cfg)
+    hw = HostWeights(cfg)
+    E = gen.centroids(cfg)
+    cap = cap_o.capacity(cfg.T, cfg.top_k, cfg.n_routed, 1.0)
+    b = dev(gen.bias_init(cfg), "f32")
+    u, b0, idx, gate, counts, out, b1, keep, nd = run_capped(layer, cfg, cap, 0, b)
+    idx_ref, gate_ref = check_routing(cfg, u, E, b0, idx, gate, counts, b1, "fp8 capped")
+    _, s64, _ = routing.route_tokens(nx.to_f64(u, cfg.in_dtype), nx.to_f64(E, cfg.router_dtype), b0, cfg)
+    used = check_keep(cfg, cap, s64, idx_ref, keep, nd, "fp8 capped")
+    dropped_t = np.nonzero(~used.all(axis=1))[0]
+    tok = np.unique(np.concatenate([_sample(cfg.T, 3, 5), dropped_t[:3]]))
+    ref = oracle_out(cfg, u, idx_ref, cap_o.dropped_gates(gate_ref, used), hw, tok, fp8=True)
+    err = rel_l2(out[tok], ref)
+    log("fp8 capped sampled", len(tok), "vs oracle B rel-L2 %.3e" % err)
+    assert err <= 1.5e-2
