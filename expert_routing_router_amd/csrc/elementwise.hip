@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       for (int i = 0; i < 8; i++) acc[i] += v[i];
     }
     for (int k = 0; k < a.K; k++) {
-      if (srow[k] < 0) continue;            // dropped selection (capacity limit)
+      // a dropped selection (capacity limit) has no row; rows outside Y are skipped too
+      if ((unsigned)srow[k] >= (unsigned)(a.T * a.K)) continue;
       float v[8];
       load8(a.y, Y_BF16, (size_t)srow[k], v);
       const float g = sg[k];

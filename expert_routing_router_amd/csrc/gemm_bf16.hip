@@ -97,7 +97,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < ACH; i++) {
     const int r = rbase + RPP * i;
-    const int rr = row0 + min(r, mvalid - 1);
+    const int rr = min(max(row0 + min(r, mvalid - 1), 0), a.rows_bound - 1);   // in range for any offsets
     const int src = a.row_index ? a.row_index[rr] : rr;
     aoff[i] = r < mvalid ? (src * K + cch * 8) * 2 : kOutOfRange;
   }
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-        if (row < mvalid) {
+        if (row < mvalid && (unsigned)(row0 + row) < (unsigned)a.rows_bound) {
           uint16_t* orow = out + (size_t)(row0 + row) * a.N;
           if (SWIGLU) {
             const int col = ntile * HN + wn * 32 + l32;
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < C::A_PER_WAVE; i++) {
     const int r = (wave + 8 * i) * C::RPB + brow;   // blocks past A_BLOCKS are never issued
-    const int rr = row0 + min(r, mvalid - 1);
+    const int rr = min(max(row0 + min(r, mvalid - 1), 0), a.rows_bound - 1);   // in range for any offsets
     const int src = a.row_index ? a.row_index[rr] : rr;
     aoff[i] = r < mvalid ? (src * K + bchunk * 8) * 2 : kOutOfRange;
   }
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-        if (row < mvalid) {
+        if (row < mvalid && (unsigned)(row0 + row) < (unsigned)a.rows_bound) {
           uint16_t* orow = out + (size_t)(row0 + row) * a.N;
           if (SWIGLU) {
             orow[ntile * HN + wn * 32 + l32] = f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));

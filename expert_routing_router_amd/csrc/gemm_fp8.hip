@@ -68,7 +68,8 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
   const float* wsc = first ? a.ws0 + (size_t)seg * a.sstride0 : a.ws1 + (size_t)(seg - a.n_first) * a.sstride1;
 
   for (int r = tid; r < BM; r += GF_THREADS)
-    srow[r] = r < mvalid ? (a.row_index ? a.row_index[row0 + r] : row0 + r) : -1;
+    srow[r] = r < mvalid && (unsigned)(row0 + r) < (unsigned)a.rows_bound
+                  ? (a.row_index ? a.row_index[row0 + r] : row0 + r) : -1;
   __syncthreads();
 
   const int cch = tid & 7, rbase = tid >> 3;
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-        if (row < mvalid) {
+        if (row < mvalid && (unsigned)(row0 + row) < (unsigned)a.rows_bound) {
           if (SWIGLU) {
             float* orow = (float*)a.out + (size_t)(row0 + row) * a.N;
             orow[ntile * 64 + wn * 32 + l32] = silu_mul(acc[i][0][r], acc[i][1][r]);
@@ -319,14 +320,14 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < C::A_PER_WAVE; i++) {
     const int r = (wave + 8 * i) * 8 + brow;
-    const int rr = row0 + min(r, mvalid - 1);
+    const int rr = min(max(row0 + min(r, mvalid - 1), 0), a.rows_bound - 1);   // in range for any offsets
     const int src = a.row_index ? a.row_index[rr] : rr;
     aoff[i] = r < mvalid ? src * K + bchunk * 16 : kOutOfRange;
   }
   int soff_row;
   {
     const int r = (wave < C::SA_WAVES ? wave : 0) * 64 + lane;
-    const int rr = row0 + min(r, mvalid - 1);
+    const int rr = min(max(row0 + min(r, mvalid - 1), 0), a.rows_bound - 1);   // in range for any offsets
     const int src = a.row_index ? a.row_index[rr] : rr;
     soff_row = r < mvalid ? src * KB * 4 : kOutOfRange;
   }
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-        if (row < mvalid) {
+        if (row < mvalid && (unsigned)(row0 + row) < (unsigned)a.rows_bound) {
           if (SWIGLU) {
             float* orow = (float*)a.out + (size_t)(row0 + row) * a.N;
             orow[ntile * HN + wn * 32 + l32] = silu_mul(acc[i][0][r], acc[i][1][r]);

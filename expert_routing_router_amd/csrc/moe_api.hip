@@ -289,7 +289,8 @@ extern "C" int moe_permute(const moe_desc_t* d, const int32_t* topk_idx, int32_t
   p.n_extra_seg = 0; p.mtile_prefix = nullptr; p.bm = 0;
   MOE_TRY(launch_permute(p, s));
   if (x_perm)
-    MOE_TRY(launch_gather_rows(u, row_token, x_perm, (long)d->T * d->top_k, d->d * (int)esize(d->in_dtype), s));
+    MOE_TRY(launch_gather_rows(u, d->T, row_token, offsets + d->n_routed, x_perm, (long)d->T * d->top_k,
+                               d->d * (int)esize(d->in_dtype), s));
   return MOE_OK;
 }
 

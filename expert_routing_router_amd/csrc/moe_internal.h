@@ -46,8 +46,8 @@ hipError_t launch_cal_mfma(int iters, float* sink, hipStream_t s);
 hipError_t launch_capacity(const int32_t* offsets, const int32_t* row_token, const int32_t* idx,
                            const float* scores, int T, int N, int K, int cap, int32_t* keep, int32_t* dropped,
                            hipStream_t s);
-hipError_t launch_gather_rows(const void* src, const int32_t* row_token, void* dst,
-                              long rows, int row_bytes, hipStream_t s);
+hipError_t launch_gather_rows(const void* src, long src_rows, const int32_t* row_token, const int32_t* n_valid,
+                              void* dst, long rows, int row_bytes, hipStream_t s);
 hipError_t launch_mtile_prefix(const int32_t* offsets, int n_seg, int bm, int32_t* out,
                                hipStream_t s);
 

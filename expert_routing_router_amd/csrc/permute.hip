@@ -30,9 +30,12 @@ __global__ __launch_bounds__(256) void bitmap_kernel(const int32_t* __restrict__
   const int w = blockIdx.x * 4 + wave;
   const int t = w * 64 + lane;
   if (t < T)
-    for (int k = 0; k < K; k++)
-      if (!keep || keep[(size_t)t * K + k])
-        atomicOr((unsigned long long*)&words[wave][idx[(size_t)t * K + k]], 1ull << lane);
+    for (int k = 0; k < K; k++) {
+      const int e = idx[(size_t)t * K + k];
+      // an expert id outside [0, N) gets no row (as a dropped selection)
+      if ((unsigned)e < (unsigned)N && (!keep || keep[(size_t)t * K + k]))
+        atomicOr((unsigned long long*)&words[wave][e], 1ull << lane);
+    }
   __syncthreads();
   const int W = cdiv(T, 64);
   if (w < W)
@@ -127,8 +130,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   const long TK = (long)T * K;
   const long total = TK + (long)n_extra * T;
   for (long p = (long)blockIdx.x * blockDim.x + threadIdx.x; p < total; p += (long)gridDim.x * blockDim.x) {
-    if (p < TK && keep && !keep[p]) {
-      slot_row[p] = -1;                     // dropped selection: no row
+    if (p < TK && ((keep && !keep[p]) || (unsigned)idx[p] >= (unsigned)N)) {
+      slot_row[p] = -1;                     // dropped selection (or an id outside [0, N)): no row
     } else if (p < TK) {
       const int t = (int)(p / K);
       const int e = idx[p];
@@ -156,11 +159,16 @@ __global__ void mtile_prefix_kernel(const int32_t* __restrict__ offsets, int n_s
   }
 }
 
-__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ src,
+// rows r < *n_valid only (the rows the dispatch wrote), and only source rows inside src
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ src, long src_rows,
                                                           const int32_t* __restrict__ row_token,
+                                                          const int32_t* __restrict__ n_valid,
                                                           uint8_t* __restrict__ dst, int row_bytes) {
   const long r = blockIdx.x;
-  const uint8_t* s = src + (size_t)row_token[r] * row_bytes;
+  if (r >= *n_valid) return;
+  const int t = row_token[r];
+  if ((unsigned long)t >= (unsigned long)src_rows) return;
+  const uint8_t* s = src + (size_t)t * row_bytes;
   uint8_t* d = dst + (size_t)r * row_bytes;
   for (int c = threadIdx.x * 16; c < row_bytes; c += blockDim.x * 16)
     *(i32x4*)(d + c) = *(const i32x4*)(s + c);
@@ -183,10 +191,11 @@ hipError_t launch_mtile_prefix(const int32_t* offsets, int n_seg, int bm, int32_
   return hipGetLastError();
 }
 
-hipError_t launch_gather_rows(const void* src, const int32_t* row_token, void* dst, long rows,
-                              int row_bytes, hipStream_t s) {
+hipError_t launch_gather_rows(const void* src, long src_rows, const int32_t* row_token, const int32_t* n_valid,
+                              void* dst, long rows, int row_bytes, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  gather_rows_kernel<<<(unsigned)rows, 256, 0, s>>>((const uint8_t*)src, row_token, (uint8_t*)dst, row_bytes);
+  gather_rows_kernel<<<(unsigned)rows, 256, 0, s>>>((const uint8_t*)src, src_rows, row_token, n_valid,
+                                                    (uint8_t*)dst, row_bytes);
   return hipGetLastError();
 }
 

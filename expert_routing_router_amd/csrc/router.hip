@@ -224,11 +224,13 @@ __device__ void select_tokens(const RouteArgs& a, RouterLdsT<BT>& sh, int t0, in
   const int S = N / G;
   for (int t = wave; t < nt; t += RT_THREADS / kWave) {
     const float* srow = sh.s[t];
-    uint32_t ok[4];                       // ordered keys; 0 = not a candidate
+    // ordered keys; 0 = not a candidate. A candidate's key is at least 1 (only one NaN bit
+    // pattern orders to 0), so K rounds always find K distinct experts in range.
+    uint32_t ok[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int e = lane + 64 * j;
-      ok[j] = e < N ? ordered_f32(srow[e] + sh.b[e]) : 0u;
+      ok[j] = e < N ? max(ordered_f32(srow[e] + sh.b[e]), 1u) : 0u;
     }
     if (G > 1) {
       uint32_t gk = 0u;
@@ -248,7 +250,7 @@ __device__ void select_tokens(const RouteArgs& a, RouterLdsT<BT>& sh, int t0, in
 #pragma unroll
         for (int j = 1; j < RT_QMAX; j++)
           if (j < q) acc = acc + top[j];                    // fp32, largest first
-        gk = ordered_f32(acc);
+        gk = max(ordered_f32(acc), 1u);
       }
       uint64_t chosen = 0ull;
       for (int m = 0; m < M; m++) {

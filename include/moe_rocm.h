@@ -136,7 +136,9 @@ int moe_route(const moe_desc_t* desc, const void* u, const void* E, const float*
  *   slot_row [T*K]: permuted row of (t, topk_idx[t,k]) at index t*K+k.
  *   counts [N_r], nullable: loads recomputed from topk_idx.
  *   u [T,d] and x_perm [T*K,d] (in_dtype), nullable together: gathered rows.
- *   ws: at least moe_workspace_bytes(desc) bytes. */
+ *   ws: at least moe_workspace_bytes(desc) bytes.
+ * An expert id outside [0, N_r) in topk_idx gets no row: its slot_row is -1,
+ * it is not counted, and the rows it would have had are not written. */
 int moe_permute(const moe_desc_t* desc, const int32_t* topk_idx, int32_t* offsets,
                 int32_t* row_token, int32_t* slot_row, int32_t* counts,
                 const void* u, void* x_perm, void* ws, size_t ws_bytes,
@@ -152,7 +154,9 @@ int moe_permute(const moe_desc_t* desc, const int32_t* topk_idx, int32_t* offset
  *   w13 [n_experts, 2*inter, d], w2 [n_experts, d, inter] expert_dtype; FP8
  *      scales w13_scale/w2_scale as in moe_weights_t.
  *   y [rows, d]: fp32 for F32 experts, bf16 otherwise.
- *   ws: at least moe_expert_ffn_workspace_bytes(...) bytes. */
+ *   ws: at least moe_expert_ffn_workspace_bytes(...) bytes.
+ * offsets must be non-decreasing with offsets[0] >= 0 and offsets[n_experts]
+ * <= rows (the kernels keep every row index they form inside [0, rows)). */
 size_t moe_expert_ffn_workspace_bytes(const moe_desc_t* desc, int32_t n_experts,
                                       int32_t inter, int32_t rows);
 int moe_expert_ffn(const moe_desc_t* desc, int32_t n_experts, int32_t inter, int32_t rows,
@@ -164,7 +168,8 @@ int moe_expert_ffn(const moe_desc_t* desc, int32_t n_experts, int32_t inter, int
 /* Combine: out_t = u_t + sum_s y_shared[s,t] + sum_k gate[t,k] * y[slot_row[t*K+k]]
  * accumulated in fp32 in that fixed order (output equation; the pwwt.cn
  * note's section 4 combine).  u, out [T,d] in_dtype; y [T*K,d] and
- * y_shared [N_s,T,d] (nullable when N_s = 0) fp32 for F32 experts, bf16 otherwise. */
+ * y_shared [N_s,T,d] (nullable when N_s = 0) fp32 for F32 experts, bf16 otherwise.
+ * A slot_row entry outside [0, T*K) (-1 for a dropped selection) adds nothing. */
 int moe_combine(const moe_desc_t* desc, const void* u, const void* y, const void* y_shared,
                 const int32_t* slot_row, const float* topk_gate, void* out,
                 moe_stream_t stream);

@@ -86,3 +86,59 @@ def test_bias_update_bit_exact():
         torch.cuda.synchronize()
         want = routing.bias_step(counts, b, T, K, 0.001)
         assert np.array_equal(host(bd).view(np.uint32), want.view(np.uint32))
+
+
+def test_permute_ignores_expert_ids_out_of_range():
+    """Entries of topk_idx outside [0, N) get no row (slot_row -1, not counted, not gathered); the
+    layout of the rest is the oracle's layout with those entries moved to an extra last expert."""
+    T, N, K = 777, 64, 6
+    rng = np.random.default_rng(21)
+    idx = _idx_random(rng, T, N, K)
+    bad = rng.random((T, K)) < 0.05
+    idx[bad] = rng.choice([-1, N, N + 7, -(1 << 30)], int(bad.sum()))
+    desc = M.make_desc(T=T, d=256, n_routed=N, top_k=K, n_shared=0, inter=128)
+    ws = torch.empty(M.moe_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    offsets = torch.empty(N + 1, dtype=torch.int32, device="cuda")
+    row_token = torch.full((T * K,), -5, dtype=torch.int32, device="cuda")
+    slot_row = torch.empty(T * K, dtype=torch.int32, device="cuda")
+    counts = torch.empty(N, dtype=torch.int32, device="cuda")
+    u = torch.randn((T, 256), device="cuda").to(torch.bfloat16)
+    x_perm = torch.zeros((T * K, 256), dtype=torch.bfloat16, device="cuda")
+    M.moe_permute(desc, dev(idx, "i32"), offsets, row_token, slot_row, ws, counts=counts, u=u, x_perm=x_perm)
+    torch.cuda.synchronize()
+    moved = np.where(bad, N, idx)
+    o, rt, sr = permute.layout_fast(moved, N + 1)
+    total = int(o[N])
+    log("permute with %d ids out of range: %d rows" % (int(bad.sum()), total))
+    assert total == T * K - int(bad.sum())
+    assert np.array_equal(host(offsets), o[:N + 1])
+    assert np.array_equal(host(row_token)[:total], rt[:total])
+    assert np.array_equal(host(slot_row), np.where(bad.reshape(-1), -1, sr))
+    assert np.array_equal(host(counts), np.bincount(idx[~bad], minlength=N))
+    assert torch.equal(x_perm[:total], u[row_token[:total].long()])
+    assert not x_perm[total:].float().abs().sum().item()
+
+
+def test_combine_skips_rows_out_of_range():
+    """slot_row entries of -1 (a dropped selection) or outside [0, T*K) add nothing."""
+    T, d, K, Ns = 129, 512, 4, 1
+    rng = np.random.default_rng(22)
+    R = T * K
+    u = nx.bf16_round_f64(rng.standard_normal((T, d))).astype(np.float32)
+    y = nx.bf16_round_f64(rng.standard_normal((R, d))).astype(np.float32)
+    ys = nx.bf16_round_f64(rng.standard_normal((Ns, T, d))).astype(np.float32)
+    slot = rng.permutation(R).astype(np.int32)
+    bad = rng.random(R) < 0.1
+    slot[bad] = rng.choice([-1, R, R + 100, -(1 << 30)], int(bad.sum()))
+    gate = rng.uniform(0, 1, (T, K)).astype(np.float32)
+    desc = M.make_desc(T=T, d=d, n_routed=16, top_k=K, n_shared=Ns, inter=128)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    M.moe_combine(desc, torch.from_numpy(u).to("cuda", torch.bfloat16), torch.from_numpy(y).to("cuda", torch.bfloat16),
+                  dev(slot, "i32"), dev(gate, "f32"), out, y_shared=torch.from_numpy(ys).to("cuda", torch.bfloat16))
+    torch.cuda.synchronize()
+    g = np.where(bad.reshape(T, K), 0.0, gate.astype(np.float64))
+    ref = u.astype(np.float64) + ys[0].astype(np.float64)
+    ref = ref + np.einsum("tk,tkd->td", g, y.astype(np.float64)[np.where(bad, 0, slot).reshape(T, K)])
+    err = rel_l2(host(out), ref)
+    log("combine with %d slots out of range: rel-L2 %.2e" % (int(bad.sum()), err))
+    assert err < 3e-3
