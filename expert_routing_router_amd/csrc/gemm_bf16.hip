@@ -243,7 +243,10 @@ struct DmaCfg {
   static constexpr int RPB = 1024 / RB;
   static constexpr int SH = RB == 64 ? 2 : 1;
   static constexpr int SUB = RB / 32;                   // 16-element k-substeps per stage
-  static constexpr int STAGES = RB == 64 ? 4 : 2;
+  // as many K=32 stages as the LDS holds (up to 7: small-row tiles keep more weight bytes in flight)
+  static constexpr int STAGES = RB == 64 ? ((160 * 1024 - 2048) / ((BM + BN) * RB) < 7
+                                                ? (160 * 1024 - 2048) / ((BM + BN) * RB) : 7)
+                                         : 2;
   static constexpr int A_BLOCKS = BM / RPB;             // 1 KB blocks per stage
   static constexpr int B_BLOCKS = BN / RPB;
   static constexpr int A_BYTES = BM * RB;
@@ -431,7 +434,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
   switch (__builtin_amdgcn_readfirstlane(mb_active)) {
     case 0: k_loop(std::integral_constant<int, 0>{}); break;
     case 1: k_loop(std::integral_constant<int, 1>{}); break;
-    case 2: k_loop(std::integral_constant<int, 2>{}); break;
+    case 2: k_loop(std::integral_constant<int, (MB >= 2 ? 2 : MB)>{}); break;
     case 3: k_loop(std::integral_constant<int, (MB >= 3 ? 3 : MB)>{}); break;
     case 4: k_loop(std::integral_constant<int, (MB >= 4 ? 4 : MB)>{}); break;
     default: k_loop(std::integral_constant<int, MB>{}); break;
@@ -499,12 +502,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   }
 }
 
-int gemm_bm(int dtype, int mean_rows, int dmodel) {
+int gemm_bm(int dtype, int mean_rows, int dmodel, int inter) {
   // FP8: 256-row tiles of the LDS-DMA kernel when the down GEMM's width is a
   // multiple of its 256-row weight tile, else the register-staged 192-row kernel.
   if (dtype == MOE_FP8_E4M3) return dmodel % 256 == 0 ? 256 : 192;
-  // one m-tile per expert when the mean load (+4 sigma of a binomial load) fits
+  // one m-tile per expert when the mean load (+4 sigma of a binomial load) fits;
+  // 64- and 128-row tiles (deeper load ring) for small loads when every product's
+  // width suits the LDS-DMA kernel
   const int need = mean_rows + 4 * (int)std::sqrt((double)(mean_rows > 0 ? mean_rows : 1));
+  const bool dma_all = dmodel % 256 == 0 && inter % 256 == 0;
+  if (dma_all && need <= 64) return 64;
+  if (dma_all && need <= 128) return 128;
   if (need <= 256) return 256;
   return 320;
 }
@@ -553,6 +561,8 @@ static hipError_t launch_any(const GemmArgs& a, int dtype, int bm, hipStream_t s
     // 256 weight rows per tile (8 waves) when the output width allows it,
     // else 128 (4 waves)
     const bool wide = SWIGLU ? a.N % 128 == 0 : a.N % 256 == 0;
+    if (bm == 64) return wide ? launch_bf16_dma<1, SWIGLU>(a, s) : hipErrorInvalidValue;
+    if (bm == 128) return wide ? launch_bf16_dma<2, SWIGLU>(a, s) : hipErrorInvalidValue;
     if (bm == 256) return wide ? launch_bf16_dma<4, SWIGLU>(a, s) : launch_bf16<4, 2, SWIGLU>(a, s);
     if (bm == 320) return wide ? launch_bf16_dma<5, SWIGLU>(a, s) : launch_bf16<5, 2, SWIGLU>(a, s);
     return hipErrorInvalidValue;

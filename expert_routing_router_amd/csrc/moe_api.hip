@@ -363,7 +363,7 @@ extern "C" int moe_expert_ffn(const moe_desc_t* d, int32_t n_experts, int32_t in
   uint8_t* qh = f8 ? base + o : nullptr;
   if (f8) o += al256((size_t)rows * inter);
   float* sh = f8 ? (float*)(base + o) : nullptr;
-  const int bm = gemm_bm(d->expert_dtype, rows / n_experts, d->d);
+  const int bm = gemm_bm(d->expert_dtype, rows / n_experts, d->d, inter);
   if (d->expert_dtype != MOE_F32) MOE_TRY(launch_mtile_prefix(offsets, n_experts, bm, mtile, s));
   return run_ffn(d, inter, x, row_token ? (long)d->T : (long)rows, x_scale, row_token, offsets, mtile, n_experts,
                  rows, w13, w13_scale, w13,
@@ -470,7 +470,7 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
 
   // 2. dispatch layout; shared experts become extra identity segments
   const long TK = (long)T * K;
-  const int bm = gemm_bm(d->expert_dtype, (int)(TK / N), d->d);
+  const int bm = gemm_bm(d->expert_dtype, (int)(TK / N), d->d, d->inter);
   PermuteArgs p;
   p.idx = idx; p.T = T; p.K = K; p.n_routed = N;
   p.bitmap = (uint64_t*)(base + L.bitmap); p.wprefix = (int32_t*)(base + L.wprefix);
@@ -526,7 +526,7 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
     int32_t* mtile_s = (int32_t*)(base + L.mtile_s);
     iota_kernel<<<cdiv(Ns + 1, 64), 64, 0, s>>>(offs_s, Ns, T);
     MOE_TRY(hipGetLastError());
-    const int bms = gemm_bm(d->expert_dtype, T, d->d);
+    const int bms = gemm_bm(d->expert_dtype, T, d->d, d->inter_shared);
     if (d->expert_dtype != MOE_F32) MOE_TRY(launch_mtile_prefix(offs_s, Ns, bms, mtile_s, s));
     uint8_t* Hs = H + (size_t)TK * (d->inter > d->inter_shared ? d->inter : d->inter_shared) * hy;
     uint8_t* Ys = Y + (size_t)TK * d->d * yy;
@@ -726,7 +726,7 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
   // router gives bit-identical affinities and selections), then A|B, H, Y
   RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, scores, idx, gate, counts);
   MOE_TRY(launch_route(ra, route_front(d), s));
-  const int bm = gemm_bm(d->expert_dtype, (int)(TK / N), d->d);
+  const int bm = gemm_bm(d->expert_dtype, (int)(TK / N), d->d, d->inter);
   PermuteArgs p;
   p.idx = idx; p.T = T; p.K = K; p.n_routed = N;
   p.bitmap = (uint64_t*)(base + L.bitmap); p.wprefix = (int32_t*)(base + L.wprefix);

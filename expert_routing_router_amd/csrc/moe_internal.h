@@ -69,7 +69,7 @@ struct GemmArgs {
   int K;                      // reduction length
   int rows_bound;             // upper bound on total rows (grid sizing)
 };
-int gemm_bm(int dtype, int mean_rows, int dmodel);
+int gemm_bm(int dtype, int mean_rows, int dmodel, int inter);
 hipError_t launch_gemm_swiglu(const GemmArgs& a, int dtype, int bm, hipStream_t s);
 hipError_t launch_gemm_down(const GemmArgs& a, int dtype, int bm, hipStream_t s);
 

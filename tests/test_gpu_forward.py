@@ -147,6 +147,24 @@ def test_forward_steps_sampled(name, steps, sampled):
             assert err <= 1e-2 and err_ffn <= 1.5e-2
 
 
+@pytest.mark.parametrize("T", [2048, 512, 96])
+def test_forward_small_batches_v3_weights(T):
+    """V3 weights at small batches: 8, 16 and 64 mean rows per expert run the 64- and 128-row
+    tiles of the grouped GEMM (deeper load ring); sampled tokens against the oracle."""
+    cfg = get_config("v3").with_(T=T)
+    layer = layer_for(cfg)
+    hw = HostWeights(cfg)
+    b = dev(gen.bias_init(cfg), "f32")
+    u, b0, idx, gate, counts, out, b1 = run_step(layer, cfg, 0, b)
+    idx_ref, gate_ref = check_routing(cfg, u, gen.centroids(cfg), b0, idx, gate, counts, b1, "v3 T=%d" % T)
+    tok = _sample(cfg.T, 6, T)
+    ref = oracle_out(cfg, u, idx_ref, gate_ref, hw, tok)
+    u64 = nx.to_f64(u[tok], cfg.in_dtype)
+    err, err_ffn = rel_l2(out[tok], ref), rel_l2(out[tok] - u64, ref - u64)
+    log("v3 T=%d sampled %d rel-L2 %.3e (FFN part %.3e)" % (T, len(tok), err, err_ffn))
+    assert err <= 1e-2 and err_ffn <= 1.5e-2
+
+
 def test_forward_fp8_sampled():
     cfg = get_config("fp8")
     layer = layer_for(cfg)
