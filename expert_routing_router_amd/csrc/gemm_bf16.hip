@@ -222,12 +222,13 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs a) {
 // ---------------------------------------------------------------- LDS-DMA path
 // Same tile and wave layout as gemm_bf16_kernel<MB, 4, ...> (8 waves, 64*MB x
 // 256 weight rows), but operands go from global memory straight into LDS with
-// buffer loads that write LDS (no register staging), through a ring of four
-// K=32 stages: three stages are in flight while one is multiplied, so each
-// CU keeps ~108 KB of loads outstanding instead of one K step's worth.
+// buffer loads that write LDS (no register staging), through a ring of K=32
+// stages, as many as the LDS holds (4 for 256- and 320-row tiles, 6 and 7 for
+// 128- and 64-row tiles): all but one are in flight while one is multiplied,
+// so each CU keeps ~108 KB of loads outstanding instead of one K step's worth.
 //
-// A stage holds RB bytes per row (RB = 64: four K=32 stages; RB = 128: two
-// K=64 stages), CPR = RB/16 chunks of 16 bytes. One load instruction of a
+// A stage holds RB bytes per row (RB = 64: K=32 stages; RB = 128: two K=64
+// stages, kept as an alternative), CPR = RB/16 chunks of 16 bytes. One load instruction of a
 // wave fills one 1 KB block of RPB = 1024/RB rows; lane l writes block byte
 // 16*l, i.e. row l/CPR, slot l%CPR, and fetches the chunk
 // c = slot ^ ((row >> SH) & (CPR-1)), SH = log2(16/CPR). The MFMA operand
