@@ -37,65 +37,88 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* p, const float* v) {
   for (int i = 0; i < 4; i++) q[i] = (int)pack_bf16x2(v[2 * i], v[2 * i + 1]);
   *(i32x4*)p = q;
 }
+// 8 consecutive elements of a bf16 (F32 = false) or fp32 array, as fp32
+template <bool F32>
+__device__ __forceinline__ void ld8(const void* p, size_t i, float* v) {
+  if constexpr (F32) {
+    const f32x4 a = *(const f32x4*)((const float*)p + i), b = *(const f32x4*)((const float*)p + i + 4);
+#pragma unroll
+    for (int k = 0; k < 4; k++) { v[k] = a[k]; v[4 + k] = b[k]; }
+  } else {
+    load_bf16x8((const uint16_t*)p + i, v);
+  }
+}
+template <bool F32>
+__device__ __forceinline__ void st8(void* p, size_t i, const float* v) {
+  if constexpr (F32) {
+    *(f32x4*)((float*)p + i) = f32x4{v[0], v[1], v[2], v[3]};
+    *(f32x4*)((float*)p + i + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    store_bf16x8((uint16_t*)p + i, v);
+  }
+}
 __device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
 
-// H = SiLU(A) * B from AB = [A | B] (rows of 2I), bf16 in and out, fp32 math
-__global__ void swiglu_fwd_kernel(const uint16_t* __restrict__ ab, uint16_t* __restrict__ h, long rows, int I) {
+// H = SiLU(A) * B from AB = [A | B] (rows of 2I), bf16 (or fp32) in and out, fp32 math
+template <bool F32>
+__global__ void swiglu_fwd_kernel(const void* __restrict__ ab, void* __restrict__ h, long rows, int I) {
   const long n8 = rows * (I / 8);
   for (long p = (long)blockIdx.x * blockDim.x + threadIdx.x; p < n8; p += (long)gridDim.x * blockDim.x) {
     const long r = p / (I / 8);
     const int c = (int)(p - r * (I / 8)) * 8;
     float a[8], b[8], o[8];
-    load_bf16x8(ab + r * 2 * I + c, a);
-    load_bf16x8(ab + r * 2 * I + I + c, b);
+    ld8<F32>(ab, r * 2 * I + c, a);
+    ld8<F32>(ab, r * 2 * I + I + c, b);
 #pragma unroll
     for (int i = 0; i < 8; i++) o[i] = a[i] * sigmoidf_(a[i]) * b[i];
-    store_bf16x8(h + r * I + c, o);
+    st8<F32>(h, r * I + c, o);
   }
 }
 
 // dA, dB from dH and AB: dA = dH * B * sig(A) * (1 + A (1 - sig(A))), dB = dH * SiLU(A)
-__global__ void swiglu_bwd_kernel(const uint16_t* __restrict__ dh, const uint16_t* __restrict__ ab,
-                                  uint16_t* __restrict__ dab, long rows, int I) {
+template <bool F32>
+__global__ void swiglu_bwd_kernel(const void* __restrict__ dh, const void* __restrict__ ab,
+                                  void* __restrict__ dab, long rows, int I) {
   const long n8 = rows * (I / 8);
   for (long p = (long)blockIdx.x * blockDim.x + threadIdx.x; p < n8; p += (long)gridDim.x * blockDim.x) {
     const long r = p / (I / 8);
     const int c = (int)(p - r * (I / 8)) * 8;
     float a[8], b[8], g[8], da[8], db[8];
-    load_bf16x8(ab + r * 2 * I + c, a);
-    load_bf16x8(ab + r * 2 * I + I + c, b);
-    load_bf16x8(dh + r * I + c, g);
+    ld8<F32>(ab, r * 2 * I + c, a);
+    ld8<F32>(ab, r * 2 * I + I + c, b);
+    ld8<F32>(dh, r * I + c, g);
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const float sg = sigmoidf_(a[i]);
       da[i] = g[i] * b[i] * sg * (1.0f + a[i] * (1.0f - sg));
       db[i] = g[i] * a[i] * sg;
     }
-    store_bf16x8(dab + r * 2 * I + c, da);
-    store_bf16x8(dab + r * 2 * I + I + c, db);
+    st8<F32>(dab, r * 2 * I + c, da);
+    st8<F32>(dab, r * 2 * I + I + c, db);
   }
 }
 
 // One workgroup per token: the K gate gradients dg = <dout_t, Y_{t,k}> (fp32),
 // and the rows of dY: g * dout for its routed rows, dout for its shared rows.
-__global__ __launch_bounds__(256) void dgate_dy_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict__ y,
+template <bool F32>
+__global__ __launch_bounds__(256) void dgate_dy_kernel(const void* __restrict__ dout, const void* __restrict__ y,
                                                        const int32_t* __restrict__ slot_row, const float* __restrict__ gate,
                                                        int d, int K, int n_shared, long shared_base, long shared_stride,
-                                                       float* __restrict__ dg, uint16_t* __restrict__ dy) {
+                                                       float* __restrict__ dg, void* __restrict__ dy) {
   __shared__ float red[64][4];
   const int t = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint16_t* drow = dout + (size_t)t * d;
+  const size_t drow = (size_t)t * d;
   for (int k = 0; k < K; k++) {
     const long row = slot_row[(size_t)t * K + k];
     const float g = gate[(size_t)t * K + k];
     float acc = 0.f;
     for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
       float a[8], b[8], o[8];
-      load_bf16x8(drow + c, a);
-      load_bf16x8(y + row * d + c, b);
+      ld8<F32>(dout, drow + c, a);
+      ld8<F32>(y, row * d + c, b);
 #pragma unroll
       for (int i = 0; i < 8; i++) { acc = fmaf(a[i], b[i], acc); o[i] = g * a[i]; }
-      store_bf16x8(dy + row * d + c, o);
+      st8<F32>(dy, row * d + c, o);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -103,8 +126,11 @@ __global__ __launch_bounds__(256) void dgate_dy_kernel(const uint16_t* __restric
   }
   for (int s = 0; s < n_shared; s++) {
     const long row = shared_base + (long)s * shared_stride + t;
-    for (int c = threadIdx.x * 8; c < d; c += 256 * 8)
-      *(i32x4*)(dy + row * d + c) = *(const i32x4*)(drow + c);
+    for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+      float a[8];
+      ld8<F32>(dout, drow + c, a);
+      st8<F32>(dy, row * d + c, a);
+    }
   }
   __syncthreads();
   if (threadIdx.x < K) {
@@ -133,8 +159,8 @@ __global__ void dz_kernel(const float* __restrict__ scores, const int32_t* __res
 }
 
 // One workgroup per token: du_t = dout_t + sum_s dX_s,t + sum_k dX_{t,k} + sum_k dz_{t,k} e_{idx_k}
-template <bool E_BF16>
-__global__ __launch_bounds__(256) void du_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict__ dx,
+template <bool E_BF16, bool F32>
+__global__ __launch_bounds__(256) void du_kernel(const void* __restrict__ dout, const void* __restrict__ dx,
                                                  const int32_t* __restrict__ slot_row, const int32_t* __restrict__ idx,
                                                  const float* __restrict__ dz, const void* __restrict__ E, int d, int K,
                                                  int n_shared, long shared_base, long shared_stride,
@@ -142,14 +168,14 @@ __global__ __launch_bounds__(256) void du_kernel(const uint16_t* __restrict__ do
   const int t = blockIdx.x;
   for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
     float acc[8], v[8];
-    load_bf16x8(dout + (size_t)t * d + c, acc);
+    ld8<F32>(dout, (size_t)t * d + c, acc);
     for (int s = 0; s < n_shared; s++) {
-      load_bf16x8(dx + (shared_base + (long)s * shared_stride + t) * d + c, v);
+      ld8<F32>(dx, (shared_base + (long)s * shared_stride + t) * d + c, v);
 #pragma unroll
       for (int i = 0; i < 8; i++) acc[i] += v[i];
     }
     for (int k = 0; k < K; k++) {
-      load_bf16x8(dx + (size_t)slot_row[(size_t)t * K + k] * d + c, v);
+      ld8<F32>(dx, (size_t)slot_row[(size_t)t * K + k] * d + c, v);
 #pragma unroll
       for (int i = 0; i < 8; i++) acc[i] += v[i];
     }
@@ -173,7 +199,8 @@ __global__ __launch_bounds__(256) void du_kernel(const uint16_t* __restrict__ do
 
 // grid (N_r, ceil(d/2048)): dE_i = sum over expert i's rows (ascending token)
 // of dz_{t,k} u_t, fp32; k is where i sits in the token's selection.
-__global__ __launch_bounds__(256) void de_kernel(const uint16_t* __restrict__ u, const int32_t* __restrict__ offsets,
+template <bool F32>
+__global__ __launch_bounds__(256) void de_kernel(const void* __restrict__ u, const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ row_token, const int32_t* __restrict__ idx,
                                                  const float* __restrict__ dz, int d, int K, float* __restrict__ dE) {
   const int i = blockIdx.x;
@@ -186,7 +213,7 @@ __global__ __launch_bounds__(256) void de_kernel(const uint16_t* __restrict__ u,
     while (k < K - 1 && idx[(size_t)t * K + k] != i) k++;
     const float z = dz[(size_t)t * K + k];
     float v[8];
-    load_bf16x8(u + (size_t)t * d + c, v);
+    ld8<F32>(u, (size_t)t * d + c, v);
 #pragma unroll
     for (int j = 0; j < 8; j++) acc[j] = fmaf(z, v[j], acc[j]);
   }
@@ -533,11 +560,32 @@ static hipError_t launch_wgrad_dma(const WgradArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// fp32 layers (the small fp32 configuration): C_e[m][n] = sum over segment e's rows r of
+// P[r][m] * Q[q(r)][n] with plain fp32 FMAs in row order, one thread per element of C.
+// grid (ceil(Nn/64), ceil(M/4), n_seg), 256 threads: 4 rows of C x 64 columns.
+__global__ __launch_bounds__(256) void wgrad_f32_kernel(const float* __restrict__ P, const float* __restrict__ Q,
+                                                        const int32_t* __restrict__ q_row,
+                                                        const int32_t* __restrict__ offsets, int M, int Nn,
+                                                        float* __restrict__ out0, float* __restrict__ out1,
+                                                        long ostride0, long ostride1, int n_first) {
+  const int seg = blockIdx.z;
+  const int m = blockIdx.y * 4 + (threadIdx.x >> 6), n = blockIdx.x * 64 + (threadIdx.x & 63);
+  if (m >= M || n >= Nn) return;
+  float acc = 0.f;
+  for (int r = offsets[seg]; r < offsets[seg + 1]; r++) {
+    const long qr = q_row ? q_row[r] : r;
+    acc = fmaf(P[(size_t)r * M + m], Q[(size_t)qr * Nn + n], acc);
+  }
+  float* out = seg < n_first ? out0 + (size_t)seg * ostride0 : out1 + (size_t)(seg - n_first) * ostride1;
+  out[(size_t)m * Nn + n] = acc;
+}
+
 // ---------------------------------------------------------------- transposes
-// dst[b][c][r] = src[b][r][c] for bf16 [batch][rows][cols], 64x64 tiles via LDS
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
-                                                             int rows, int cols) {
-  __shared__ uint16_t tile[64][65];
+// dst[b][c][r] = src[b][r][c] for [batch][rows][cols] of 2- or 4-byte elements, 64x64 tiles via LDS
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                        int rows, int cols) {
+  __shared__ T tile[64][65];
   const size_t base = (size_t)blockIdx.z * rows * cols;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
@@ -556,25 +604,29 @@ static dim3 grid_1d(long n, int per_block) {
   return dim3((unsigned)std::min<long>(cdiv<long>(n, per_block), 8192));
 }
 
-hipError_t launch_swiglu_fwd(const void* ab, void* h, long rows, int I, hipStream_t s) {
+hipError_t launch_swiglu_fwd(const void* ab, void* h, long rows, int I, int dtype, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  swiglu_fwd_kernel<<<grid_1d(rows * (I / 8), 256), 256, 0, s>>>((const uint16_t*)ab, (uint16_t*)h, rows, I);
+  if (dtype == MOE_F32) swiglu_fwd_kernel<true><<<grid_1d(rows * (I / 8), 256), 256, 0, s>>>(ab, h, rows, I);
+  else swiglu_fwd_kernel<false><<<grid_1d(rows * (I / 8), 256), 256, 0, s>>>(ab, h, rows, I);
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd(const void* dh, const void* ab, void* dab, long rows, int I, hipStream_t s) {
+hipError_t launch_swiglu_bwd(const void* dh, const void* ab, void* dab, long rows, int I, int dtype, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  swiglu_bwd_kernel<<<grid_1d(rows * (I / 8), 256), 256, 0, s>>>((const uint16_t*)dh, (const uint16_t*)ab,
-                                                                  (uint16_t*)dab, rows, I);
+  if (dtype == MOE_F32) swiglu_bwd_kernel<true><<<grid_1d(rows * (I / 8), 256), 256, 0, s>>>(dh, ab, dab, rows, I);
+  else swiglu_bwd_kernel<false><<<grid_1d(rows * (I / 8), 256), 256, 0, s>>>(dh, ab, dab, rows, I);
   return hipGetLastError();
 }
 
 hipError_t launch_dgate_dy(const void* dout, const void* y, const int32_t* slot_row, const float* gate, int T, int d,
-                           int K, int n_shared, long shared_base, long shared_stride, float* dg, void* dy,
+                           int K, int n_shared, long shared_base, long shared_stride, float* dg, void* dy, int dtype,
                            hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  dgate_dy_kernel<<<T, 256, 0, s>>>((const uint16_t*)dout, (const uint16_t*)y, slot_row, gate, d, K, n_shared,
-                                    shared_base, shared_stride, dg, (uint16_t*)dy);
+  if (dtype == MOE_F32)
+    dgate_dy_kernel<true><<<T, 256, 0, s>>>(dout, y, slot_row, gate, d, K, n_shared, shared_base, shared_stride, dg, dy);
+  else
+    dgate_dy_kernel<false><<<T, 256, 0, s>>>(dout, y, slot_row, gate, d, K, n_shared, shared_base, shared_stride, dg,
+                                             dy);
   return hipGetLastError();
 }
 
@@ -582,19 +634,34 @@ hipError_t launch_router_bwd(const float* scores, const int32_t* idx, const floa
                              const void* dx, const int32_t* slot_row, const void* E, int e_dtype, const void* u,
                              const int32_t* offsets, const int32_t* row_token, int T, int N, int d, int K,
                              int n_shared, long shared_base, long shared_stride, float* dz, float* du, float* dE,
-                             hipStream_t s) {
+                             int dtype, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   dz_kernel<<<cdiv(T, 256), 256, 0, s>>>(scores, idx, dg, T, N, K, dz);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (e_dtype == MOE_BF16)
-    du_kernel<true><<<T, 256, 0, s>>>((const uint16_t*)dout, (const uint16_t*)dx, slot_row, idx, dz, E, d, K,
-                                      n_shared, shared_base, shared_stride, du);
+  const bool f32 = dtype == MOE_F32;
+  if (e_dtype == MOE_BF16 && !f32)
+    du_kernel<true, false><<<T, 256, 0, s>>>(dout, dx, slot_row, idx, dz, E, d, K, n_shared, shared_base,
+                                             shared_stride, du);
+  else if (e_dtype == MOE_BF16)
+    du_kernel<true, true><<<T, 256, 0, s>>>(dout, dx, slot_row, idx, dz, E, d, K, n_shared, shared_base,
+                                            shared_stride, du);
+  else if (!f32)
+    du_kernel<false, false><<<T, 256, 0, s>>>(dout, dx, slot_row, idx, dz, E, d, K, n_shared, shared_base,
+                                              shared_stride, du);
   else
-    du_kernel<false><<<T, 256, 0, s>>>((const uint16_t*)dout, (const uint16_t*)dx, slot_row, idx, dz, E, d, K,
-                                       n_shared, shared_base, shared_stride, du);
+    du_kernel<false, true><<<T, 256, 0, s>>>(dout, dx, slot_row, idx, dz, E, d, K, n_shared, shared_base,
+                                             shared_stride, du);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  de_kernel<<<dim3(N, cdiv(d, 2048)), 256, 0, s>>>((const uint16_t*)u, offsets, row_token, idx, dz, d, K, dE);
+  if (f32) de_kernel<true><<<dim3(N, cdiv(d, 2048)), 256, 0, s>>>(u, offsets, row_token, idx, dz, d, K, dE);
+  else de_kernel<false><<<dim3(N, cdiv(d, 2048)), 256, 0, s>>>(u, offsets, row_token, idx, dz, d, K, dE);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad_f32(const WgradArgs& a, const float* P, const float* Q, hipStream_t s) {
+  if (a.n_seg <= 0) return hipSuccess;
+  wgrad_f32_kernel<<<dim3(cdiv(a.Nn, 64), cdiv(a.M, 4), a.n_seg), 256, 0, s>>>(
+      P, Q, a.q_row, a.offsets, a.M, a.Nn, a.out0, a.out1, a.ostride0, a.ostride1, a.n_first);
   return hipGetLastError();
 }
 
@@ -607,10 +674,13 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_transpose_bf16(const void* src, void* dst, int batch, int rows, int cols, hipStream_t s) {
+hipError_t launch_transpose(const void* src, void* dst, int batch, int rows, int cols, int dtype, hipStream_t s) {
   if (batch <= 0 || rows <= 0 || cols <= 0) return hipSuccess;
-  transpose_bf16_kernel<<<dim3(cdiv(cols, 64), cdiv(rows, 64), batch), 256, 0, s>>>(
-      (const uint16_t*)src, (uint16_t*)dst, rows, cols);
+  const dim3 grid(cdiv(cols, 64), cdiv(rows, 64), batch);
+  if (dtype == MOE_F32)
+    transpose_kernel<float><<<grid, 256, 0, s>>>((const float*)src, (float*)dst, rows, cols);
+  else
+    transpose_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, rows, cols);
   return hipGetLastError();
 }
 

@@ -612,9 +612,13 @@ extern "C" int moe_quantize_fp8(int32_t kind, const void* src, int32_t src_dtype
 // ---------------------------------------------------------------- backward
 // Supported: bf16 u and experts, I (and I_s) a multiple of 128, shared
 // experts of the routed experts' size (or none), T > 0 handled, T == 0 no-op.
+// bf16 layers (I % 128 == 0) and fp32 layers; shared experts of the routed size
 static int backward_shape_ok(const moe_desc_t* d) {
-  if (d->in_dtype != MOE_BF16 || d->expert_dtype != MOE_BF16) return MOE_ENOTSUP;
-  if (d->inter % 128) return MOE_ENOTSUP;
+  const bool bf = d->in_dtype == MOE_BF16 && d->expert_dtype == MOE_BF16;
+  const bool f32 = d->in_dtype == MOE_F32 && d->expert_dtype == MOE_F32;
+  if (!bf && !f32) return MOE_ENOTSUP;
+  if (bf && d->inter % 128) return MOE_ENOTSUP;
+  if (f32 && d->inter % 8) return MOE_ENOTSUP;
   if (d->n_shared && d->inter_shared != d->inter) return MOE_ENOTSUP;
   return MOE_OK;
 }
@@ -629,6 +633,7 @@ static BwdWs bwd_layout(const moe_desc_t* d) {
   BwdWs w;
   const size_t T = d->T, K = d->top_k, N = d->n_routed, Ns = d->n_shared, I = d->inter, D = d->d;
   const size_t W = (T + 63) / 64, n_seg = N + Ns, R = T * K + Ns * T;
+  const size_t es = d->expert_dtype == MOE_F32 ? 4 : 2;     // activations A|B, H, Y, dY, dH, dA|dB
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += al256(bytes); return at; };
   w.idx = take(T * K * 4);
@@ -641,16 +646,16 @@ static BwdWs bwd_layout(const moe_desc_t* d) {
   w.mtile = take((n_seg + 1) * 4);
   w.row_token = take(R * 4);
   w.slot_row = take(T * K * 4);
-  w.ab = take(R * 2 * I * 2);
-  w.h = take(R * I * 2);
-  w.y = take(R * D * 2);          // Y, then dX
-  w.dy = take(R * D * 2);
-  w.dh = take(R * I * 2);
-  w.dab = take(R * 2 * I * 2);
+  w.ab = take(R * 2 * I * es);
+  w.h = take(R * I * es);
+  w.y = take(R * D * es);          // Y, then dX
+  w.dy = take(R * D * es);
+  w.dh = take(R * I * es);
+  w.dab = take(R * 2 * I * es);
   w.dg = take(T * K * 4);
   w.dz = take(T * K * 4);
   // transposed, padded operands of the weight-gradient GEMMs (d a multiple of 256)
-  w.pitch = D % 256 == 0 ? wgrad_pitch((long)R, (int)n_seg) : 0;
+  w.pitch = D % 256 == 0 && es == 2 ? wgrad_pitch((long)R, (int)n_seg) : 0;
   const size_t wide = D > 2 * I ? D : 2 * I;
   w.pt = w.pitch ? take(wide * (size_t)w.pitch * 2) : 0;
   w.qt = w.pitch ? take(wide * (size_t)w.pitch * 2) : 0;
@@ -674,12 +679,12 @@ extern "C" int moe_transpose_expert_weights(const moe_desc_t* d, const moe_weigh
                       !aligned(wt->w2_shared)))
     return MOE_EINVAL;
   hipStream_t s = (hipStream_t)stream;
-  const int I = d->inter, D = d->d;
-  MOE_TRY(launch_transpose_bf16(w->w13, (void*)wt->w13, d->n_routed, 2 * I, D, s));
-  MOE_TRY(launch_transpose_bf16(w->w2, (void*)wt->w2, d->n_routed, D, I, s));
+  const int I = d->inter, D = d->d, dt = d->expert_dtype;
+  MOE_TRY(launch_transpose(w->w13, (void*)wt->w13, d->n_routed, 2 * I, D, dt, s));
+  MOE_TRY(launch_transpose(w->w2, (void*)wt->w2, d->n_routed, D, I, dt, s));
   if (d->n_shared) {
-    MOE_TRY(launch_transpose_bf16(w->w13_shared, (void*)wt->w13_shared, d->n_shared, 2 * I, D, s));
-    MOE_TRY(launch_transpose_bf16(w->w2_shared, (void*)wt->w2_shared, d->n_shared, D, I, s));
+    MOE_TRY(launch_transpose(w->w13_shared, (void*)wt->w13_shared, d->n_shared, 2 * I, D, dt, s));
+    MOE_TRY(launch_transpose(w->w2_shared, (void*)wt->w2_shared, d->n_shared, D, I, dt, s));
   }
   return MOE_OK;
 }
@@ -705,6 +710,7 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
   const int T = d->T, K = d->top_k, N = d->n_routed, Ns = d->n_shared, I = d->inter, D = d->d;
   const long TK = (long)T * K, R = TK + (long)Ns * T;
   const int n_seg = N + Ns;
+  const int dt = d->expert_dtype;                    // MOE_BF16 or MOE_F32 (activations and weights)
   int32_t* idx = (int32_t*)(base + L.idx);
   float* gate = (float*)(base + L.gate);
   int32_t* counts = (int32_t*)(base + L.counts);
@@ -739,21 +745,21 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
                             Kred, (int)R);
     ga.w1 = Ns ? w1 : w0;
     ga.n_first = N;
-    return launch_gemm_down(ga, MOE_BF16, bm, s);
+    return launch_gemm_down(ga, dt, bm, s);
   };
   const long s13 = 2L * I * D, s2 = (long)D * I;
   MOE_TRY(grouped(u, T, row_token, w->w13, w->w13_shared, s13, AB, 2 * I, D));      // [A|B] = X W13^T
-  MOE_TRY(launch_swiglu_fwd(AB, H, R, I, s));                                         // H = SiLU(A) B
+  MOE_TRY(launch_swiglu_fwd(AB, H, R, I, dt, s));                                     // H = SiLU(A) B
   MOE_TRY(grouped(H, R, nullptr, w->w2, w->w2_shared, s2, Y, D, I));                // Y = H W2^T
 
   // backward
-  MOE_TRY(launch_dgate_dy(dout, Y, slot_row, gate, T, D, K, Ns, TK, T, dg, dY, s));   // dg, dY
+  MOE_TRY(launch_dgate_dy(dout, Y, slot_row, gate, T, D, K, Ns, TK, T, dg, dY, dt, s));   // dg, dY
   MOE_TRY(grouped(dY, R, nullptr, wt->w2, wt->w2_shared, s2, dH, I, D));             // dH = dY W2
-  MOE_TRY(launch_swiglu_bwd(dH, AB, dAB, R, I, s));                                   // dA | dB
+  MOE_TRY(launch_swiglu_bwd(dH, AB, dAB, R, I, dt, s));                               // dA | dB
   void* dX = Y;                                                                       // Y is no longer needed
   MOE_TRY(grouped(dAB, R, nullptr, wt->w13, wt->w13_shared, s13, dX, D, 2 * I));     // dX = [dA dB] W13
   MOE_TRY(launch_router_bwd(scores, idx, dg, dout, dX, slot_row, w->centroids, d->router_dtype, u, offsets,
-                            row_token, T, N, D, K, Ns, TK, T, dz, g->du, g->dE, s));  // dz, du, dE
+                            row_token, T, N, D, K, Ns, TK, T, dz, g->du, g->dE, dt, s));  // dz, du, dE
   WgradArgs wa;
   wa.offsets = offsets; wa.n_seg = n_seg; wa.n_first = N;
   if (L.pitch) {
@@ -762,10 +768,12 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
   }
   wa.P = (const uint16_t*)dY; wa.Q = (const uint16_t*)H; wa.q_row = nullptr; wa.q_rows = R; wa.M = D; wa.Nn = I;
   wa.out0 = g->dw2; wa.ostride0 = s2; wa.out1 = Ns ? g->dw2_shared : g->dw2; wa.ostride1 = s2;
-  MOE_TRY(launch_wgrad(wa, s));                                                       // dW2 = dY^T H
+  if (dt == MOE_F32) MOE_TRY(launch_wgrad_f32(wa, (const float*)dY, (const float*)H, s));
+  else MOE_TRY(launch_wgrad(wa, s));                                                  // dW2 = dY^T H
   wa.P = (const uint16_t*)dAB; wa.Q = (const uint16_t*)u; wa.q_row = row_token; wa.q_rows = T; wa.M = 2 * I;
   wa.Nn = D;
   wa.out0 = g->dw13; wa.ostride0 = s13; wa.out1 = Ns ? g->dw13_shared : g->dw13; wa.ostride1 = s13;
-  MOE_TRY(launch_wgrad(wa, s));                                                       // dW13 = [dA dB]^T X
+  if (dt == MOE_F32) MOE_TRY(launch_wgrad_f32(wa, (const float*)dAB, (const float*)u, s));
+  else MOE_TRY(launch_wgrad(wa, s));                                                  // dW13 = [dA dB]^T X
   return MOE_OK;
 }

@@ -100,17 +100,20 @@ struct WgradArgs {
 };
 long wgrad_pitch(long rows, int n_seg);
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
-hipError_t launch_swiglu_fwd(const void* ab, void* h, long rows, int I, hipStream_t s);
-hipError_t launch_swiglu_bwd(const void* dh, const void* ab, void* dab, long rows, int I, hipStream_t s);
+// fp32 layers: P, Q fp32 (the args' P/Q/pt/qt are ignored)
+hipError_t launch_wgrad_f32(const WgradArgs& a, const float* P, const float* Q, hipStream_t s);
+// element-wise backward pieces; dtype MOE_BF16 or MOE_F32 for the activations they read and write
+hipError_t launch_swiglu_fwd(const void* ab, void* h, long rows, int I, int dtype, hipStream_t s);
+hipError_t launch_swiglu_bwd(const void* dh, const void* ab, void* dab, long rows, int I, int dtype, hipStream_t s);
 hipError_t launch_dgate_dy(const void* dout, const void* y, const int32_t* slot_row, const float* gate, int T, int d,
-                           int K, int n_shared, long shared_base, long shared_stride, float* dg, void* dy,
+                           int K, int n_shared, long shared_base, long shared_stride, float* dg, void* dy, int dtype,
                            hipStream_t s);
 hipError_t launch_router_bwd(const float* scores, const int32_t* idx, const float* dg, const void* dout,
                              const void* dx, const int32_t* slot_row, const void* E, int e_dtype, const void* u,
                              const int32_t* offsets, const int32_t* row_token, int T, int N, int d, int K,
                              int n_shared, long shared_base, long shared_stride, float* dz, float* du, float* dE,
-                             hipStream_t s);
-hipError_t launch_transpose_bf16(const void* src, void* dst, int batch, int rows, int cols, hipStream_t s);
+                             int dtype, hipStream_t s);
+hipError_t launch_transpose(const void* src, void* dst, int batch, int rows, int cols, int dtype, hipStream_t s);
 
 // sequence-wise balance loss (forward value)
 size_t seq_balance_ws_bytes(int T, int N, int seq_len);

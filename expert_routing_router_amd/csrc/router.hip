@@ -32,7 +32,7 @@ extern "C" __device__ unsigned int __ockl_wfred_min_u32(unsigned int);
 namespace moe {
 
 constexpr int RT_BT = 32;
-constexpr int RT_BT_SEL = 8;
+constexpr int RT_BT_SEL = 4;
 constexpr int RT_THREADS = 256;
 constexpr int RT_NMAX = 256;
 constexpr int RT_QMAX = 8;
@@ -550,7 +550,7 @@ hipError_t launch_route(const RouteArgs& a, int front, hipStream_t s) {
   const bool ub = a.in_dtype == MOE_BF16;
   switch (front) {
     case kFrontScoresIn:
-      // selection only: 8 tokens per workgroup (2 per wave) for more waves in flight
+      // selection only: 4 tokens per workgroup (one per wave) for more waves in flight
       route_kernel<kFrontScoresIn, false, false, RT_BT_SEL><<<dim3(cdiv(a.T, RT_BT_SEL)), RT_THREADS, 0, s>>>(a);
       break;
     case kFrontMfma: route_kernel<kFrontMfma, true, true><<<grid, RT_THREADS, 0, s>>>(a); break;

@@ -111,18 +111,18 @@ class MoELayer:
         return self.out
 
     def backward(self, u: torch.Tensor, b: torch.Tensor, dout: torch.Tensor, stream=None):
-        """Gradients of forward(u, b) for the upstream gradient dout [T, d] (bf16), for the routing
+        """Gradients of forward(u, b) for the upstream gradient dout [T, d] (in_dtype), for the routing
         the forward chooses with this b: a dict of fp32 device tensors du [T, d], dE [N_r, d],
         dw13 [N_r, 2I, d], dw2 [N_r, d, I] (and dw13s, dw2s for the shared experts). The
         transposed weight copies and the gradient buffers are allocated on the first call."""
         cfg, dev = self.cfg, self.device
         if getattr(self, "_wt", None) is None:
             I, d, N, ns = cfg.inter, cfg.d, cfg.n_routed, max(cfg.n_shared, 1)
-            bf = torch.bfloat16
-            self._w13t = torch.empty((N, d, 2 * I), dtype=bf, device=dev)
-            self._w2t = torch.empty((N, I, d), dtype=bf, device=dev)
-            self._w13st = torch.empty((ns, d, 2 * I), dtype=bf, device=dev)
-            self._w2st = torch.empty((ns, I, d), dtype=bf, device=dev)
+            wdt = self.w13.dtype                          # bf16 or fp32, as the experts
+            self._w13t = torch.empty((N, d, 2 * I), dtype=wdt, device=dev)
+            self._w2t = torch.empty((N, I, d), dtype=wdt, device=dev)
+            self._w13st = torch.empty((ns, d, 2 * I), dtype=wdt, device=dev)
+            self._w2st = torch.empty((ns, I, d), dtype=wdt, device=dev)
             sh = cfg.n_shared > 0
             self._wt = L.make_weights(None, self._w13t, self._w2t, self._w13st if sh else None,
                                       self._w2st if sh else None)

@@ -192,23 +192,24 @@ typedef struct moe_grads {
   float* dw2_shared;
 } moe_grads_t;
 
-/* Transposed expert weights for moe_backward (bf16 layers): fills
- * wt->w13 [N_r, d, 2I] and wt->w2 [N_r, I, d] (and the shared ones) from the
- * weights in w. Other members of wt are ignored. */
+/* Transposed expert weights for moe_backward: fills wt->w13 [N_r, d, 2I] and
+ * wt->w2 [N_r, I, d] (and the shared ones) from the weights in w, in the
+ * experts' dtype (bf16 or fp32). Other members of wt are ignored. */
 int moe_transpose_expert_weights(const moe_desc_t* desc, const moe_weights_t* w, moe_weights_t* wt,
                                  moe_stream_t stream);
 
 /* Backward of moe_forward for the routing it chooses (same u, b, weights):
- * given dout = dL/dout [T, d] (bf16), writes dL/du, dL/dE and the expert
+ * given dout = dL/dout [T, d] (in_dtype), writes dL/du, dL/dE and the expert
  * weight gradients. The selection and the bias are piecewise constant (b only
  * routes: pwwt.cn note 1.1.2-1.1.3), so gradients flow through the gates'
  * dependence on the affinities, g = s_sel / sum(s_sel), and the SwiGLU
  * experts (output equation of the xyznot.com guides, section 2):
  *   dg = <dout, Y>, dY = g dout, dH = dY W2, dA|dB from SwiGLU, dX = [dA dB] W13,
  *   ds = (dg - sum g dg) / sum s, dz = ds s (1 - s), dE = dz^T u.
- * The forward is recomputed inside (bf16 intermediates, fp32 accumulation).
- * Supported: bf16 u and experts, I % 128 == 0, N_s == 0 or I_s == I;
- * MOE_ENOTSUP otherwise. wt: moe_transpose_expert_weights of w.
+ * The forward is recomputed inside (intermediates in the experts' dtype,
+ * fp32 accumulation). Supported: bf16 u and experts with I % 128 == 0, or
+ * fp32 u and experts with I % 8 == 0; N_s == 0 or I_s == I; MOE_ENOTSUP
+ * otherwise. wt: moe_transpose_expert_weights of w.
  * ws: moe_backward_workspace_bytes(desc) bytes (0 when unsupported). */
 size_t moe_backward_workspace_bytes(const moe_desc_t* desc);
 int moe_backward(const moe_desc_t* desc, const moe_weights_t* w, const moe_weights_t* wt, const void* u,

@@ -182,3 +182,21 @@ def test_capacity_arg_errors(lib):
     assert fc(-1, need_cap) == M.MOE_EINVAL
     assert fc(256, need) == M.MOE_EWORKSPACE
     assert fc(256, need_cap, MIS) == M.MOE_EINVAL
+
+
+def test_backward_support_matrix(lib):
+    """moe_backward covers bf16 layers with I % 128 == 0 and fp32 layers; the workspace size is 0
+    (and the call MOE_ENOTSUP) otherwise."""
+    bf = M.make_desc(T=64, d=512, n_routed=16, top_k=4, n_shared=1, inter=256)
+    f32 = M.make_desc(T=64, d=256, n_routed=16, top_k=4, n_shared=1, inter=128, in_dtype="f32",
+                      router_dtype="f32", expert_dtype="f32")
+    f8 = M.make_desc(T=64, d=512, n_routed=16, top_k=4, n_shared=1, inter=256, router_dtype="f32",
+                     expert_dtype="fp8")
+    odd = M.make_desc(T=64, d=512, n_routed=16, top_k=4, n_shared=1, inter=192)
+    assert M.moe_backward_workspace_bytes(bf) > 0 and M.moe_backward_workspace_bytes(f32) > 0
+    assert M.moe_backward_workspace_bytes(f8) == 0 and M.moe_backward_workspace_bytes(odd) == 0
+    w = M.MoeWeights(A, A, A, A, A, None, None, None, None)
+    g = M.MoeGrads(A, A, A, A, A, A)
+    st = lib.moe_backward(ctypes.byref(f8), ctypes.byref(w), ctypes.byref(w), A, A, A, ctypes.byref(g), A,
+                          1 << 40, None)
+    assert st == M.MOE_ENOTSUP

@@ -32,7 +32,8 @@ def _cfg(name):
 
 def _dout(cfg, seed=11):
     rng = np.random.default_rng(seed)
-    return gen.f32_to_bf16_bits(rng.standard_normal((cfg.T, cfg.d)).astype(np.float32))
+    x = rng.standard_normal((cfg.T, cfg.d)).astype(np.float32)
+    return gen.f32_to_bf16_bits(x) if cfg.in_dtype == "bf16" else x
 
 
 def _run(cfg, step=0):
@@ -42,7 +43,7 @@ def _run(cfg, step=0):
     dout = _dout(cfg)
     b_dev = dev(b, "f32")
     layer.forward(dev(u, cfg.in_dtype), b_dev, update_bias=False)
-    g = layer.backward(dev(u, cfg.in_dtype), b_dev, dev(dout, "bf16"))
+    g = layer.backward(dev(u, cfg.in_dtype), b_dev, dev(dout, cfg.in_dtype))
     torch.cuda.synchronize()
     return layer, u, b, dout, g
 
@@ -55,22 +56,28 @@ def _oracle_inputs(cfg, u, b):
 
 
 def _weights(cfg, experts):
-    w13 = {e: nx.to_f64(gen.expert_w13(cfg, e), "bf16") for e in experts}
-    w2 = {e: nx.to_f64(gen.expert_w2(cfg, e), "bf16") for e in experts}
-    w13s = [nx.to_f64(gen.shared_w13(cfg, s), "bf16") for s in range(cfg.n_shared)]
-    w2s = [nx.to_f64(gen.shared_w2(cfg, s), "bf16") for s in range(cfg.n_shared)]
+    dt = "bf16" if cfg.expert_dtype == "bf16" else "f32"
+    w13 = {e: nx.to_f64(gen.expert_w13(cfg, e), dt) for e in experts}
+    w2 = {e: nx.to_f64(gen.expert_w2(cfg, e), dt) for e in experts}
+    w13s = [nx.to_f64(gen.shared_w13(cfg, s), dt) for s in range(cfg.n_shared)]
+    w2s = [nx.to_f64(gen.shared_w2(cfg, s), dt) for s in range(cfg.n_shared)]
     return w13, w2, w13s, w2s
 
 
-@pytest.mark.parametrize("name", ["small", "ragged"])
+def _dout64(cfg, dout):
+    return nx.bf16_to_f64(dout) if cfg.in_dtype == "bf16" else dout.astype(np.float64)
+
+
+@pytest.mark.parametrize("name", ["small", "ragged", "tiny"])
 def test_backward_full(name):
+    """bf16 layers at the bf16 bar (rel-L2 <= 1e-2); the fp32 layer (tiny) at the fp32 bar (1e-5)."""
     cfg = _cfg(name)
     layer, u, b, dout, g = _run(cfg)
     u64, E64, r = _oracle_inputs(cfg, u, b)
     idx_gpu = host(layer.idx)
     assert np.array_equal(np.sort(idx_gpu, 1), np.sort(r.idx, 1)), "routing differs from the oracle's"
     w13, w2, w13s, w2s = _weights(cfg, range(cfg.n_routed))
-    ref = backward.layer_grads(u64, E64, r.idx, nx.bf16_to_f64(dout), w13, w2, w13s, w2s)
+    ref = backward.layer_grads(u64, E64, r.idx, _dout64(cfg, dout), w13, w2, w13s, w2s)
     used = sorted(ref["dw13"])
     errs = {
         "du": rel_l2(host(g["du"]), ref["du"]),
@@ -82,8 +89,9 @@ def test_backward_full(name):
         errs["dw13s"] = rel_l2(host(g["dw13s"])[:cfg.n_shared], np.stack(ref["dw13s"]))
         errs["dw2s"] = rel_l2(host(g["dw2s"])[:cfg.n_shared], np.stack(ref["dw2s"]))
     log(name, " ".join("%s %.2e" % kv for kv in errs.items()))
+    bar = 1e-5 if cfg.expert_dtype == "f32" else 1e-2
     for k, v in errs.items():
-        assert v <= 1e-2, (k, v)
+        assert v <= bar, (k, v)
     # an expert no token chose gets an exactly zero gradient
     unused = sorted(set(range(cfg.n_routed)) - set(used))
     for e in unused:
