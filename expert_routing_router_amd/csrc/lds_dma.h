@@ -29,6 +29,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// the same, and also every LDS read of this wave done (lgkmcnt 0)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
 // Buffer resource words of a raw buffer (the operands above need them in
 // SGPRs: base and size must be the same in every lane).
 __device__ __forceinline__ i32x4 rsrc_words(const void* base, long bytes) {

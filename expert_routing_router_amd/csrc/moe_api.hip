@@ -459,7 +459,8 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
   // 1. router
   prof_mark(-1, s);
   float* scores = capped ? (float*)(base + L.scores) : nullptr;
-  RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, nullptr, idx, gate, counts);
+  // the loads come from the dispatch's bitmaps below, not from the router
+  RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, nullptr, idx, gate, nullptr);
   if (two_phase_router(d)) {
     MOE_TRY(launch_route_two_phase(ra, base + L.rscratch, s));
   } else {
@@ -475,12 +476,13 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
   p.idx = idx; p.T = T; p.K = K; p.n_routed = N;
   p.bitmap = (uint64_t*)(base + L.bitmap); p.wprefix = (int32_t*)(base + L.wprefix);
   p.counts_ws = nullptr; p.offsets = offsets; p.row_token = row_token; p.slot_row = slot_row;
-  p.counts_out = nullptr;
+  p.counts_out = counts;                 // every selection's load (before any dropping)
   int32_t* keep = nullptr;
   if (capped) {
     // no-drop layout first (rows of each expert in token order), then the kept subset
     p.n_extra_seg = 0; p.mtile_prefix = nullptr; p.bm = 0;
     MOE_TRY(launch_permute(p, s));
+    p.counts_out = nullptr;
     keep = keep_out ? keep_out : (int32_t*)(base + L.keep);
     MOE_TRY(launch_capacity(offsets, row_token, idx, scores, T, N, K, cap, keep,
                             n_dropped ? n_dropped : (int32_t*)(base + L.dropped), s));
@@ -624,7 +626,7 @@ static int backward_shape_ok(const moe_desc_t* d) {
 }
 
 struct BwdWs {
-  size_t idx, gate, counts, scores, bitmap, wprefix, offsets, mtile, row_token, slot_row;
+  size_t idx, gate, scores, bitmap, wprefix, offsets, mtile, row_token, slot_row;
   size_t ab, h, y, dy, dh, dab, dg, dz, pt, qt, kofs, total;
   long pitch;
 };
@@ -638,7 +640,6 @@ static BwdWs bwd_layout(const moe_desc_t* d) {
   auto take = [&](size_t bytes) { size_t at = o; o += al256(bytes); return at; };
   w.idx = take(T * K * 4);
   w.gate = take(T * K * 4);
-  w.counts = take(N * 4);
   w.scores = take(T * N * 4);
   w.bitmap = take(W * N * 8);
   w.wprefix = take(W * N * 4);
@@ -713,7 +714,6 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
   const int dt = d->expert_dtype;                    // MOE_BF16 or MOE_F32 (activations and weights)
   int32_t* idx = (int32_t*)(base + L.idx);
   float* gate = (float*)(base + L.gate);
-  int32_t* counts = (int32_t*)(base + L.counts);
   float* scores = (float*)(base + L.scores);
   int32_t* offsets = (int32_t*)(base + L.offsets);
   int32_t* mtile = (int32_t*)(base + L.mtile);
@@ -730,7 +730,7 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
 
   // forward recompute: the same routing and dispatch as moe_forward (the fused
   // router gives bit-identical affinities and selections), then A|B, H, Y
-  RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, scores, idx, gate, counts);
+  RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, scores, idx, gate, nullptr);   // loads not needed
   MOE_TRY(launch_route(ra, route_front(d), s));
   const int bm = gemm_bm(d->expert_dtype, (int)(TK / N), d->d, d->inter);
   PermuteArgs p;

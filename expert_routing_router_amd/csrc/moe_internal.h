@@ -10,7 +10,8 @@ namespace moe {
 enum RouterFront { kFrontScoresIn = 0, kFrontMfma = 1, kFrontMfmaSplitE = 2, kFrontF64 = 3 };
 struct RouteArgs {
   const void* u; const void* E; const float* b; const float* scores_in;
-  float* scores_out; int32_t* idx; float* gate; int32_t* counts;
+  float* scores_out; int32_t* idx; float* gate;
+  int32_t* counts;   // nullable: per-expert loads, counted after the selection by a separate kernel
   int T, d, n_routed, top_k, n_groups, topk_groups, group_topk, group_score_biased;
   int in_dtype, router_dtype;
 };
@@ -22,6 +23,8 @@ bool route_two_phase_ok(const RouteArgs& a);
 size_t route_two_phase_bytes(int T, int N, int d, int router_dtype);
 hipError_t launch_route_two_phase(const RouteArgs& a, void* scratch, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, long n, hipStream_t s);
+// counts[e] = number of the n entries of idx equal to e (zeroed first)
+hipError_t launch_count_loads(const int32_t* idx, long n, int N, int32_t* counts, hipStream_t s);
 
 // ---------------------------------------------------------------- permute
 // Workspace pieces: bitmap [N_r][W] u64 (W = ceil(T/64)), wprefix [N_r][W] i32.

@@ -15,7 +15,7 @@
 // the production selection.
 //
 // Precision: the MFMA front end accumulates bf16 products (exact in fp32) in
-// fp32 over 64-element chunks of d and sums the chunks in fp64; the sigmoid
+// fp32 over 128-element chunks of d and sums the chunks in fp64; the sigmoid
 // is evaluated in fp64 and rounded once to fp32. fp32 centroids are split into
 // three bf16 terms (hi + mid + lo reproduces the fp32 value exactly), so the
 // products stay exact on the bf16 MFMA path; the hi products and the much
@@ -27,7 +27,6 @@
 #include <type_traits>
 
 extern "C" __device__ unsigned int __ockl_wfred_max_u32(unsigned int);
-extern "C" __device__ unsigned int __ockl_wfred_min_u32(unsigned int);
 
 namespace moe {
 
@@ -41,7 +40,6 @@ template <int BT>
 struct RouterLdsT {
   float s[BT][RT_NMAX];
   float b[RT_NMAX];
-  int cnt[RT_NMAX];
 };
 using RouterLds = RouterLdsT<RT_BT>;      // the fused front ends work on 32 tokens
 
@@ -72,8 +70,8 @@ __device__ __forceinline__ void split3(const float* x, bf16x8& hi, bf16x8& mid, 
 // at k-group (l>>4); D element (4*(l>>4)+r, l&15) in register r.
 // Wave w owns expert blocks w, w+4, ... (16 experts each) for all 32 tokens.
 // Fragments are loaded straight from global memory three k-steps ahead of
-// their MFMAs (four rotating register sets); every two k-steps the fp32 MFMA
-// sums are flushed into fp64 accumulators.
+// their MFMAs (four rotating register sets); every four k-steps (128 elements
+// of d) the fp32 MFMA sums are flushed into fp64 accumulators.
 template <bool SPLIT_E>
 struct RouterFrag {
   bf16x8 a0, a1;
@@ -178,9 +176,7 @@ __device__ void front_mfma(const RouteArgs& a, RouterLds& sh, int t0) {
     mfma(f[0]);
     load(f[0], s0 + 4);
     mfma(f[1]);
-    flush();
     load(f[1], s0 + 5);
-    zero_acc();
     mfma(f[2]);
     load(f[2], s0 + 6);
     mfma(f[3]);
@@ -213,15 +209,77 @@ __device__ void front_f64(const RouteArgs& a, RouterLds& sh, int t0, int nt) {
 }
 
 // ---------------------------------------------------------------- selection
+// v with lane l replaced by lane l ^ OFF's value
+template <int OFF>
+__device__ __forceinline__ float xor_lane(float v) {
+  if constexpr (OFF < 32) return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (OFF << 10)));
+  else return __shfl_xor(v, 32, kWave);
+}
+// max over the aligned run of S lanes (S a power of two) that holds this lane
+__device__ __forceinline__ float segment_max(float v, int S) {
+  if (S > 1) v = fmaxf(v, xor_lane<1>(v));
+  if (S > 2) v = fmaxf(v, xor_lane<2>(v));
+  if (S > 4) v = fmaxf(v, xor_lane<4>(v));
+  if (S > 8) v = fmaxf(v, xor_lane<8>(v));
+  if (S > 16) v = fmaxf(v, xor_lane<16>(v));
+  if (S > 32) v = fmaxf(v, xor_lane<32>(v));
+  return v;
+}
+
+// Group scores when each group is an aligned run of S lanes of one expert slot
+// (S a power of two, at most 64): every group's top-q scores are extracted at
+// once by segmented max reductions, removing one holder of each maximum (the
+// lowest lane) before the next; their fp32 sum is taken largest first, as in
+// the per-lane loop it replaces. Returns lane g's group key (g < G), else 0.
+__device__ __forceinline__ uint32_t group_keys_segmented(const RouteArgs& a, const float* b, const float* srow,
+                                                         int lane, int S, int G, int q) {
+  const int N = a.n_routed;
+  const int segbase = lane & ~(S - 1);
+  const uint64_t segmask = S == 64 ? ~0ull : ((1ull << S) - 1ull);
+  float gsum[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    gsum[j] = -INFINITY;
+    if (64 * j >= N) continue;
+    const int e = lane + 64 * j;
+    float v = -INFINITY;
+    if (e < N) {
+      v = a.group_score_biased ? srow[e] + b[e] : srow[e];
+      if (v != v) v = -INFINITY;               // a NaN score never ranks
+    }
+    float acc = 0.f;
+    for (int r = 0; r < q; r++) {
+      const float m = segment_max(v, S);
+      acc = r == 0 ? m : acc + m;
+      if (r + 1 < q) {
+        const uint64_t hit = (__ballot(v == m) >> segbase) & segmask;
+        if (lane == segbase + __ffsll((unsigned long long)hit) - 1) v = -INFINITY;
+      }
+    }
+    gsum[j] = acc;
+  }
+  // lane g < G takes group g's sum from slot (g*S)/64, lane (g*S)%64
+  const int src = (lane * S) & 63, slot = (lane * S) >> 6;
+  float mine = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const float x = __shfl(gsum[j], src, kWave);
+    if (slot == j) mine = x;
+  }
+  return lane < G ? max(ordered_f32(mine), 1u) : 0u;
+}
+
 // One wave per token. Expert e lives in lane (e & 63), slot (e >> 6). Each
-// selection round is two wave reductions (device-library, DPP based): the
-// largest ordered key, then the lowest expert index holding it -- the total
-// order (key desc, index asc); -0 and +0 share one ordered key.
+// selection round is one wave reduction (device library, DPP based) for the
+// largest ordered key and one ballot per slot for the lowest expert index
+// holding it -- the total order (key desc, index asc); -0 and +0 share one
+// ordered key.
 template <int BT>
 __device__ void select_tokens(const RouteArgs& a, RouterLdsT<BT>& sh, int t0, int nt) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int N = a.n_routed, K = a.top_k, G = a.n_groups, M = a.topk_groups, q = a.group_topk;
   const int S = N / G;
+  const bool seg_groups = (S & (S - 1)) == 0 && S <= 64;
   for (int t = wave; t < nt; t += RT_THREADS / kWave) {
     const float* srow = sh.s[t];
     // ordered keys; 0 = not a candidate. A candidate's key is at least 1 (only one NaN bit
@@ -234,7 +292,9 @@ __device__ void select_tokens(const RouteArgs& a, RouterLdsT<BT>& sh, int t0, in
     }
     if (G > 1) {
       uint32_t gk = 0u;
-      if (lane < G) {
+      if (seg_groups) {
+        gk = group_keys_segmented(a, sh.b, srow, lane, S, G, q);
+      } else if (lane < G) {
         float top[RT_QMAX];
 #pragma unroll
         for (int i = 0; i < RT_QMAX; i++) top[i] = -INFINITY;
@@ -255,9 +315,12 @@ __device__ void select_tokens(const RouteArgs& a, RouterLdsT<BT>& sh, int t0, in
       uint64_t chosen = 0ull;
       for (int m = 0; m < M; m++) {
         const uint32_t gmax = __ockl_wfred_max_u32(gk);
-        const uint32_t g = __ockl_wfred_min_u32(lane < G && gk == gmax ? (uint32_t)lane : 0xFFFFFFFFu);
-        chosen |= 1ull << g;
-        if (lane == (int)g) gk = 0u;
+        const uint64_t holders = __ballot(lane < G && gk == gmax);     // lowest group index first
+        if (gmax && holders) {
+          const int g = (int)__builtin_ctzll(holders);
+          chosen |= 1ull << g;
+          if (lane == g) gk = 0u;
+        }
       }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
@@ -265,29 +328,36 @@ __device__ void select_tokens(const RouteArgs& a, RouterLdsT<BT>& sh, int t0, in
         if (e < N && !((chosen >> (e / S)) & 1ull)) ok[j] = 0u;
       }
     }
+    // Round k: the largest key is one wave reduction; the lowest expert index
+    // holding it comes from one ballot per slot (expert lane + 64 j, so the
+    // first slot with a holder, then its lowest lane); it is wave-uniform, so
+    // only one slot is touched to remove it.
     int my_e = 0;
     for (int k = 0; k < K; k++) {
       const uint32_t lmax = max(max(ok[0], ok[1]), max(ok[2], ok[3]));
       const uint32_t kmax = __ockl_wfred_max_u32(lmax);
-      uint32_t li = 0xFFFFFFFFu;
+      int e = -1;
+      if (kmax) {
 #pragma unroll
-      for (int j = 3; j >= 0; j--)
-        if (ok[j] == kmax) li = (uint32_t)(lane + 64 * j);    // lowest index of this lane
-      const int e = (int)__ockl_wfred_min_u32(kmax ? li : 0xFFFFFFFFu);
+        for (int j = 3; j >= 0; j--) {
+          const uint64_t m = __ballot(ok[j] == kmax);
+          if (m) e = 64 * j + (int)__builtin_ctzll(m);
+        }
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        if (e == lane + 64 * j) ok[j] = 0u;
+        for (int j = 0; j < 4; j++)
+          if ((e >> 6) == j && lane == (e & 63)) ok[j] = 0u;
+      }
       if (lane == k) my_e = e;
     }
+    // gate denominator: the selected scores in selection order, summed in fp64
+    const float my_s = lane < K && my_e >= 0 ? srow[my_e] : 0.f;
     double sum = 0.0;
-    for (int k = 0; k < K; k++) sum += (double)srow[__shfl(my_e, k, kWave)];
+    for (int k = 0; k < K; k++) sum += (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
     if (lane < K) {
-      const float sv = srow[my_e];
-      const float g = sum > 0.0 ? (float)((double)sv / sum) : 1.0f / (float)K;
+      const float g = sum > 0.0 ? (float)((double)my_s / sum) : 1.0f / (float)K;
       const size_t o = (size_t)(t0 + t) * K + lane;
       a.idx[o] = my_e;
       a.gate[o] = g;
-      atomicAdd(&sh.cnt[my_e], 1);
     }
   }
 }
@@ -300,7 +370,6 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
   const int nt = min(BT, a.T - t0);
   for (int e = threadIdx.x; e < a.n_routed; e += RT_THREADS) {
     sh.b[e] = a.b[e];
-    sh.cnt[e] = 0;
   }
   if constexpr (FRONT == kFrontScoresIn) {
     for (int p = threadIdx.x; p < nt * a.n_routed; p += RT_THREADS) {
@@ -322,9 +391,6 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     }
   }
   select_tokens(a, sh, t0, nt);
-  __syncthreads();
-  for (int e = threadIdx.x; e < a.n_routed; e += RT_THREADS)
-    if (sh.cnt[e]) atomicAdd(&a.counts[e], sh.cnt[e]);
 }
 
 // ---------------------------------------------------------------- two-phase router
@@ -334,7 +400,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
 // of a 128-token x 64-expert tile and writes them to a scores buffer; phase 2
 // is route_kernel in scores-in mode (the same selection code). Phase 1 does
 // the same arithmetic as front_mfma -- the same 16x16x32 MFMAs on the same
-// operands, fp32 partials over 64-element chunks of d summed in fp64 in chunk
+// operands, fp32 partials over 128-element chunks of d summed in fp64 in chunk
 // order, the split of fp32 centroids into hi/mid/lo bf16 planes, the same
 // sigmoid -- so both routers give bit-identical affinities.
 constexpr int LG_BT = 128;          // tokens per workgroup
@@ -424,55 +490,122 @@ __global__ __launch_bounds__(256, 1) void logits_kernel(const uint16_t* __restri
 #pragma unroll
       for (int r = 0; r < 4; r++) z64[m][j][r] = 0.0;
 
-  const int nk = d / LG_BK;
-#pragma unroll
-  for (int p = 0; p < C::STAGES - 1; p++) issue(min(p, nk - 1), p);
-  int buf = 0, nbuf = C::STAGES - 1;
-  for (int kt = 0; kt < nk; kt++) {
-    wait_vmcnt<(C::STAGES - 2) * C::LOADS>();
-    __syncthreads();
-    issue(min(kt + C::STAGES - 1, nk - 1), nbuf);
+  // operand fragments of one step: a[ks][m] (token blocks), b[ks][j][plane] (expert blocks)
+  struct Frag { bf16x8 a[2][2]; bf16x8 b[2][4][NPLANES]; };
+  // fp32 sums of one 128-element chunk: h from the hi plane, l from mid + lo
+  struct Acc { f32x4 h[2][4]; f32x4 l[2][4]; };
+  auto read_frags = [&](Frag& f, int buf) __attribute__((always_inline)) {
     const uint8_t* U = lds + buf * C::STAGE;
     const uint8_t* Ep = U + C::U_BYTES;
-    f32x4 acc[2][4], acs[2][4];
-#pragma unroll
-    for (int m = 0; m < 2; m++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) acc[m][j] = acs[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
-      const bf16x8 a0 = *(const bf16x8*)(U + (wave * 32) * 128 + roff[ks]);
-      const bf16x8 a1 = *(const bf16x8*)(U + (wave * 32 + 16) * 128 + roff[ks]);
+      f.a[ks][0] = *(const bf16x8*)(U + (wave * 32) * 128 + roff[ks]);
+      f.a[ks][1] = *(const bf16x8*)(U + (wave * 32 + 16) * 128 + roff[ks]);
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        if (NPLANES == 1) {
-          const bf16x8 B = *(const bf16x8*)(Ep + (j * 16) * 128 + roff[ks]);
-          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, B, acc[0][j], 0, 0, 0);
-          acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, B, acc[1][j], 0, 0, 0);
-        } else {
-          const bf16x8 h = *(const bf16x8*)(Ep + (j * 16) * 128 + roff[ks]);
-          const bf16x8 md = *(const bf16x8*)(Ep + C::E_BYTES + (j * 16) * 128 + roff[ks]);
-          const bf16x8 lo = *(const bf16x8*)(Ep + 2 * C::E_BYTES + (j * 16) * 128 + roff[ks]);
-          acs[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, lo, acs[0][j], 0, 0, 0);
-          acs[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, lo, acs[1][j], 0, 0, 0);
-          acs[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, md, acs[0][j], 0, 0, 0);
-          acs[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, md, acs[1][j], 0, 0, 0);
-          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, h, acc[0][j], 0, 0, 0);
-          acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, h, acc[1][j], 0, 0, 0);
-        }
-      }
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int p = 0; p < NPLANES; p++)
+          f.b[ks][j][p] = *(const bf16x8*)(Ep + p * C::E_BYTES + (j * 16) * 128 + roff[ks]);
     }
+  };
+  // one step's MFMAs; FIRST starts a chunk (the accumulators restart from zero)
+  auto mma = [&](auto first_tag, Acc& A, const Frag& f) __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first_tag)::value;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int m = 0; m < 2; m++) {
+          const bool z = FIRST && ks == 0;
+          if constexpr (NPLANES > 1) {
+            A.l[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[ks][m], f.b[ks][j][2], z ? zero : A.l[m][j], 0, 0, 0);
+            A.l[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[ks][m], f.b[ks][j][1], A.l[m][j], 0, 0, 0);
+          }
+          A.h[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[ks][m], f.b[ks][j][0], z ? zero : A.h[m][j], 0, 0, 0);
+        }
+  };
+  auto fold = [&](const Acc& A) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < 2; m++)
 #pragma unroll
       for (int j = 0; j < 4; j++)
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-          z64[m][j][r] += (double)acc[m][j][r];
-          if (NPLANES > 1) z64[m][j][r] += (double)acs[m][j][r];
+          z64[m][j][r] += (double)A.h[m][j][r];
+          if (NPLANES > 1) z64[m][j][r] += (double)A.l[m][j][r];
         }
-    buf = buf + 1 == C::STAGES ? 0 : buf + 1;
-    nbuf = nbuf + 1 == C::STAGES ? 0 : nbuf + 1;
+  };
+
+  // Ring of S stage buffers, software-pipelined: step kt waits for stage kt+1
+  // (S-2 younger stages may stay in flight) and for its own LDS reads of stage
+  // kt, then a barrier (every wave holds stage kt in registers and sees stage
+  // kt+1 in LDS); it refills stage kt's buffer with step kt+S, reads stage
+  // kt+1's fragments (after the last step: the re-read copy, unused) and runs
+  // stage kt's MFMAs. Chunks of 128 elements (two
+  // steps) alternate between two accumulator sets, and a chunk's fp32 sums are
+  // folded into fp64 (in chunk order) during the first step of the next chunk,
+  // so LDS reads, MFMAs and the fp64 work of different steps overlap. Loads
+  // past the last step re-read it into buffers that are never read again, so
+  // the count per step is fixed.
+  constexpr int S = C::STAGES;
+  // three planes: the next fragments are read after this step's MFMAs, and one
+  // accumulator set is used, so the registers of one fragment set and one
+  // accumulator set suffice
+  constexpr bool kEarlyReads = NPLANES == 1;
+  const int nk = d / LG_BK;                    // even: d % 128 == 0
+  Frag F0, F1;
+  Acc A0, A1;
+#pragma unroll
+  for (int m = 0; m < 2; m++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) A1.h[m][j] = A1.l[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < S; p++) issue(min(p, nk - 1), p);
+  wait_vmcnt<(S - 1) * C::LOADS>();
+  __syncthreads();
+  read_frags(F0, 0);
+  auto step = [&](auto first_tag, auto fold_tag, Acc& acc, const Acc& prev, const Frag& cur, Frag& nxt, int kt)
+      __attribute__((always_inline)) {
+    wait_vmcnt_lgkm0<(S - 2) * C::LOADS>();
+    __syncthreads();
+    issue(min(kt + S, nk - 1), kt % S);
+    if (kEarlyReads) {
+      read_frags(nxt, (kt + 1) % S);
+      __builtin_amdgcn_sched_barrier(0);     // the reads go out before the MFMAs
+    }
+    mma(first_tag, acc, cur);
+    if constexpr (decltype(fold_tag)::value) fold(prev);
+    if (!kEarlyReads) {
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(nxt, (kt + 1) % S);
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int kt = 0;
+  if constexpr (kEarlyReads) {
+    for (; kt + 4 <= nk; kt += 4) {
+      step(T_{}, T_{}, A0, A1, F0, F1, kt);
+      step(F_{}, F_{}, A0, A1, F1, F0, kt + 1);
+      step(T_{}, T_{}, A1, A0, F0, F1, kt + 2);
+      step(F_{}, F_{}, A1, A0, F1, F0, kt + 3);
+    }
+    if (kt < nk) {                             // nk % 4 == 2: one more chunk
+      step(T_{}, T_{}, A0, A1, F0, F1, kt);
+      step(F_{}, F_{}, A0, A1, F1, F0, kt + 1);
+      fold(A0);
+    } else {
+      fold(A1);
+    }
+  } else {
+    // three planes: one accumulator set, each chunk folded right after its second step
+    for (; kt < nk; kt += 2) {
+      step(T_{}, F_{}, A0, A0, F0, F1, kt);
+      step(F_{}, F_{}, A0, A0, F1, F0, kt + 1);
+      fold(A0);
+    }
   }
   wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
 
@@ -531,6 +664,35 @@ hipError_t launch_route_two_phase(const RouteArgs& a, void* scratch, hipStream_t
   return launch_route(b, kFrontScoresIn, s);
 }
 
+// Per-expert loads from the selections. The router kernels add no counts
+// themselves: thousands of workgroups adding into the same N counters
+// serialise on those addresses. Here each of a few workgroups histograms a
+// contiguous slice of idx in LDS and adds its nonzero bins, so each counter
+// takes at most gridDim.x global atomics.
+__global__ __launch_bounds__(256) void count_loads_kernel(const int32_t* __restrict__ idx, long n, int N,
+                                                          int32_t* __restrict__ counts) {
+  __shared__ int h[RT_NMAX];
+  for (int e = threadIdx.x; e < N; e += 256) h[e] = 0;
+  __syncthreads();
+  const long per = (n + gridDim.x - 1) / gridDim.x;
+  const long lo = (long)blockIdx.x * per, hi = lo + per < n ? lo + per : n;
+  for (long i = lo + threadIdx.x; i < hi; i += 256) {
+    const int e = idx[i];
+    if ((unsigned)e < (unsigned)N) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += 256)
+    if (h[e]) atomicAdd(&counts[e], h[e]);
+}
+
+hipError_t launch_count_loads(const int32_t* idx, long n, int N, int32_t* counts, hipStream_t s) {
+  hipError_t e = launch_fill_i32(counts, 0, N, s);
+  if (e != hipSuccess || n <= 0) return e;
+  const int blocks = (int)std::min<long>(cdiv<long>(n, 2048), 32);
+  count_loads_kernel<<<blocks, 256, 0, s>>>(idx, n, N, counts);
+  return hipGetLastError();
+}
+
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, long n) {
   for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
     p[i] = v;
@@ -544,8 +706,6 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, long n, hipStream_t s) {
 }
 
 hipError_t launch_route(const RouteArgs& a, int front, hipStream_t s) {
-  hipError_t e = launch_fill_i32(a.counts, 0, a.n_routed, s);
-  if (e != hipSuccess) return e;
   const dim3 grid(cdiv(a.T, RT_BT));
   const bool ub = a.in_dtype == MOE_BF16;
   switch (front) {
@@ -564,7 +724,9 @@ hipError_t launch_route(const RouteArgs& a, int front, hipStream_t s) {
       else route_kernel<kFrontF64, false, false><<<grid, RT_THREADS, 0, s>>>(a);
     }
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.counts) return e;
+  return launch_count_loads(a.idx, (long)a.T * a.top_k, a.n_routed, a.counts, s);
 }
 
 }  // namespace moe
