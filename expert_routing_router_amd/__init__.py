@@ -15,7 +15,7 @@ from ._lib import (  # noqa: F401
     moe_validate, moe_workspace_bytes, moe_expert_ffn_workspace_bytes,
     moe_route, moe_permute, moe_expert_ffn, moe_combine, moe_update_bias, moe_forward,
     moe_quantize_fp8, moe_seq_balance_workspace_bytes, moe_seq_balance_loss,
-    moe_transpose_expert_weights, moe_backward_workspace_bytes, moe_backward, make_grads,
+    moe_transpose_expert_weights, moe_pack_expert_weights, moe_backward_workspace_bytes, moe_backward, make_grads,
     moe_capacity_workspace_bytes, moe_capacity_mask, moe_forward_capacity,
     moe_profile_enable, moe_profile_read, STAGES,
     moe_calibrate_read, moe_calibrate_mfma_bf16, MOE_CAL_MFMA_WAVES,

@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "moe_rocm.h")
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_QUANT_ACT_1x128, MOE_QUANT_W_128x128 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 
 
@@ -42,7 +42,7 @@ class MoeDesc(ctypes.Structure):
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "centroids", "w13", "w2", "w13_shared", "w2_shared", "w13_scale", "w2_scale",
-        "w13_shared_scale", "w2_shared_scale")]
+        "w13_shared_scale", "w2_shared_scale", "w13_blk", "w2_blk", "w13_shared_blk", "w2_shared_blk")]
 
 
 class MoeGrads(ctypes.Structure):
@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
             "moe_quantize_fp8": ([I32, P, I32, I32, I32, P, P, P], I32),
             "moe_seq_balance_workspace_bytes": ([D, I32], SZ),
             "moe_transpose_expert_weights": ([D, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeights), P], I32),
+            "moe_pack_expert_weights": ([D, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeights), P], I32),
             "moe_backward_workspace_bytes": ([D], SZ),
             "moe_backward": ([D, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeights), P, P, P,
                               ctypes.POINTER(MoeGrads), P, SZ, P], I32),
@@ -264,6 +265,11 @@ def moe_transpose_expert_weights(desc, weights: MoeWeights, wt: MoeWeights, stre
         ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(wt), _stream(stream)))
 
 
+def moe_pack_expert_weights(desc, weights: MoeWeights, wb: MoeWeights, stream=None):
+    _check("moe_pack_expert_weights", lib().moe_pack_expert_weights(
+        ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(wb), _stream(stream)))
+
+
 def moe_backward_workspace_bytes(desc) -> int:
     return lib().moe_backward_workspace_bytes(ctypes.byref(desc))
 
@@ -309,8 +315,11 @@ def moe_profile_read(reset=True):
 
 
 def make_weights(centroids, w13, w2, w13_shared=None, w2_shared=None, w13_scale=None,
-                 w2_scale=None, w13_shared_scale=None, w2_shared_scale=None) -> MoeWeights:
+                 w2_scale=None, w13_shared_scale=None, w2_shared_scale=None, w13_blk=None, w2_blk=None,
+                 w13_shared_blk=None, w2_shared_blk=None) -> MoeWeights:
     return MoeWeights(*[_ptr(t, n, False) for t, n in (
         (centroids, "centroids"), (w13, "w13"), (w2, "w2"), (w13_shared, "w13_shared"),
         (w2_shared, "w2_shared"), (w13_scale, "w13_scale"), (w2_scale, "w2_scale"),
-        (w13_shared_scale, "w13_shared_scale"), (w2_shared_scale, "w2_shared_scale"))])
+        (w13_shared_scale, "w13_shared_scale"), (w2_shared_scale, "w2_shared_scale"),
+        (w13_blk, "w13_blk"), (w2_blk, "w2_blk"), (w13_shared_blk, "w13_shared_blk"),
+        (w2_shared_blk, "w2_shared_blk"))])

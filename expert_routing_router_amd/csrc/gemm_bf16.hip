@@ -287,30 +287,38 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
   const int row0 = seg_begin + mtile * BM;
   const int mvalid = min(BM, seg_end - row0);
   const int K = a.K;
+  const int mt = sprefix[seg] + mtile;                // this m-tile's index over all segments
   const uint16_t* wbase = seg < a.n_first
       ? (const uint16_t*)a.w0 + (size_t)seg * a.wstride0
       : (const uint16_t*)a.w1 + (size_t)(seg - a.n_first) * a.wstride1;
+  const bool xblk = a.x_blocked, wblk = a.w_blocked;
 
   // ---- per-lane global offsets of this wave's blocks (fixed over K). Block
   // wave + 8i starts at row RPB*(wave + 8i); the +8i part leaves the swizzle unchanged.
   const int brow = lane / C::CPR;                              // row within a block
   const int bchunk = (lane % C::CPR) ^ (((C::RPB * wave + brow) >> C::SH) & (C::CPR - 1));
-  const i32x4 xr = rsrc_words(a.x, a.x_rows * (long)K * 2);
-  const i32x4 wr = rsrc_words(wbase, (long)(SWIGLU ? 2 * a.N : a.N) * K * 2);
+  // K-blocked operands: the tile's block is the buffer (rows past mvalid hold
+  // padding, whose products only reach output rows that are not stored), and
+  // block i of a stage is its kilobyte i; else rows are addressed in place
+  const i32x4 xr = xblk ? rsrc_words((const uint16_t*)a.x + (size_t)mt * BM * K, (long)BM * K * 2)
+                        : rsrc_words(a.x, a.x_rows * (long)K * 2);
+  const i32x4 wr = wblk ? rsrc_words(wbase + (size_t)ntile * BN * K, (long)BN * K * 2)
+                        : rsrc_words(wbase, (long)(SWIGLU ? 2 * a.N : a.N) * K * 2);
+  const int astep = xblk ? BM * RB : RB, bstep = wblk ? BN * RB : RB;   // bytes per K step
   int aoff[C::A_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::A_PER_WAVE; i++) {
     const int r = (wave + 8 * i) * C::RPB + brow;   // blocks past A_BLOCKS are never issued
     const int rr = min(max(row0 + min(r, mvalid - 1), 0), a.rows_bound - 1);   // in range for any offsets
     const int src = a.row_index ? a.row_index[rr] : rr;
-    aoff[i] = r < mvalid ? (src * K + bchunk * 8) * 2 : kOutOfRange;
+    aoff[i] = xblk ? (wave + 8 * i) * 1024 + lane * 16 : r < mvalid ? (src * K + bchunk * 8) * 2 : kOutOfRange;
   }
   int boff[C::B_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::B_PER_WAVE; i++) {
     const int r = (wave + 8 * i) * C::RPB + brow;   // 0 .. BN-1
     const int wrow = SWIGLU ? (r < HN ? ntile * HN + r : a.N + ntile * HN + (r - HN)) : ntile * BN + r;
-    boff[i] = (wrow * K + bchunk * 8) * 2;
+    boff[i] = wblk ? (wave + 8 * i) * 1024 + lane * 16 : (wrow * K + bchunk * 8) * 2;
   }
   const uint32_t lds0 = lds_addr(lds);
   constexpr int A_EXTRA = C::A_EXTRA;           // waves below this issue A_PER_WAVE blocks
@@ -319,13 +327,12 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
   // blocks first (the last one only on waves that have it), then its B blocks.
   auto issue_part = [&](auto p_tag, int kt, int buf) __attribute__((always_inline)) {
     constexpr int P = decltype(p_tag)::value;
-    const int soff = kt * RB;
     const uint32_t sbase = lds0 + buf * C::STAGE;
     if constexpr (P < C::A_PER_WAVE) {
-      if (P < C::A_PER_WAVE - 1 || a_full) dma_b128(xr, aoff[P], soff, sbase + (wave + 8 * P) * 1024);
+      if (P < C::A_PER_WAVE - 1 || a_full) dma_b128(xr, aoff[P], kt * astep, sbase + (wave + 8 * P) * 1024);
     } else if constexpr (P < C::A_PER_WAVE + C::B_PER_WAVE) {
       constexpr int Q = P - C::A_PER_WAVE;
-      dma_b128(wr, boff[Q], soff, sbase + C::A_BYTES + (wave + 8 * Q) * 1024);
+      dma_b128(wr, boff[Q], kt * bstep, sbase + C::A_BYTES + (wave + 8 * Q) * 1024);
     }
   };
   constexpr int NPARTS = C::A_PER_WAVE + C::B_PER_WAVE;
@@ -442,6 +449,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
   }
 
   uint16_t* out = (uint16_t*)a.out;
+  // K-blocked H (SwiGLU only): this wave's 32 columns are one 32-element step of the down GEMM
+  uint16_t* hblk = out + ((size_t)mt * (a.N / 32) + (ntile * HN + wn * 32) / 32) * BM * 32;
 #pragma unroll
   for (int i = 0; i < MB; i++) {
     if (i < mb_active) {
@@ -450,7 +459,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
         const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
         if (row < mvalid && (unsigned)(row0 + row) < (unsigned)a.rows_bound) {
           uint16_t* orow = out + (size_t)(row0 + row) * a.N;
-          if (SWIGLU) {
+          if (SWIGLU && a.out_blocked) {
+            hblk[row * 32 + (((l32 >> 3) ^ ((row >> 2) & 3)) << 3) + (l32 & 7)] =
+                f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
+          } else if (SWIGLU) {
             orow[ntile * HN + wn * 32 + l32] = f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
           } else {
             const int col = ntile * BN + wn * 64 + l32;
@@ -562,6 +574,7 @@ static hipError_t launch_any(const GemmArgs& a, int dtype, int bm, hipStream_t s
     // 256 weight rows per tile (8 waves) when the output width allows it,
     // else 128 (4 waves)
     const bool wide = SWIGLU ? a.N % 128 == 0 : a.N % 256 == 0;
+    if ((a.w_blocked || a.x_blocked || a.out_blocked) && (!wide || a.K % 32)) return hipErrorInvalidValue;
     if (bm == 64) return wide ? launch_bf16_dma<1, SWIGLU>(a, s) : hipErrorInvalidValue;
     if (bm == 128) return wide ? launch_bf16_dma<2, SWIGLU>(a, s) : hipErrorInvalidValue;
     if (bm == 256) return wide ? launch_bf16_dma<4, SWIGLU>(a, s) : launch_bf16<4, 2, SWIGLU>(a, s);
@@ -570,6 +583,40 @@ static hipError_t launch_any(const GemmArgs& a, int dtype, int bm, hipStream_t s
   }
   return hipErrorInvalidValue;
 }
+
+// ---------------------------------------------------------------- K-blocked weights
+// dst[mat][tile][step][256 rows][32 elements]: row r of a tile stores its
+// 16-byte chunk c of the step at slot c ^ ((r >> 2) & 3), which is where the
+// LDS-DMA kernel's lane for that slot fetches it from a row-major operand.
+__global__ void pack_blocked_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, long n_chunks,
+                                    int rows, int K, int swiglu_i) {
+  const int steps = K / 32, tiles = rows / 256;
+  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < n_chunks; q += (long)gridDim.x * blockDim.x) {
+    const int slot = (int)(q & 3);
+    const int r = (int)((q >> 2) & 255);
+    long rest = q >> 10;
+    const int kt = (int)(rest % steps);
+    rest /= steps;
+    const int t = (int)(rest % tiles);
+    const long mat = rest / tiles;
+    const int srow = swiglu_i > 0 ? (r < 128 ? t * 128 + r : swiglu_i + t * 128 + (r - 128)) : t * 256 + r;
+    const int c = slot ^ ((r >> 2) & 3);
+    const i32x4 v = *(const i32x4*)(src + ((size_t)mat * rows + srow) * K + kt * 32 + c * 8);
+    *(i32x4*)(dst + (size_t)q * 8) = v;
+  }
+}
+
+hipError_t launch_pack_blocked(const uint16_t* src, uint16_t* dst, int n_mat, int rows, int K, int swiglu_i,
+                               hipStream_t s) {
+  if (rows % 256 || K % 32 || (swiglu_i > 0 && rows != 2 * swiglu_i)) return hipErrorInvalidValue;
+  const long n_chunks = (long)n_mat * rows * (K / 8);
+  if (n_chunks <= 0) return hipSuccess;
+  const int blocks = (int)std::min<long>(cdiv<long>(n_chunks, 256), 8192);
+  pack_blocked_kernel<<<blocks, 256, 0, s>>>(src, dst, n_chunks, rows, K, swiglu_i);
+  return hipGetLastError();
+}
+
+long blocked_rows(long rows_bound, int n_seg, int bm) { return (rows_bound / bm + n_seg) * (long)bm; }
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, bool swiglu, int bm, hipStream_t s);
 

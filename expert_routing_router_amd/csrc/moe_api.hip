@@ -164,6 +164,22 @@ static bool two_phase_router(const moe_desc_t* d) {
 
 static bool fused_shared(const moe_desc_t* d) { return d->n_shared == 0 || d->inter == d->inter_shared; }
 
+// rows of H: bf16 experts may store H K-blocked (each m-tile padded to its tile
+// height, at most kMaxTileRows), for the routed and shared passes together
+constexpr size_t kMaxTileRows = 320;
+static size_t h_rows(const moe_desc_t* d, size_t rows, size_t n_seg) {
+  return d->expert_dtype == MOE_BF16 ? rows + (n_seg + 1) * kMaxTileRows : rows;
+}
+
+// K-blocked weights apply to bf16 experts whose products all take the LDS-DMA kernel
+static bool blocked_ok(const moe_desc_t* d) {
+  const bool shared_ok = d->n_shared == 0 || d->inter_shared % 128 == 0;
+  return d->expert_dtype == MOE_BF16 && d->inter % 128 == 0 && d->d % 256 == 0 && shared_ok;
+}
+static bool use_blocked(const moe_desc_t* d, const moe_weights_t* w) {
+  return blocked_ok(d) && w->w13_blk && w->w2_blk && (d->n_shared == 0 || (w->w13_shared_blk && w->w2_shared_blk));
+}
+
 static Ws layout(const moe_desc_t* d, bool capacity = false) {
   Ws w;
   const size_t T = d->T, K = d->top_k, N = d->n_routed, Ns = d->n_shared;
@@ -186,7 +202,7 @@ static Ws layout(const moe_desc_t* d, bool capacity = false) {
   w.slot_row = take(T * K * 4);
   w.offs_s = take((Ns + 1) * 4);
   w.mtile_s = take((Ns + 1) * 4);
-  w.H = take(R * Imax * hy);
+  w.H = take(h_rows(d, R, n_seg) * Imax * hy);
   w.Y = take(R * (size_t)d->d * yy);
   if (d->expert_dtype == MOE_FP8_E4M3) {
     w.qu = take(T * d->d);
@@ -306,11 +322,12 @@ static GemmArgs gemm_args(const void* x, long x_rows, const float* xs, const int
 }
 
 // GEMM1 + (FP8: quantise H) + GEMM2 over one set of segments.
+// blocked: w13/w13b/w2/w2b are K-blocked copies (bf16); H is then written and read K-blocked.
 static int run_ffn(const moe_desc_t* d, int inter, const void* x, long x_rows, const float* xs, const int32_t* ridx,
                    const int32_t* offsets, const int32_t* mtile, int n_seg, int rows_bound,
                    const void* w13, const float* s13, const void* w13b, const float* s13b,
                    const void* w2, const float* s2, const void* w2b, const float* s2b, int n_first,
-                   void* H, uint8_t* qh, float* sh, void* Y, int bm, hipStream_t s) {
+                   void* H, uint8_t* qh, float* sh, void* Y, int bm, hipStream_t s, bool blocked = false) {
   const int dt = d->expert_dtype;
   const bool f8 = dt == MOE_FP8_E4M3;
   const long ws13 = 2L * inter * d->d, ws2 = (long)d->d * inter;
@@ -318,6 +335,7 @@ static int run_ffn(const moe_desc_t* d, int inter, const void* x, long x_rows, c
   GemmArgs g1 = gemm_args(x, x_rows, xs, ridx, offsets, mtile, n_seg, w13, s13, ws13, ss13, H, inter, d->d,
                           rows_bound);
   g1.w1 = w13b; g1.ws1 = s13b; g1.n_first = n_first;
+  g1.w_blocked = g1.out_blocked = blocked;
   MOE_TRY(launch_gemm_swiglu(g1, dt, bm, s));
   prof_mark(MOE_STAGE_GEMM1, s);
   const void* x2 = H;
@@ -330,6 +348,7 @@ static int run_ffn(const moe_desc_t* d, int inter, const void* x, long x_rows, c
   GemmArgs g2 = gemm_args(x2, rows_bound, xs2, nullptr, offsets, mtile, n_seg, w2, s2, ws2, ss2, Y, d->d, inter,
                           rows_bound);
   g2.w1 = w2b; g2.ws1 = s2b; g2.n_first = n_first;
+  g2.w_blocked = g2.x_blocked = blocked;
   MOE_TRY(launch_gemm_down(g2, dt, bm, s));
   prof_mark(MOE_STAGE_GEMM2, s);
   return MOE_OK;
@@ -511,16 +530,21 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
 
   // 4. experts
   const void* y_shared = nullptr;
+  const bool blk = use_blocked(d, w);
+  const void* w13r = blk ? w->w13_blk : w->w13;
+  const void* w2r = blk ? w->w2_blk : w->w2;
+  const void* w13s = blk ? w->w13_shared_blk : w->w13_shared;
+  const void* w2s = blk ? w->w2_shared_blk : w->w2_shared;
   if (fused) {
     int st2 = run_ffn(d, d->inter, x, T, xs, row_token, offsets, mtile, N + Ns, (int)(TK + (long)Ns * T),
-                      w->w13, w->w13_scale, Ns ? w->w13_shared : w->w13, Ns ? w->w13_shared_scale : w->w13_scale,
-                      w->w2, w->w2_scale, Ns ? w->w2_shared : w->w2, Ns ? w->w2_shared_scale : w->w2_scale, N,
-                      H, qh, shs, Y, bm, s);
+                      w13r, w->w13_scale, Ns ? w13s : w13r, Ns ? w->w13_shared_scale : w->w13_scale,
+                      w2r, w->w2_scale, Ns ? w2s : w2r, Ns ? w->w2_shared_scale : w->w2_scale, N,
+                      H, qh, shs, Y, bm, s, blk);
     if (st2) return st2;
     if (Ns) y_shared = Y + (size_t)TK * d->d * yy;
   } else {
-    int st2 = run_ffn(d, d->inter, x, T, xs, row_token, offsets, mtile, N, (int)TK, w->w13, w->w13_scale, w->w13,
-                      w->w13_scale, w->w2, w->w2_scale, w->w2, w->w2_scale, N, H, qh, shs, Y, bm, s);
+    int st2 = run_ffn(d, d->inter, x, T, xs, row_token, offsets, mtile, N, (int)TK, w13r, w->w13_scale, w13r,
+                      w->w13_scale, w2r, w->w2_scale, w2r, w->w2_scale, N, H, qh, shs, Y, bm, s, blk);
     if (st2) return st2;
   }
   if (!fused && Ns > 0) {
@@ -530,13 +554,13 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
     MOE_TRY(hipGetLastError());
     const int bms = gemm_bm(d->expert_dtype, T, d->d, d->inter_shared);
     if (d->expert_dtype != MOE_F32) MOE_TRY(launch_mtile_prefix(offs_s, Ns, bms, mtile_s, s));
-    uint8_t* Hs = H + (size_t)TK * (d->inter > d->inter_shared ? d->inter : d->inter_shared) * hy;
+    uint8_t* Hs = H + h_rows(d, TK, N) * (d->inter > d->inter_shared ? d->inter : d->inter_shared) * hy;
     uint8_t* Ys = Y + (size_t)TK * d->d * yy;
     uint8_t* qhs = f8 ? qh + (size_t)TK * d->inter : nullptr;
     float* shss = f8 ? shs + (size_t)TK * (d->inter / 128) : nullptr;
-    int st2 = run_ffn(d, d->inter_shared, x, T, xs, row_token + TK, offs_s, mtile_s, Ns, Ns * T, w->w13_shared,
-                  w->w13_shared_scale, w->w13_shared, w->w13_shared_scale, w->w2_shared, w->w2_shared_scale,
-                  w->w2_shared, w->w2_shared_scale, Ns, Hs, qhs, shss, Ys, bms, s);
+    int st2 = run_ffn(d, d->inter_shared, x, T, xs, row_token + TK, offs_s, mtile_s, Ns, Ns * T, w13s,
+                      w->w13_shared_scale, w13s, w->w13_shared_scale, w2s, w->w2_shared_scale,
+                      w2s, w->w2_shared_scale, Ns, Hs, qhs, shss, Ys, bms, s, blk);
     if (st2) return st2;
     y_shared = Ys;
   }
@@ -686,6 +710,27 @@ extern "C" int moe_transpose_expert_weights(const moe_desc_t* d, const moe_weigh
   if (d->n_shared) {
     MOE_TRY(launch_transpose(w->w13_shared, (void*)wt->w13_shared, d->n_shared, 2 * I, D, dt, s));
     MOE_TRY(launch_transpose(w->w2_shared, (void*)wt->w2_shared, d->n_shared, D, I, dt, s));
+  }
+  return MOE_OK;
+}
+
+extern "C" int moe_pack_expert_weights(const moe_desc_t* d, const moe_weights_t* w, moe_weights_t* wb,
+                                       moe_stream_t stream) {
+  int st = moe_validate(d);
+  if (st) return st;
+  if (!blocked_ok(d)) return MOE_ENOTSUP;
+  if (!w || !wb || !aligned(w->w13) || !aligned(w->w2) || !aligned(wb->w13) || !aligned(wb->w2)) return MOE_EINVAL;
+  if (d->n_shared && (!aligned(w->w13_shared) || !aligned(w->w2_shared) || !aligned(wb->w13_shared) ||
+                      !aligned(wb->w2_shared)))
+    return MOE_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  const int I = d->inter, Is = d->inter_shared, D = d->d;
+  auto u16 = [](const void* p) { return (const uint16_t*)p; };
+  MOE_TRY(launch_pack_blocked(u16(w->w13), (uint16_t*)wb->w13, d->n_routed, 2 * I, D, I, s));
+  MOE_TRY(launch_pack_blocked(u16(w->w2), (uint16_t*)wb->w2, d->n_routed, D, I, 0, s));
+  if (d->n_shared) {
+    MOE_TRY(launch_pack_blocked(u16(w->w13_shared), (uint16_t*)wb->w13_shared, d->n_shared, 2 * Is, D, Is, s));
+    MOE_TRY(launch_pack_blocked(u16(w->w2_shared), (uint16_t*)wb->w2_shared, d->n_shared, D, Is, 0, s));
   }
   return MOE_OK;
 }

@@ -71,7 +71,19 @@ struct GemmArgs {
   int N;                      // output columns (I for the SwiGLU GEMM, d for down)
   int K;                      // reduction length
   int rows_bound;             // upper bound on total rows (grid sizing)
+  // K-blocked operands (bf16 LDS-DMA kernel only): a tile's rows are stored per 32-element
+  // step as [step][tile rows][64 B] with the kernel's LDS chunk swizzle applied, so each
+  // 1 KB load instruction reads one contiguous kilobyte.
+  int w_blocked = 0;          // w0/w1: moe_pack_expert_weights layout
+  int x_blocked = 0;          // x: per m-tile (mtile_prefix numbering) blocks of BM rows, K = this GEMM's K
+  int out_blocked = 0;        // SwiGLU output H written in the x_blocked layout of the down GEMM
 };
+// rows of a K-blocked activation buffer: every m-tile padded to bm rows
+long blocked_rows(long rows_bound, int n_seg, int bm);
+// bf16 weights [n_mat][rows][K] -> K-blocked tiles of 256 rows; swiglu_i > 0: rows = 2*swiglu_i and
+// tile t holds gate rows t*128.. and up rows swiglu_i + t*128..
+hipError_t launch_pack_blocked(const uint16_t* src, uint16_t* dst, int n_mat, int rows, int K, int swiglu_i,
+                               hipStream_t s);
 int gemm_bm(int dtype, int mean_rows, int dmodel, int inter);
 hipError_t launch_gemm_swiglu(const GemmArgs& a, int dtype, int bm, hipStream_t s);
 hipError_t launch_gemm_down(const GemmArgs& a, int dtype, int bm, hipStream_t s);

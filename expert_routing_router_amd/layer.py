@@ -7,6 +7,7 @@ needs a second full host copy. All arithmetic happens in libmoe_rocm.so.
 """
 
 from concurrent.futures import ThreadPoolExecutor
+import ctypes
 import os
 
 import numpy as np
@@ -25,10 +26,12 @@ def np_to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
 
 
 class MoELayer:
-    def __init__(self, cfg, gen, device="cuda", threads=0):
+    def __init__(self, cfg, gen, device="cuda", threads=0, blocked_weights=True):
         """cfg: layer configuration (T, d, N_r, ... dtypes); gen: the input source, an object
         with centroids(cfg), expert_w13(cfg, e), expert_w2(cfg, e), shared_w13(cfg, s),
-        shared_w2(cfg, s) returning numpy arrays (bf16 bits as uint16, or fp32)."""
+        shared_w2(cfg, s) returning numpy arrays (bf16 bits as uint16, or fp32).
+        blocked_weights: also keep K-blocked copies of bf16 expert weights (moe_pack_expert_weights)
+        for the forward, where the shapes allow it; self.blocked says whether they are in use."""
         self.cfg = cfg
         self.device = torch.device(device)
         self.desc = L.desc_from_config(cfg)
@@ -85,6 +88,9 @@ class MoELayer:
                                       self.s13, self.s2,
                                       self.s13s if cfg.n_shared else None,
                                       self.s2s if cfg.n_shared else None)
+        self.blocked = False
+        if blocked_weights and cfg.expert_dtype == "bf16":
+            self._pack_weights()
         self.ws = torch.empty(L.moe_workspace_bytes(self.desc), dtype=torch.uint8, device=dev)
         T, K = cfg.T, cfg.top_k
         self.idx = torch.empty((T, K), dtype=torch.int32, device=dev)
@@ -92,6 +98,25 @@ class MoELayer:
         self.counts = torch.empty(cfg.n_routed, dtype=torch.int32, device=dev)
         iodt = torch.bfloat16 if cfg.in_dtype == "bf16" else torch.float32
         self.out = torch.empty((T, d), dtype=iodt, device=dev)
+
+    def _pack_weights(self):
+        sh = self.cfg.n_shared > 0
+        blk = [torch.empty_like(t) for t in (self.w13, self.w2)] + \
+              ([torch.empty_like(t) for t in (self.w13s, self.w2s)] if sh else [None, None])
+        wb = L.make_weights(None, *blk)
+        st = L.lib().moe_pack_expert_weights(ctypes.byref(self.desc), ctypes.byref(self.weights),
+                                             ctypes.byref(wb), None)
+        if st == L.MOE_ENOTSUP:
+            return
+        if st != L.MOE_OK:
+            raise L.MoeError("moe_pack_expert_weights", st, L.lib())
+        torch.cuda.synchronize(self.device)
+        self._blk = blk
+        w = self.weights
+        w.w13_blk, w.w2_blk = blk[0].data_ptr(), blk[1].data_ptr()
+        if sh:
+            w.w13_shared_blk, w.w2_shared_blk = blk[2].data_ptr(), blk[3].data_ptr()
+        self.blocked = True
 
     def forward(self, u: torch.Tensor, b: torch.Tensor, update_bias=True, stream=None):
         L.moe_forward(self.desc, self.weights, u, b, self.out, self.ws, update_bias,

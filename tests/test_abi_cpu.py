@@ -22,14 +22,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = L.header_symbols()
-    assert len(names) == 25, names
+    assert len(names) == 26, names
     raw = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_strerror(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == L.ABI_VERSION == 2
     for st in (0, -1, -2, -3, -4):
         assert lib.moe_strerror(st)
     assert b"unknown" in lib.moe_strerror(7)
@@ -80,8 +80,9 @@ def test_descriptor_rules(lib, kw, want):
 
 def test_bad_abi_version(lib):
     d = _v3()
-    d.abi_version = 2
-    assert M.moe_validate(d) == M.MOE_EINVAL
+    for v in (1, 3):
+        d.abi_version = v
+        assert M.moe_validate(d) == M.MOE_EINVAL
     assert lib.moe_validate(None) == M.MOE_EINVAL
 
 
@@ -200,3 +201,21 @@ def test_backward_support_matrix(lib):
     st = lib.moe_backward(ctypes.byref(f8), ctypes.byref(w), ctypes.byref(w), A, A, A, ctypes.byref(g), A,
                           1 << 40, None)
     assert st == M.MOE_ENOTSUP
+
+
+def test_pack_arg_errors(lib):
+    """K-blocked weight copies exist for bf16 experts with I % 128 == 0, I_s % 128 == 0 and
+    d % 256 == 0 (MOE_ENOTSUP otherwise); misaligned pointers are refused before any launch."""
+    w = M.MoeWeights(A, A, A, A, A, None, None, None, None)
+    bad = M.MoeWeights(A, MIS, A, A, A, None, None, None, None)
+    pack = lambda d, src, dst: lib.moe_pack_expert_weights(ctypes.byref(d), ctypes.byref(src), ctypes.byref(dst), None)
+    ok = M.make_desc(T=64, d=512, n_routed=16, top_k=4, n_shared=1, inter=256)
+    assert pack(ok, w, bad) == M.MOE_EINVAL and pack(ok, bad, w) == M.MOE_EINVAL
+    for kw in (dict(inter=192), dict(d=384), dict(inter_shared=320),
+               dict(router_dtype="f32", expert_dtype="fp8")):
+        args = dict(T=64, d=512, n_routed=16, top_k=4, n_shared=1, inter=256)
+        args.update(kw)
+        assert pack(M.make_desc(**args), w, w) == M.MOE_ENOTSUP, kw
+    f32 = M.make_desc(T=64, d=512, n_routed=16, top_k=4, n_shared=1, inter=256, in_dtype="f32",
+                      router_dtype="f32", expert_dtype="f32")
+    assert pack(f32, w, w) == M.MOE_ENOTSUP
