@@ -315,7 +315,12 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
   const int bchunk = (lane & 7) ^ ((((wave & 1) << 2) + (lane >> 4)) & 7);   // block parity = wave parity
   const i32x4 xr = rsrc_words(a.x, a.x_rows * (long)K);
   const i32x4 sr = rsrc_words(a.x_scale, a.x_rows * (long)KB * 4);
-  const i32x4 wr = rsrc_words(wbase, (long)(SWIGLU ? 2 * a.N : a.N) * K);
+  // K-blocked weights (moe_pack_expert_weights): the tile's 256 rows per 128-element block are one
+  // contiguous 32 KB with this kernel's chunk swizzle applied, so block i of a stage is its kilobyte i
+  const bool wblk = a.w_blocked;
+  const i32x4 wr = wblk ? rsrc_words(wbase + (size_t)ntile * BN * K, (long)BN * K)
+                        : rsrc_words(wbase, (long)(SWIGLU ? 2 * a.N : a.N) * K);
+  const int bstep = wblk ? BN * F8_BK : F8_BK;
   int aoff[C::A_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::A_PER_WAVE; i++) {
@@ -336,7 +341,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
   for (int i = 0; i < C::B_PER_WAVE; i++) {
     const int r = (wave + 8 * i) * 8 + brow;
     const int wrow = SWIGLU ? (r < HN ? ntile * HN + r : a.N + ntile * HN + (r - HN)) : ntile * BN + r;
-    boff[i] = wrow * K + bchunk * 16;
+    boff[i] = wblk ? (wave + 8 * i) * 1024 + lane * 16 : wrow * K + bchunk * 16;
   }
   const uint32_t lds0 = lds_addr(lds);
   const bool sa_wave = wave < C::SA_WAVES;
@@ -347,7 +352,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
     for (int i = 0; i < C::A_PER_WAVE; i++) dma_b128(xr, aoff[i], koff, sbase + (wave + 8 * i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::B_PER_WAVE; i++)
-      dma_b128(wr, boff[i], koff, sbase + C::A_BYTES + (wave + 8 * i) * 1024);
+      dma_b128(wr, boff[i], kb * bstep, sbase + C::A_BYTES + (wave + 8 * i) * 1024);
     if (sa_wave) dma_b32(sr, soff_row, kb * 4, sbase + C::A_BYTES + C::B_BYTES + wave * 256);
   };
 
@@ -491,7 +496,39 @@ static hipError_t launch_fp8_t(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// dst[mat][tile][block][256 rows][128 bytes]: row r's 16-byte chunk c of a
+// 128-element block sits at slot c ^ ((r >> 1) & 7), where the LDS-DMA kernel's
+// lane for that slot fetches it from a row-major operand
+__global__ void pack_blocked_f8_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, long n_chunks,
+                                       int rows, int K, int swiglu_i) {
+  const int blocks = K / F8_BK, tiles = rows / 256;
+  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < n_chunks; q += (long)gridDim.x * blockDim.x) {
+    const int slot = (int)(q & 7);
+    const int r = (int)((q >> 3) & 255);
+    long rest = q >> 11;
+    const int kb = (int)(rest % blocks);
+    rest /= blocks;
+    const int t = (int)(rest % tiles);
+    const long mat = rest / tiles;
+    const int srow = swiglu_i > 0 ? (r < 128 ? t * 128 + r : swiglu_i + t * 128 + (r - 128)) : t * 256 + r;
+    const int c = slot ^ ((r >> 1) & 7);
+    *(i32x4*)(dst + (size_t)q * 16) = *(const i32x4*)(src + ((size_t)mat * rows + srow) * K + kb * F8_BK + c * 16);
+  }
+}
+
+hipError_t launch_pack_blocked_f8(const uint8_t* src, uint8_t* dst, int n_mat, int rows, int K, int swiglu_i,
+                                  hipStream_t s) {
+  if (rows % 256 || K % F8_BK || (swiglu_i > 0 && rows != 2 * swiglu_i)) return hipErrorInvalidValue;
+  const long n_chunks = (long)n_mat * rows * (K / 16);
+  if (n_chunks <= 0) return hipSuccess;
+  const int blocks = (int)std::min<long>(cdiv<long>(n_chunks, 256), 8192);
+  pack_blocked_f8_kernel<<<blocks, 256, 0, s>>>(src, dst, n_chunks, rows, K, swiglu_i);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_fp8(const GemmArgs& a, bool swiglu, int bm, hipStream_t s) {
+  // K-blocked weights only on the LDS-DMA kernel; blocked activations are a bf16 feature
+  if (a.x_blocked || a.out_blocked || (a.w_blocked && bm != 256)) return hipErrorInvalidValue;
   // 256-row tiles: the LDS-DMA kernel (needs the down GEMM's width a multiple of 256)
   if (bm == 256) return swiglu ? launch_fp8_dma<4, true>(a, s) : launch_fp8_dma<4, false>(a, s);
   if (bm == 192) return swiglu ? launch_fp8_t<3, true>(a, s) : launch_fp8_t<3, false>(a, s);

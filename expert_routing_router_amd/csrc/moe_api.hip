@@ -171,10 +171,12 @@ static size_t h_rows(const moe_desc_t* d, size_t rows, size_t n_seg) {
   return d->expert_dtype == MOE_BF16 ? rows + (n_seg + 1) * kMaxTileRows : rows;
 }
 
-// K-blocked weights apply to bf16 experts whose products all take the LDS-DMA kernel
+// K-blocked weights apply to bf16 and FP8 experts whose products all take the LDS-DMA kernels
+// (FP8: 256-row tiles, which gemm_bm picks when d % 256 == 0)
 static bool blocked_ok(const moe_desc_t* d) {
   const bool shared_ok = d->n_shared == 0 || d->inter_shared % 128 == 0;
-  return d->expert_dtype == MOE_BF16 && d->inter % 128 == 0 && d->d % 256 == 0 && shared_ok;
+  const bool dt_ok = d->expert_dtype == MOE_BF16 || d->expert_dtype == MOE_FP8_E4M3;
+  return dt_ok && d->inter % 128 == 0 && d->d % 256 == 0 && shared_ok;
 }
 static bool use_blocked(const moe_desc_t* d, const moe_weights_t* w) {
   return blocked_ok(d) && w->w13_blk && w->w2_blk && (d->n_shared == 0 || (w->w13_shared_blk && w->w2_shared_blk));
@@ -335,7 +337,8 @@ static int run_ffn(const moe_desc_t* d, int inter, const void* x, long x_rows, c
   GemmArgs g1 = gemm_args(x, x_rows, xs, ridx, offsets, mtile, n_seg, w13, s13, ws13, ss13, H, inter, d->d,
                           rows_bound);
   g1.w1 = w13b; g1.ws1 = s13b; g1.n_first = n_first;
-  g1.w_blocked = g1.out_blocked = blocked;
+  g1.w_blocked = blocked;
+  g1.out_blocked = blocked && !f8;             // FP8: H is quantised row-major by its own pass
   MOE_TRY(launch_gemm_swiglu(g1, dt, bm, s));
   prof_mark(MOE_STAGE_GEMM1, s);
   const void* x2 = H;
@@ -348,7 +351,8 @@ static int run_ffn(const moe_desc_t* d, int inter, const void* x, long x_rows, c
   GemmArgs g2 = gemm_args(x2, rows_bound, xs2, nullptr, offsets, mtile, n_seg, w2, s2, ws2, ss2, Y, d->d, inter,
                           rows_bound);
   g2.w1 = w2b; g2.ws1 = s2b; g2.n_first = n_first;
-  g2.w_blocked = g2.x_blocked = blocked;
+  g2.w_blocked = blocked;
+  g2.x_blocked = blocked && !f8;
   MOE_TRY(launch_gemm_down(g2, dt, bm, s));
   prof_mark(MOE_STAGE_GEMM2, s);
   return MOE_OK;
@@ -725,12 +729,16 @@ extern "C" int moe_pack_expert_weights(const moe_desc_t* d, const moe_weights_t*
     return MOE_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   const int I = d->inter, Is = d->inter_shared, D = d->d;
-  auto u16 = [](const void* p) { return (const uint16_t*)p; };
-  MOE_TRY(launch_pack_blocked(u16(w->w13), (uint16_t*)wb->w13, d->n_routed, 2 * I, D, I, s));
-  MOE_TRY(launch_pack_blocked(u16(w->w2), (uint16_t*)wb->w2, d->n_routed, D, I, 0, s));
+  auto pack = [&](const void* src, const void* dst, int n_mat, int rows, int K, int swiglu_i) {
+    return d->expert_dtype == MOE_BF16
+        ? launch_pack_blocked((const uint16_t*)src, (uint16_t*)dst, n_mat, rows, K, swiglu_i, s)
+        : launch_pack_blocked_f8((const uint8_t*)src, (uint8_t*)dst, n_mat, rows, K, swiglu_i, s);
+  };
+  MOE_TRY(pack(w->w13, wb->w13, d->n_routed, 2 * I, D, I));
+  MOE_TRY(pack(w->w2, wb->w2, d->n_routed, D, I, 0));
   if (d->n_shared) {
-    MOE_TRY(launch_pack_blocked(u16(w->w13_shared), (uint16_t*)wb->w13_shared, d->n_shared, 2 * Is, D, Is, s));
-    MOE_TRY(launch_pack_blocked(u16(w->w2_shared), (uint16_t*)wb->w2_shared, d->n_shared, D, Is, 0, s));
+    MOE_TRY(pack(w->w13_shared, wb->w13_shared, d->n_shared, 2 * Is, D, Is));
+    MOE_TRY(pack(w->w2_shared, wb->w2_shared, d->n_shared, D, Is, 0));
   }
   return MOE_OK;
 }

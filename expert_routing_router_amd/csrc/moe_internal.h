@@ -84,6 +84,9 @@ long blocked_rows(long rows_bound, int n_seg, int bm);
 // tile t holds gate rows t*128.. and up rows swiglu_i + t*128..
 hipError_t launch_pack_blocked(const uint16_t* src, uint16_t* dst, int n_mat, int rows, int K, int swiglu_i,
                                hipStream_t s);
+// FP8 codes: tiles of 256 rows, 128-element blocks (the FP8 LDS-DMA kernel's stage)
+hipError_t launch_pack_blocked_f8(const uint8_t* src, uint8_t* dst, int n_mat, int rows, int K, int swiglu_i,
+                                  hipStream_t s);
 int gemm_bm(int dtype, int mean_rows, int dmodel, int inter);
 hipError_t launch_gemm_swiglu(const GemmArgs& a, int dtype, int bm, hipStream_t s);
 hipError_t launch_gemm_down(const GemmArgs& a, int dtype, int bm, hipStream_t s);

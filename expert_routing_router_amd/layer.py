@@ -30,7 +30,7 @@ class MoELayer:
         """cfg: layer configuration (T, d, N_r, ... dtypes); gen: the input source, an object
         with centroids(cfg), expert_w13(cfg, e), expert_w2(cfg, e), shared_w13(cfg, s),
         shared_w2(cfg, s) returning numpy arrays (bf16 bits as uint16, or fp32).
-        blocked_weights: also keep K-blocked copies of bf16 expert weights (moe_pack_expert_weights)
+        blocked_weights: also keep K-blocked copies of bf16 / FP8 expert weights (moe_pack_expert_weights)
         for the forward, where the shapes allow it; self.blocked says whether they are in use."""
         self.cfg = cfg
         self.device = torch.device(device)
@@ -89,7 +89,7 @@ class MoELayer:
                                       self.s13s if cfg.n_shared else None,
                                       self.s2s if cfg.n_shared else None)
         self.blocked = False
-        if blocked_weights and cfg.expert_dtype == "bf16":
+        if blocked_weights and cfg.expert_dtype in ("bf16", "fp8"):
             self._pack_weights()
         self.ws = torch.empty(L.moe_workspace_bytes(self.desc), dtype=torch.uint8, device=dev)
         T, K = cfg.T, cfg.top_k

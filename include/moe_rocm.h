@@ -96,11 +96,11 @@ typedef struct moe_weights {
   const float* w13_shared_scale;
   const float* w2_shared_scale;
   /* Optional K-blocked copies of w13, w2, w13_shared, w2_shared made by
-   * moe_pack_expert_weights (bf16 experts). When the routed ones (and, with
-   * N_s > 0, the shared ones) are all set, moe_forward and
-   * moe_forward_capacity read them instead of the row-major arrays and keep
-   * their intermediate H K-blocked too; the results are bit-identical. NULL:
-   * the row-major arrays are used. */
+   * moe_pack_expert_weights (bf16 or FP8 codes). When the routed ones (and,
+   * with N_s > 0, the shared ones) are all set, moe_forward and
+   * moe_forward_capacity read them instead of the row-major arrays (bf16:
+   * and keep their intermediate H K-blocked too); the results are
+   * bit-identical. NULL: the row-major arrays are used. */
   const void*  w13_blk;
   const void*  w2_blk;
   const void*  w13_shared_blk;
@@ -208,18 +208,21 @@ typedef struct moe_grads {
 int moe_transpose_expert_weights(const moe_desc_t* desc, const moe_weights_t* w, moe_weights_t* wt,
                                  moe_stream_t stream);
 
-/* K-blocked copies of the expert weights, the layout the grouped GEMM's LDS
- * ring consumes: for each matrix, tiles of 256 rows (SwiGLU w13: W1 rows
- * 128t..128t+127 then W3 rows I+128t..), then 32-element steps of the
- * reduction, then the tile's 256 rows of 64 bytes, each row's four 16-byte
- * chunks c stored at slot c ^ ((row >> 2) & 3). A tile's step is then one
- * contiguous 16 KB, so every 1 KB load instruction of the kernel reads one
- * contiguous kilobyte instead of sixteen 64-byte pieces of different rows
- * (a layout choice for gfx950's load path; the products are unchanged).
- * Fills wb->w13, wb->w2 (and wb->w13_shared, wb->w2_shared when N_s > 0),
- * each the size of its source, from w; other members of wb are ignored; the
- * caller then passes them as w13_blk ... in moe_weights_t. bf16 experts with
- * I % 128 == 0, I_s % 128 == 0 and d % 256 == 0; MOE_ENOTSUP otherwise. */
+/* K-blocked copies of the expert weights, the layout the grouped GEMMs' LDS
+ * rings consume: for each matrix, tiles of 256 rows (SwiGLU w13: W1 rows
+ * 128t..128t+127 then W3 rows I+128t..), then steps of the reduction, then
+ * the tile's 256 rows of one step each. bf16: 32-element steps (64-byte
+ * rows), a row's four 16-byte chunks c stored at slot c ^ ((row >> 2) & 3).
+ * FP8 codes: 128-element steps (128-byte rows), chunk c of eight at slot
+ * c ^ ((row >> 1) & 7); the block scales keep their layout. A tile's step is
+ * then one contiguous block, so every 1 KB load instruction of the kernels
+ * reads one contiguous kilobyte instead of pieces of 16 (bf16) or 8 (FP8)
+ * different rows (a layout choice for gfx950's load path; the products are
+ * unchanged). Fills wb->w13, wb->w2 (and wb->w13_shared, wb->w2_shared when
+ * N_s > 0), each the size of its source, from w; other members of wb are
+ * ignored; the caller then passes them as w13_blk ... in moe_weights_t.
+ * bf16 or FP8 experts with I % 128 == 0, I_s % 128 == 0 and d % 256 == 0;
+ * MOE_ENOTSUP otherwise. */
 int moe_pack_expert_weights(const moe_desc_t* desc, const moe_weights_t* w, moe_weights_t* wb,
                             moe_stream_t stream);
 

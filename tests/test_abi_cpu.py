@@ -204,7 +204,7 @@ def test_backward_support_matrix(lib):
 
 
 def test_pack_arg_errors(lib):
-    """K-blocked weight copies exist for bf16 experts with I % 128 == 0, I_s % 128 == 0 and
+    """K-blocked weight copies exist for bf16 and FP8 experts with I % 128 == 0, I_s % 128 == 0 and
     d % 256 == 0 (MOE_ENOTSUP otherwise); misaligned pointers are refused before any launch."""
     w = M.MoeWeights(A, A, A, A, A, None, None, None, None)
     bad = M.MoeWeights(A, MIS, A, A, A, None, None, None, None)
@@ -212,7 +212,7 @@ def test_pack_arg_errors(lib):
     ok = M.make_desc(T=64, d=512, n_routed=16, top_k=4, n_shared=1, inter=256)
     assert pack(ok, w, bad) == M.MOE_EINVAL and pack(ok, bad, w) == M.MOE_EINVAL
     for kw in (dict(inter=192), dict(d=384), dict(inter_shared=320),
-               dict(router_dtype="f32", expert_dtype="fp8")):
+               dict(router_dtype="f32", expert_dtype="fp8", d=384)):
         args = dict(T=64, d=512, n_routed=16, top_k=4, n_shared=1, inter=256)
         args.update(kw)
         assert pack(M.make_desc(**args), w, w) == M.MOE_ENOTSUP, kw

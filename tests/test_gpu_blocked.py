@@ -4,7 +4,7 @@ written out here with numpy; the forward on blocked copies is checked against
 the forward on the row-major weights, which must agree bit for bit (the same
 operands reach the same MFMAs in the same order; only where the loads fetch
 them from changes). The oracle parity tests of moe_forward run on the blocked
-copies too, since MoELayer packs bf16 weights by default."""
+copies too, since MoELayer packs bf16 and FP8 weights by default."""
 
 import numpy as np
 import pytest
@@ -19,40 +19,47 @@ from workloads import gen, get_config
 pytestmark = pytest.mark.gpu
 
 
-def pack_ref(w, swiglu_i):
-    """[n, rows, K] -> [n, tiles, steps, 256, 32]: tiles of 256 rows (SwiGLU: gate rows 128t.. then
-    up rows swiglu_i + 128t..), 32-element steps, row r's 16-byte chunk c at slot c ^ ((r >> 2) & 3)."""
+def pack_ref(w, swiglu_i, fp8=False):
+    """[n, rows, K] -> [n, tiles, steps, 256, step]: tiles of 256 rows (SwiGLU: gate rows 128t.. then
+    up rows swiglu_i + 128t..), steps of 32 bf16 / 128 FP8 elements, row r's 16-byte chunk c at slot
+    c ^ ((r >> 2) & 3) (bf16, 4 chunks) or c ^ ((r >> 1) & 7) (FP8, 8 chunks)."""
     n, rows, K = w.shape
-    tiles, steps = rows // 256, K // 32
+    step, nch = (128, 8) if fp8 else (32, 4)
+    per = 16 // w.dtype.itemsize                                              # elements per chunk
+    tiles, steps = rows // 256, K // step
     r = np.arange(256)
-    slot_chunk = np.arange(4)[None, :] ^ ((r[:, None] >> 2) & 3)           # [256, 4]: chunk held by each slot
-    out = np.empty((n, tiles, steps, 256, 32), w.dtype)
+    swz = ((r >> 1) & 7) if fp8 else ((r >> 2) & 3)
+    slot_chunk = np.arange(nch)[None, :] ^ swz[:, None]                      # [256, nch]: chunk held by each slot
+    out = np.empty((n, tiles, steps, 256, step), w.dtype)
     for t in range(tiles):
         if swiglu_i:
             src = np.concatenate([np.arange(128) + 128 * t, swiglu_i + 128 * t + np.arange(128)])
         else:
             src = 256 * t + np.arange(256)
-        tile = w[:, src, :].reshape(n, 256, steps, 4, 8)
+        tile = w[:, src, :].reshape(n, 256, steps, nch, per)
         g = np.take_along_axis(tile, slot_chunk[None, :, None, :, None], axis=3)
-        out[:, t] = g.transpose(0, 2, 1, 3, 4).reshape(n, steps, 256, 32)
+        out[:, t] = g.transpose(0, 2, 1, 3, 4).reshape(n, steps, 256, step)
     return out
 
 
-def test_pack_layout_matches_definition():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_pack_layout_matches_definition(fp8):
     d, I, Is, N, Ns = 512, 256, 384, 3, 1
-    desc = M.make_desc(T=16, d=d, n_routed=N, top_k=2, n_shared=Ns, inter=I, inter_shared=Is)
+    extra = dict(router_dtype="f32", expert_dtype="fp8") if fp8 else {}
+    desc = M.make_desc(T=16, d=d, n_routed=N, top_k=2, n_shared=Ns, inter=I, inter_shared=Is, **extra)
     rng = np.random.default_rng(7)
-    src = {k: rng.integers(0, 1 << 16, size=s, dtype=np.uint16)
+    dt, hi = (np.uint8, 1 << 8) if fp8 else (np.uint16, 1 << 16)
+    src = {k: rng.integers(0, hi, size=s, dtype=dt)
            for k, s in (("w13", (N, 2 * I, d)), ("w2", (N, d, I)), ("w13s", (Ns, 2 * Is, d)), ("w2s", (Ns, d, Is)))}
-    t = {k: torch.from_numpy(v.view(np.int16)).cuda() for k, v in src.items()}
+    t = {k: torch.from_numpy(v if fp8 else v.view(np.int16)).cuda() for k, v in src.items()}
     o = {k: torch.empty_like(v) for k, v in t.items()}
     w = M.make_weights(None, t["w13"], t["w2"], t["w13s"], t["w2s"])
     wb = M.make_weights(None, o["w13"], o["w2"], o["w13s"], o["w2s"])
     M.moe_pack_expert_weights(desc, w, wb)
     torch.cuda.synchronize()
     for k, si in (("w13", I), ("w2", 0), ("w13s", Is), ("w2s", 0)):
-        got = o[k].cpu().numpy().view(np.uint16).reshape(-1)
-        ref = pack_ref(src[k], si).reshape(-1)
+        got = o[k].cpu().numpy().view(dt).reshape(-1)
+        ref = pack_ref(src[k], si, fp8).reshape(-1)
         assert np.array_equal(got, ref), k
 
 
@@ -83,11 +90,11 @@ def _same(a, b, tag):
                            y.view(torch.int16) if y.dtype == torch.bfloat16 else y), (tag, name)
 
 
-@pytest.mark.parametrize("name,kw", [("v3", {}), ("mid", {}), ("mid", dict(T=300))])
+@pytest.mark.parametrize("name,kw", [("v3", {}), ("mid", {}), ("mid", dict(T=300)), ("fp8", dict(T=2048))])
 def test_blocked_forward_bit_identical(name, kw):
     cfg = get_config(name, **kw)
     layer = layer_for(cfg)
-    assert layer.blocked, "bf16 layer of this shape keeps K-blocked weights"
+    assert layer.blocked, "a bf16 / FP8 layer of this shape keeps K-blocked weights"
     for step in range(2):
         u = dev(gen.tokens(cfg, step), cfg.in_dtype)
         b0 = dev(gen.bias_init(cfg), "f32")
