@@ -120,27 +120,56 @@ __device__ __forceinline__ float load_src(const void* p, size_t i, bool bf) {
   return bf ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
 }
 
-// One wave per (row, 128-column tile): amax, scale = fl32(amax/448), codes.
+// 16 lanes per (row, 128-column tile), 8 consecutive columns per lane (one
+// 16-byte bf16 or two 16-byte fp32 loads, one 8-byte store of codes), 16
+// tiles per workgroup: amax over the tile by xor swizzles inside the 16-lane
+// group, scale = fl32(amax/448), codes = e4m3(v / scale). A tile's 16 lanes
+// are live or not together, so the swizzles never read a lane that left.
+template <int OFF>
+__device__ __forceinline__ float swz_xor(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (OFF << 10)));
+}
 template <bool BF>
 __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__ src, long rows, int cols,
                                                         const int32_t* __restrict__ row_index,
                                                         uint8_t* __restrict__ q, float* __restrict__ scale) {
-  const int lane = threadIdx.x & 63;
-  const long tile = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int sub = threadIdx.x & 15;
+  const long tile = ((long)blockIdx.x * 256 + threadIdx.x) >> 4;
   const int tpr = cols / 128;
   if (tile >= rows * tpr) return;
   const long r = tile / tpr;
-  const int c0 = (int)(tile - r * tpr) * 128;
+  const int c0 = (int)(tile - r * tpr) * 128 + sub * 8;
   const long sr = row_index ? row_index[r] : r;
-  const float v0 = load_src(src, (size_t)sr * cols + c0 + 2 * lane, BF);
-  const float v1 = load_src(src, (size_t)sr * cols + c0 + 2 * lane + 1, BF);
-  float m = fmaxf(fabsf(v0), fabsf(v1));
+  float v[8];
+  if (BF) {
+    const i32x4 raw = *(const i32x4*)((const uint16_t*)src + (size_t)sr * cols + c0);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = __uint_as_float((uint32_t)raw[i] << 16);
+      v[2 * i + 1] = __uint_as_float((uint32_t)raw[i] & 0xFFFF0000u);
+    }
+  } else {
+    const f32x4* p = (const f32x4*)((const float*)src + (size_t)sr * cols + c0);
+    const f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int i = 0; i < 4; i++) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+  m = fmaxf(m, swz_xor<1>(m));
+  m = fmaxf(m, swz_xor<2>(m));
+  m = fmaxf(m, swz_xor<4>(m));
+  m = fmaxf(m, swz_xor<8>(m));
   const float sc = m == 0.0f ? 1.0f : m / 448.0f;
-  const uint32_t b0 = e4m3_encode(v0 / sc), b1 = e4m3_encode(v1 / sc);
-  *(uint16_t*)(q + (size_t)r * cols + c0 + 2 * lane) = (uint16_t)(b0 | (b1 << 8));
-  if (lane == 0) scale[(size_t)r * tpr + c0 / 128] = sc;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    lo |= e4m3_encode(v[i] / sc) << (8 * i);
+    hi |= e4m3_encode(v[4 + i] / sc) << (8 * i);
+  }
+  *(uint2*)(q + (size_t)r * cols + c0) = make_uint2(lo, hi);
+  if (sub == 0) scale[(size_t)r * tpr + c0 / 128] = sc;
 }
 
 // One workgroup per 128x128 block.
@@ -175,7 +204,7 @@ hipError_t launch_quant_act(const void* src, int src_dtype, long rows, int cols,
                             uint8_t* q, float* scale, hipStream_t s) {
   const long tiles = rows * (cols / 128);
   if (tiles <= 0) return hipSuccess;
-  const unsigned grid = (unsigned)cdiv<long>(tiles, 4);
+  const unsigned grid = (unsigned)cdiv<long>(tiles, 16);
   if (src_dtype == MOE_BF16) quant_act_kernel<true><<<grid, 256, 0, s>>>(src, rows, cols, row_index, q, scale);
   else quant_act_kernel<false><<<grid, 256, 0, s>>>(src, rows, cols, row_index, q, scale);
   return hipGetLastError();

@@ -108,3 +108,33 @@ def test_grouped_swiglu_direct_rows_and_fp8():
         log("fp8 expert", e, "vs oracle B %.2e" % eB, "vs A %.2e" % eA, "(B vs A %.2e)" % eAB)
         assert eB < 1.5e-2
         assert eA < eAB * 1.25 + 5e-3
+
+
+@pytest.mark.parametrize("src_dtype", ["f32", "bf16"])
+def test_quant_act_bit_exact_special_tiles(src_dtype):
+    """The 1x128 activation quantiser (fp32 source: the FP8 path's H; bf16: u) against the oracle's
+    encoder, bit for bit, on tiles with an all-zero row, values in E4M3's subnormal range, signed
+    zeros, exact ties between codes, outliers and ordinary normals; rows of 5 tiles, 67 rows."""
+    rng = np.random.default_rng(11)
+    rows, cols = 67, 640
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[0] = 0.0
+    x[1, :128] = -0.0
+    x[2] = rng.standard_normal(cols).astype(np.float32) * 1e-3
+    x[3, 5] = 448.0                                        # tile amax 448: scale 1, codes of x exactly
+    x[3, 6:128] = np.float32(448.0) * np.float32(1.5) / 16  # a tie halfway between two codes
+    x[rng.integers(4, rows, 40), rng.integers(0, cols, 40)] = 50.0
+    if src_dtype == "bf16":
+        bits = gen.f32_to_bf16_bits(x)
+        src = dev(bits, "bf16")
+        x32 = nx.bf16_to_f64(bits).astype(np.float32)
+    else:
+        src = dev(x, "f32")
+        x32 = x
+    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    s = torch.empty((rows, cols // 128), dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8(M.MOE_QUANT_ACT_1x128, src, rows, cols, q, s)
+    torch.cuda.synchronize()
+    cq, cs = nx.quant_act_1x128(x32)
+    assert np.array_equal(host(s), cs)
+    assert np.array_equal(host(q), cq)
