@@ -54,6 +54,14 @@ SCORE_CASES = [
     ("k1_g64", 33, 128, 1, 64, 1, 1, 1, True),
     ("q3_groups", 257, 96, 6, 6, 2, 3, 1, False),
     ("all_experts", 50, 16, 16, 1, 1, 16, 1, True),
+    # group sizes S = N/G: powers of two up to 64 are scored by segmented cross-lane reductions
+    # (S = 64 spans a whole 64-lane slot), other sizes by a lane per group
+    ("s64_groups", 777, 256, 8, 4, 2, 4, 1, False),
+    ("s64_groups_ties", 300, 256, 8, 4, 2, 4, 1, True),
+    ("s8_groups_ties", 500, 64, 6, 8, 3, 2, 1, True),
+    ("s1_groups", 40, 16, 4, 16, 4, 1, 1, True),
+    ("s32_partial_slot", 400, 96, 4, 3, 2, 2, 1, True),
+    ("s24_lane_per_group", 300, 96, 6, 4, 2, 3, 1, True),
 ]
 
 
