@@ -616,8 +616,6 @@ hipError_t launch_pack_blocked(const uint16_t* src, uint16_t* dst, int n_mat, in
   return hipGetLastError();
 }
 
-long blocked_rows(long rows_bound, int n_seg, int bm) { return (rows_bound / bm + n_seg) * (long)bm; }
-
 hipError_t launch_gemm_fp8(const GemmArgs& a, bool swiglu, int bm, hipStream_t s);
 
 hipError_t launch_gemm_swiglu(const GemmArgs& a, int dtype, int bm, hipStream_t s) {

@@ -78,8 +78,6 @@ struct GemmArgs {
   int x_blocked = 0;          // x: per m-tile (mtile_prefix numbering) blocks of BM rows, K = this GEMM's K
   int out_blocked = 0;        // SwiGLU output H written in the x_blocked layout of the down GEMM
 };
-// rows of a K-blocked activation buffer: every m-tile padded to bm rows
-long blocked_rows(long rows_bound, int n_seg, int bm);
 // bf16 weights [n_mat][rows][K] -> K-blocked tiles of 256 rows; swiglu_i > 0: rows = 2*swiglu_i and
 // tile t holds gate rows t*128.. and up rows swiglu_i + t*128..
 hipError_t launch_pack_blocked(const uint16_t* src, uint16_t* dst, int n_mat, int rows, int K, int swiglu_i,
