@@ -9,9 +9,32 @@ namespace moe {
 // out_t = u_t + sum_s Ys[s][t] + sum_k gate[t,k] * Y[slot_row[t*K+k]]
 // (output equation of the DeepSeek-V3 guides, "Metodo" section 2; the pwwt.cn
 // note's section 4 combine). fp32 accumulation in that fixed order, one
-// workgroup per token, 8 elements per thread per step.
+// workgroup of 128 threads per token, 8 elements per thread per step. A step
+// issues the loads of all its rows (u, the shared rows, up to 8 routed rows)
+// before it adds any of them, so each wave keeps ~10 loads in flight instead
+// of one row at a time.
+constexpr int CB_THREADS = 128;
+constexpr int CB_ROWS = 8;           // routed rows loaded together (K > 8 runs in groups of 8)
+
+template <bool BF>
+__device__ __forceinline__ void combine_load8(const void* base, size_t row, int d, int c, float* v) {
+  if (BF) {
+    const i32x4 q = *(const i32x4*)((const uint16_t*)base + row * d + c);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = __uint_as_float(((uint32_t)q[i]) << 16);
+      v[2 * i + 1] = __uint_as_float(((uint32_t)q[i]) & 0xFFFF0000u);
+    }
+  } else {
+    const f32x4 p0 = *(const f32x4*)((const float*)base + row * d + c);
+    const f32x4 p1 = *(const f32x4*)((const float*)base + row * d + c + 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) { v[i] = p0[i]; v[4 + i] = p1[i]; }
+  }
+}
+
 template <bool IO_BF16, bool Y_BF16>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(CB_THREADS) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x;
   __shared__ int32_t srow[64];
   __shared__ float sg[64];
@@ -20,38 +43,44 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     sg[threadIdx.x] = a.gate[(size_t)t * a.K + threadIdx.x];
   }
   __syncthreads();
-  for (int c = threadIdx.x * 8; c < a.d; c += 256 * 8) {
+  const unsigned n_rows = (unsigned)(a.T * a.K);
+  for (int c = threadIdx.x * 8; c < a.d; c += CB_THREADS * 8) {
+    // A dropped selection (capacity limit) has no row, and rows outside Y are skipped too:
+    // their slots load row 0 (always inside Y) and add nothing, so every load is
+    // unconditional. Group g's routed rows are loaded before anything is added (group 0
+    // before the shared rows), and added after, in the fixed order.
     float acc[8];
-    auto load8 = [&](const void* base, bool bf, size_t row, float* v) {
-      if (bf) {
-        const i32x4 q = *(const i32x4*)((const uint16_t*)base + row * a.d + c);
+    bool use[CB_ROWS];
+    float v[CB_ROWS][8];
+    auto load_group = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          v[2 * i] = __uint_as_float(((uint32_t)q[i]) << 16);
-          v[2 * i + 1] = __uint_as_float(((uint32_t)q[i]) & 0xFFFF0000u);
-        }
-      } else {
-        const f32x4 p0 = *(const f32x4*)((const float*)base + row * a.d + c);
-        const f32x4 p1 = *(const f32x4*)((const float*)base + row * a.d + c + 4);
-#pragma unroll
-        for (int i = 0; i < 4; i++) { v[i] = p0[i]; v[4 + i] = p1[i]; }
+      for (int j = 0; j < CB_ROWS; j++) {
+        use[j] = k0 + j < a.K && (unsigned)srow[k0 + j] < n_rows;
+        combine_load8<Y_BF16>(a.y, use[j] ? (size_t)srow[k0 + j] : 0, a.d, c, v[j]);
       }
     };
-    load8(a.u, IO_BF16, t, acc);
+    auto add_group = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < CB_ROWS; j++) {
+        if (use[j]) {
+          const float g = sg[k0 + j];
+#pragma unroll
+          for (int i = 0; i < 8; i++) acc[i] = fmaf(g, v[j][i], acc[i]);
+        }
+      }
+    };
+    combine_load8<IO_BF16>(a.u, t, a.d, c, acc);
+    load_group(0);
     for (int s = 0; s < a.n_shared; s++) {
-      float v[8];
-      load8(a.y_shared, Y_BF16, (size_t)s * a.shared_stride + t, v);
+      float w[8];
+      combine_load8<Y_BF16>(a.y_shared, (size_t)s * a.shared_stride + t, a.d, c, w);
 #pragma unroll
-      for (int i = 0; i < 8; i++) acc[i] += v[i];
+      for (int i = 0; i < 8; i++) acc[i] += w[i];
     }
-    for (int k = 0; k < a.K; k++) {
-      // a dropped selection (capacity limit) has no row; rows outside Y are skipped too
-      if ((unsigned)srow[k] >= (unsigned)(a.T * a.K)) continue;
-      float v[8];
-      load8(a.y, Y_BF16, (size_t)srow[k], v);
-      const float g = sg[k];
-#pragma unroll
-      for (int i = 0; i < 8; i++) acc[i] = fmaf(g, v[i], acc[i]);
+    add_group(0);
+    for (int k0 = CB_ROWS; k0 < a.K; k0 += CB_ROWS) {
+      load_group(k0);
+      add_group(k0);
     }
     if (IO_BF16) {
       i32x4 q;
@@ -69,10 +98,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   const bool io = a.io_dtype == MOE_BF16, yb = a.y_dtype == MOE_BF16;
-  if (io && yb) combine_kernel<true, true><<<a.T, 256, 0, s>>>(a);
-  else if (io) combine_kernel<true, false><<<a.T, 256, 0, s>>>(a);
-  else if (yb) combine_kernel<false, true><<<a.T, 256, 0, s>>>(a);
-  else combine_kernel<false, false><<<a.T, 256, 0, s>>>(a);
+  if (io && yb) combine_kernel<true, true><<<a.T, CB_THREADS, 0, s>>>(a);
+  else if (io) combine_kernel<true, false><<<a.T, CB_THREADS, 0, s>>>(a);
+  else if (yb) combine_kernel<false, true><<<a.T, CB_THREADS, 0, s>>>(a);
+  else combine_kernel<false, false><<<a.T, CB_THREADS, 0, s>>>(a);
   return hipGetLastError();
 }
 
