@@ -42,7 +42,7 @@ extern "C" {
 /* status codes */
 #define MOE_OK          0
 #define MOE_EINVAL     -1  /* bad dimension, NULL required pointer, misaligned pointer */
-#define MOE_ENOTSUP    -2  /* dtype / shape combination this build does not implement */
+#define MOE_ENOTSUP    -2  /* dtype / shape combination the library does not implement */
 #define MOE_EWORKSPACE -3  /* workspace smaller than the call needs */
 #define MOE_EHIP       -4  /* a HIP launch or runtime call failed */
 
