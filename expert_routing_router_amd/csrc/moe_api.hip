@@ -324,7 +324,8 @@ static GemmArgs gemm_args(const void* x, long x_rows, const float* xs, const int
 }
 
 // GEMM1 + (FP8: quantise H) + GEMM2 over one set of segments.
-// blocked: w13/w13b/w2/w2b are K-blocked copies (bf16); H is then written and read K-blocked.
+// blocked: w13/w13b/w2/w2b are K-blocked copies (bf16, or FP8 codes); for bf16, H is then
+// written and read K-blocked too.
 static int run_ffn(const moe_desc_t* d, int inter, const void* x, long x_rows, const float* xs, const int32_t* ridx,
                    const int32_t* offsets, const int32_t* mtile, int n_seg, int rows_bound,
                    const void* w13, const float* s13, const void* w13b, const float* s13b,
