@@ -261,7 +261,10 @@ struct DmaCfg {
   static_assert(BYTES <= 160 * 1024 - 2048, "LDS budget");
 };
 
-template <int MB, bool SWIGLU, int RB>
+// WBLK: the weights are K-blocked (a.w_blocked); they are then read with the
+// non-temporal hint, whole lines at a time, so they do not push the activation
+// rows the tile's other n-tiles re-read out of L2
+template <int MB, bool SWIGLU, int RB, bool WBLK>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
   using C = DmaCfg<MB, RB>;
   constexpr int BM = C::BM, BN = C::BN, HN = BN / 2;
@@ -291,7 +294,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
   const uint16_t* wbase = seg < a.n_first
       ? (const uint16_t*)a.w0 + (size_t)seg * a.wstride0
       : (const uint16_t*)a.w1 + (size_t)(seg - a.n_first) * a.wstride1;
-  const bool xblk = a.x_blocked, wblk = a.w_blocked;
+  const bool xblk = a.x_blocked;
+  constexpr bool wblk = WBLK;
 
   // ---- per-lane global offsets of this wave's blocks (fixed over K). Block
   // wave + 8i starts at row RPB*(wave + 8i); the +8i part leaves the swizzle unchanged.
@@ -332,7 +336,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
       if (P < C::A_PER_WAVE - 1 || a_full) dma_b128(xr, aoff[P], kt * astep, sbase + (wave + 8 * P) * 1024);
     } else if constexpr (P < C::A_PER_WAVE + C::B_PER_WAVE) {
       constexpr int Q = P - C::A_PER_WAVE;
-      dma_b128(wr, boff[Q], kt * bstep, sbase + C::A_BYTES + (wave + 8 * Q) * 1024);
+      if constexpr (WBLK) dma_b128_nt(wr, boff[Q], kt * bstep, sbase + C::A_BYTES + (wave + 8 * Q) * 1024);
+      else dma_b128(wr, boff[Q], kt * bstep, sbase + C::A_BYTES + (wave + 8 * Q) * 1024);
     }
   };
   constexpr int NPARTS = C::A_PER_WAVE + C::B_PER_WAVE;
@@ -555,7 +560,7 @@ static hipError_t launch_bf16_dma(const GemmArgs& a, hipStream_t s) {
   const long mtiles_bound = (long)a.rows_bound / C::BM + a.n_seg;
   const long grid = (mtiles_bound * n_tiles + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  auto k = gemm_bf16_dma_kernel<MB, SWIGLU, RB>;
+  auto k = a.w_blocked ? gemm_bf16_dma_kernel<MB, SWIGLU, RB, true> : gemm_bf16_dma_kernel<MB, SWIGLU, RB, false>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
   if (e != hipSuccess) return e;
   k<<<dim3((unsigned)grid), C::THREADS, C::BYTES, s>>>(a);

@@ -22,6 +22,14 @@ __device__ __forceinline__ void dma_b128(i32x4 rsrc, int voff, int soff, uint32_
                :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0) : "memory");
 }
 
+// The same with the non-temporal hint: for data read once (K-blocked weights,
+// whose loads cover whole lines), so it is not kept in L2 at the expense of
+// operands other workgroups re-read.
+__device__ __forceinline__ void dma_b128_nt(i32x4 rsrc, int voff, int soff, uint32_t m0) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0) : "memory");
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
