@@ -1,5 +1,6 @@
 // Router of the DeepSeekMoE layer on gfx950: affinities, biased group-limited
-// top-K, normalised gates and per-expert loads, fused in one kernel.
+// top-K and normalised gates (route_kernel, with a fused front end or fed by
+// the tiled logits_kernel), and the per-expert loads (count_loads_kernel).
 //
 //   s_{i,t} = sigmoid(u_t . e_i)       -- DeepSeek-V3 Technical Report guides
 //                                         (xyznot.com), "Metodo" section 2
@@ -8,7 +9,8 @@
 //   groups ranked by the sum of their   -- pwwt.cn note 1.3 (node-limited
 //   top K_r/M scores, at most M kept       routing; nodes = expert groups here)
 //
-// One workgroup (4 waves) owns 32 tokens and every expert. The front end
+// route_kernel: one workgroup (4 waves) owns 32 tokens and every expert (4
+// tokens when the affinities are handed in). The front end
 // writes the fp32 affinities of its tokens into LDS; the selection back end is
 // one code path whatever the front end was (MFMA logits, fp64 logits, or
 // affinities handed in by the caller), so the scores-in mode exercises exactly
