@@ -219,3 +219,15 @@ def test_pack_arg_errors(lib):
     f32 = M.make_desc(T=64, d=512, n_routed=16, top_k=4, n_shared=1, inter=256, in_dtype="f32",
                       router_dtype="f32", expert_dtype="f32")
     assert pack(f32, w, w) == M.MOE_ENOTSUP
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py times the one-GPU path only: --gpus N with N > 1 exits with a message, before any
+    GPU work."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
