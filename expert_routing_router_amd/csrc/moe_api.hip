@@ -144,6 +144,9 @@ extern "C" int moe_validate(const moe_desc_t* d) {
   const long wide2 = d->inter_shared > wide ? d->inter_shared : wide;
   // byte offsets of 2-byte rows stay below 2^31 (buffer-load range and int offsets)
   if (rows * wide2 >= (1L << 30) || (long)d->T * d->d >= (1L << 30)) return MOE_ENOTSUP;
+  // the router addresses the centroids (as three bf16 planes for fp32 centroids)
+  // with 32-bit byte offsets
+  if (3L * d->n_routed * d->d * 2 >= (1L << 31)) return MOE_ENOTSUP;
   return MOE_OK;
 }
 

@@ -284,13 +284,16 @@ __device__ void select_tokens(const RouteArgs& a, RouterLdsT<BT>& sh, int t0, in
   const bool seg_groups = (S & (S - 1)) == 0 && S <= 64;
   for (int t = wave; t < nt; t += RT_THREADS / kWave) {
     const float* srow = sh.s[t];
-    // ordered keys; 0 = not a candidate. A candidate's key is at least 1 (only one NaN bit
-    // pattern orders to 0), so K rounds always find K distinct experts in range.
+    // ordered keys; 0 = not a candidate. A candidate's key is at least 1, so K rounds
+    // always find K distinct experts in range. A NaN key takes 1, the lowest
+    // candidate key: it ranks after every number (-inf included), as a NaN score
+    // never ranks in the group scores either.
     uint32_t ok[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int e = lane + 64 * j;
-      ok[j] = e < N ? max(ordered_f32(srow[e] + sh.b[e]), 1u) : 0u;
+      const float kv = e < N ? srow[e] + sh.b[e] : 0.f;
+      ok[j] = e < N ? (kv != kv ? 1u : max(ordered_f32(kv), 1u)) : 0u;
     }
     if (G > 1) {
       uint32_t gk = 0u;

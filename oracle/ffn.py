@@ -10,7 +10,10 @@ evaluated, with no capacity limit.
 
 FP8 diagnostic ("oracle B"): the same layer on E4M3-dequantised u, H and W with
 the pages' 1x128 / 128x128 scaling (xyznot.com guides, FP8 key idea; pwwt.cn
-note §3), to separate quantisation error from kernel error.
+note §3), to separate quantisation error from kernel error. u is quantised
+once, in 1x128 tiles along d; H in 1x128 tiles along I inside each expert;
+W13 and W2 in 128x128 blocks. Pinned against an independent construction with
+torch's float8_e4m3fn cast (tests/test_oracle_ffn.py).
 """
 
 import numpy as np

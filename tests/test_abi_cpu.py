@@ -68,6 +68,9 @@ BAD = [
     (dict(expert_dtype="fp8", inter=2048 + 64), M.MOE_ENOTSUP),
     (dict(expert_dtype="bf16", in_dtype="f32"), M.MOE_ENOTSUP),
     (dict(T=1 << 20), M.MOE_ENOTSUP),            # row offsets beyond 2^31
+    # centroid byte offsets (three bf16 planes of fp32 centroids) beyond 2^31
+    (dict(T=1, n_groups=1, topk_groups=1, group_topk=8, n_shared=0, inter=128, d=1 << 21,
+          router_dtype="f32"), M.MOE_ENOTSUP),
 ]
 
 

@@ -6,7 +6,11 @@
 * the literal output equation summed over *all* N_r experts with zero gates
   for the unselected ones equals the oracle's sparse evaluation;
 * zero weights give out = u exactly; doubling W2 doubles out - u;
-* the order of the K slots does not matter.
+* the order of the K slots does not matter;
+* the FP8 diagnostic (oracle B) equals an independent construction of the
+  pages' E4M3 recipe with torch's float8_e4m3fn cast, on inputs where leaving
+  H unquantised, tiling H along the tokens or tiling the weights 1x128 would
+  each be caught.
 """
 
 import numpy as np
@@ -122,3 +126,96 @@ def test_fp8_oracle_b_close_to_a():
     # E4M3 keeps 3 mantissa bits: per-element rounding of ~2^-4/sqrt(3) RMS on u, W
     # and H gives an FFN-relative error of a few percent, whatever the kernel.
     assert 0.02 < rel_ffn < 0.08 and rel < 0.06
+
+
+# ----------------------------------------------------------------------------- FP8 oracle B
+# The pages fix the FP8 granularity (xyznot.com guides, key-ideas FP8 bullet;
+# pwwt.cn note section 3): activations in 1x128 tiles along the reduction
+# dimension (u along d, H along I), weights in 128x128 blocks, E4M3 values
+# with one fp32 scale each. The reference below is built independently of the
+# oracle, with torch's own float8_e4m3fn cast: scale = fl32(amax / 448) (1 when
+# the tile is all zero), code = E4M3(fl32(x / scale)) rounded to nearest even
+# and saturated at +-448, value = code * scale.
+
+def _q_tiles(x32: torch.Tensor, tr: int, tc: int) -> torch.Tensor:
+    """Quantise-dequantise a float32 [R, C] matrix in tr x tc tiles -> float64."""
+    R, C = x32.shape
+    t = x32.reshape(R // tr, tr, C // tc, tc)
+    amax = t.abs().amax(dim=(1, 3), keepdim=True)
+    scale = torch.where(amax == 0, torch.ones_like(amax), amax / 448.0)       # fp32 division
+    q = (t / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return (q.to(torch.float64) * scale.to(torch.float64)).reshape(R, C)
+
+
+def _fp8_expert_torch(x64, w13, w2, mutation=None):
+    """One FP8 SwiGLU expert as the pages' recipe prescribes; `mutation` plants
+    one plausible slip so the test can show it would be caught."""
+    x = torch.from_numpy(np.asarray(x64, np.float64)).float()
+    w13 = torch.from_numpy(np.asarray(w13, np.float32))
+    w2 = torch.from_numpy(np.asarray(w2, np.float32))
+    wt = (1, 128) if mutation == "weights_1x128" else (128, 128)
+    xq = _q_tiles(x, 1, 128)
+    w13q = _q_tiles(w13, *wt)
+    w2q = _q_tiles(w2, *wt)
+    inter = w13.shape[0] // 2
+    a = xq @ w13q[:inter].T
+    v = xq @ w13q[inter:].T
+    h = a * torch.sigmoid(a) * v
+    if mutation == "h_unquantised":
+        hq = h
+    elif mutation == "h_tiles_along_tokens":
+        hq = _q_tiles(h.float().T.contiguous(), 1, 128).T
+    else:
+        hq = _q_tiles(h.float(), 1, 128)
+    return (hq @ w2q.T).numpy()
+
+
+def _fp8_pin_inputs(R=256, d=256, inter=256):
+    """Inputs on which each slip moves the result far above rounding: rows of x
+    span 2^-3..2^3 and one 128-column tile of half the rows is 2^4 larger; the
+    weights' row magnitudes vary inside each 128x128 block; the second
+    128-column half of H is about 2^6 above the first."""
+    rng = np.random.default_rng(1234)
+    x = rng.standard_normal((R, d)).astype(np.float32)
+    x *= (2.0 ** (np.arange(R) % 7 - 3)).astype(np.float32)[:, None]
+    x[::2, 128:256] *= np.float32(16.0)
+    x[5, :128] = 0.0                                  # an all-zero tile takes scale 1
+    w13 = (rng.standard_normal((2 * inter, d)) / np.sqrt(d)).astype(np.float32)
+    w13 *= (1.0 + 3.0 * (np.arange(2 * inter) % 5 == 0)).astype(np.float32)[:, None]
+    hi = np.r_[np.arange(128, inter), inter + np.arange(128, inter)]
+    w13[hi] *= np.float32(8.0)
+    w2 = (rng.standard_normal((d, inter)) / np.sqrt(inter)).astype(np.float32)
+    w2 *= (1.0 + 3.0 * (np.arange(d) % 3 == 0)).astype(np.float32)[:, None]
+    w2[:, 128:] /= np.float32(64.0)
+    return x.astype(np.float64), w13, w2
+
+
+def test_fp8_oracle_b_expert_matches_independent_recipe():
+    x, w13, w2 = _fp8_pin_inputs()
+    # the oracle quantises u once per layer (before the experts), H inside each expert
+    got = ffn._expert(ffn._fp8_act(x), w13.astype(np.float64), w2.astype(np.float64), fp8=True)
+    ref = _fp8_expert_torch(x, w13, w2)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel < 1e-12, rel
+    # each plausible slip in the oracle (or in a kernel) moves the result by
+    # orders of magnitude more than the bar above: measured 2.2e-2 with H left
+    # unquantised, 2.5e-2 with H tiled along the tokens, 7.3e-2 with 1x128
+    # weight tiles (the correct recipe agrees exactly, 0.0)
+    for m in ("h_unquantised", "h_tiles_along_tokens", "weights_1x128"):
+        bad = _fp8_expert_torch(x, w13, w2, mutation=m)
+        assert np.linalg.norm(got - bad) / np.linalg.norm(ref) > 1e-3, m
+
+
+def test_fp8_oracle_b_layer_matches_independent_recipe():
+    cfg = _small_cfg(T=40, d=256, n_routed=8, top_k=2, inter=128, inter_shared=256,
+                     expert_dtype="fp8", in_dtype="bf16", outlier_frac=0.01)
+    u, E, w13, w2, w13s, w2s = _inputs(cfg)
+    u64 = ffn.nx.to_f64(u, "bf16")
+    r, _, _ = routing.route_tokens(u64, E.astype(np.float64), np.zeros(cfg.n_routed, np.float32), cfg)
+    got = ffn.layer(cfg, u, r.idx, r.gate, w13, w2, w13s, w2s, fp8=True)
+    ref = u64 + _fp8_expert_torch(u64, w13s[0], w2s[0])
+    for t in range(cfg.T):
+        for k in range(cfg.top_k):
+            e = r.idx[t, k]
+            ref[t] += r.gate[t, k] * _fp8_expert_torch(u64[t:t + 1], w13[e], w2[e])[0]
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref - u64) < 1e-12
