@@ -40,14 +40,28 @@ def _w64(arr, dtype):
 
 
 def layer(cfg, u, idx, gate64, w13, w2, w13s, w2s, tokens=None, wdtype=None,
-          fp8=False):
+          fp8=False, weights=None):
     """Layer output for `tokens` (default all): u + shared + sum_k g_k y_k (fp64).
 
     u, weights: canonical input arrays (bf16 bits or fp32). idx/gate64: routing.
     Experts are converted to fp64 one at a time. Returns [len(tokens), d] fp64.
     With fp8=True, u, H and the weights go through E4M3 quantise-dequantise.
+
+    weights: optional callable (kind, i) -> (w13, w2) for kind "shared" or
+    "routed", returning the expert's fp64 weights as the layer uses them (for
+    fp8, already through fp8_weights); then w13/w2/w13s/w2s are not read. It
+    lets a caller prepare experts ahead (for example on other threads) without
+    changing what is computed. Experts are used in ascending order.
     """
     wdtype = wdtype or ("bf16" if cfg.expert_dtype == "bf16" else "f32")
+
+    def expert_w(kind, i):
+        if weights is not None:
+            return weights(kind, i)
+        a, b = (w13s[i], w2s[i]) if kind == "shared" else (w13[i], w2[i])
+        a, b = _w64(a, wdtype), _w64(b, wdtype)
+        return fp8_weights(a, b) if fp8 else (a, b)
+
     T = u.shape[0]
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     u64 = nx.to_f64(u[tok], cfg.in_dtype)
@@ -57,14 +71,22 @@ def layer(cfg, u, idx, gate64, w13, w2, w13s, w2s, tokens=None, wdtype=None,
         xq = u64
     out = u64.copy()
     for s in range(cfg.n_shared):
-        out += _expert(xq, _w64(w13s[s], wdtype), _w64(w2s[s], wdtype), fp8)
+        out += _expert(xq, *expert_w("shared", s), fp8)
     sub_idx = idx[tok]
     sub_gate = gate64[tok]
     for e in np.unique(sub_idx):
         rows, ks = np.nonzero(sub_idx == e)
-        y = _expert(xq[rows], _w64(w13[e], wdtype), _w64(w2[e], wdtype), fp8)
+        y = _expert(xq[rows], *expert_w("routed", int(e)), fp8)
         out[rows] += sub_gate[rows, ks][:, None] * y
     return out
+
+
+def fp8_weights(w13_64, w2_64):
+    """One expert's weights through E4M3 with one fp32 scale per 128x128 block
+    (W13 [2I, d] and W2 [d, I] each blocked on its own), back to fp64."""
+    c13, s13 = nx.quant_w_128x128(w13_64.astype(np.float32))
+    c2, s2 = nx.quant_w_128x128(w2_64.astype(np.float32))
+    return nx.dequant_w(c13, s13), nx.dequant_w(c2, s2)
 
 
 def _fp8_act(x64):
@@ -73,14 +95,12 @@ def _fp8_act(x64):
 
 
 def _expert(x64, w13_64, w2_64, fp8):
+    """One expert on rows x64. fp8: the weights are already E4M3-dequantised
+    (fp8_weights); H is quantised here, in 1x128 tiles along I."""
     if not fp8:
         return swiglu(x64, w13_64, w2_64)
     inter = w13_64.shape[0] // 2
-    c13, s13 = nx.quant_w_128x128(w13_64.astype(np.float32))
-    c2, s2 = nx.quant_w_128x128(w2_64.astype(np.float32))
-    w13q = nx.dequant_w(c13, s13)
-    w2q = nx.dequant_w(c2, s2)
-    a = x64 @ w13q[:inter].T
-    v = x64 @ w13q[inter:].T
+    a = x64 @ w13_64[:inter].T
+    v = x64 @ w13_64[inter:].T
     h = a * _sig(a) * v
-    return _fp8_act(h) @ w2q.T
+    return _fp8_act(h) @ w2_64.T

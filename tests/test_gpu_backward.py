@@ -15,6 +15,7 @@ import torch
 from expert_routing_router_amd.layer import MoELayer
 from oracle import backward, numerics as nx, routing
 from tests.gpu_util import dev, host, log, rel_l2
+from tests.host_weights import CachedGen
 from workloads import gen, get_config
 
 pytestmark = pytest.mark.gpu
@@ -37,7 +38,7 @@ def _dout(cfg, seed=11):
 
 
 def _run(cfg, step=0):
-    layer = MoELayer(cfg, gen)
+    layer = MoELayer(cfg, CachedGen)
     u = gen.tokens(cfg, step)
     b = gen.bias_init(cfg) + np.float32(0.003) * ((np.arange(cfg.n_routed) % 5) - 2).astype(np.float32)
     dout = _dout(cfg)

@@ -13,6 +13,7 @@ import torch
 import expert_routing_router_amd as M
 from expert_routing_router_amd.layer import MoELayer
 from tests.gpu_util import dev, log
+from tests.host_weights import CachedGen
 from tests.test_gpu_forward import layer_for
 from workloads import gen, get_config
 
@@ -107,7 +108,7 @@ def test_blocked_forward_bit_identical(name, kw):
 def test_blocked_capacity_forward_bit_identical():
     """The capped forward runs the shared experts in their own pass (own m-tiles, own blocked H)."""
     cfg = get_config("mid", T=1024, inter_shared=1024)
-    layer = MoELayer(cfg, gen)
+    layer = MoELayer(cfg, CachedGen)
     assert layer.blocked
     u = dev(gen.tokens(cfg, 0), cfg.in_dtype)
     b0 = dev(gen.bias_init(cfg), "f32")
@@ -120,7 +121,7 @@ def test_blocked_capacity_forward_bit_identical():
 def test_unblocked_layer_matches_blocked_layer():
     """A layer built without blocked copies gives the same forward as one with them."""
     cfg = get_config("mid", T=512)
-    a = MoELayer(cfg, gen, blocked_weights=False)
+    a = MoELayer(cfg, CachedGen, blocked_weights=False)
     assert not a.blocked
     b = layer_for(cfg)
     assert b.blocked

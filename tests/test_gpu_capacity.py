@@ -16,7 +16,8 @@ import expert_routing_router_amd as M
 from expert_routing_router_amd.layer import MoELayer
 from oracle import capacity as cap_o, ffn, numerics as nx, routing
 from tests.gpu_util import dev, host, log, rel_l2
-from tests.test_gpu_forward import HostWeights, check_routing, layer_for, oracle_out, _sample
+from tests.host_weights import CachedGen
+from tests.test_gpu_forward import check_routing, layer_for, oracle_out, _sample
 from workloads import gen, get_config
 
 pytestmark = pytest.mark.gpu
@@ -116,7 +117,7 @@ def run_capped(layer, cfg, cap, step, b_dev):
                                         ("mid", dict(T=300, n_shared=0), 1.0)])
 def test_forward_capacity_full(name, kw, cf):
     cfg = get_config(name, **kw)
-    layer = MoELayer(cfg, gen)
+    layer = MoELayer(cfg, CachedGen)
     cap = cap_o.capacity(cfg.T, cfg.top_k, cfg.n_routed, cf)
     b = dev(gen.bias_init(cfg), "f32")
     u, b0, idx, gate, counts, out, b1, keep, nd = run_capped(layer, cfg, cap, 0, b)
@@ -139,7 +140,6 @@ def test_forward_capacity_v3_sampled_steps():
     in between; masks checked in full, outputs on sampled tokens."""
     cfg = get_config("skew").with_(T=4096)
     layer = layer_for(cfg)
-    hw = HostWeights(cfg)
     E = gen.centroids(cfg)
     cap = cap_o.capacity(cfg.T, cfg.top_k, cfg.n_routed, 1.0)
     b = dev(gen.bias_init(cfg), "f32")
@@ -152,7 +152,7 @@ def test_forward_capacity_v3_sampled_steps():
         # tokens with a dropped selection, plus a random sample
         dropped_t = np.nonzero(~used.all(axis=1))[0]
         tok = np.unique(np.concatenate([_sample(cfg.T, 4, step), dropped_t[:4]]))
-        ref = oracle_out(cfg, u, idx_ref, cap_o.dropped_gates(gate_ref, used), hw, tok)
+        ref = oracle_out(cfg, u, idx_ref, cap_o.dropped_gates(gate_ref, used), tok)
         err = rel_l2(out[tok], ref)
         log(tag, "sampled", len(tok), "rel-L2 %.3e" % err)
         assert err <= 1e-2
@@ -161,7 +161,7 @@ def test_forward_capacity_v3_sampled_steps():
 def test_capacity_above_every_load_matches_forward():
     """A capacity no expert reaches drops nothing: the capped forward equals moe_forward."""
     cfg = get_config("mid", T=512)
-    layer = MoELayer(cfg, gen)
+    layer = MoELayer(cfg, CachedGen)
     u = dev(gen.tokens(cfg, 0), "bf16")
     b = dev(gen.bias_init(cfg), "f32")
     layer.forward(u, b.clone(), update_bias=False)
@@ -177,10 +177,10 @@ def test_capacity_above_every_load_matches_forward():
 def test_forward_capacity_fp8_sampled():
     """The FP8 V3-shape layer at capacity factor 1 (the capped forward takes the separate
     shared-expert pass there too): mask as above, sampled outputs against oracle B (the same
-    E4M3 recipe on the CPU) with the dropped gates zeroed, at the FP8 bar."""
+    E4M3 recipe on the CPU) with the dropped gates zeroed, at the bar of the plain FP8 forward
+    against oracle B."""
     cfg = get_config("fp8")
     layer = layer_for(cfg)
-    hw = HostWeights(cfg)
     E = gen.centroids(cfg)
     cap = cap_o.capacity(cfg.T, cfg.top_k, cfg.n_routed, 1.0)
     b = dev(gen.bias_init(cfg), "f32")
@@ -190,7 +190,7 @@ def test_forward_capacity_fp8_sampled():
     used = check_keep(cfg, cap, s64, idx_ref, keep, nd, "fp8 capped")
     dropped_t = np.nonzero(~used.all(axis=1))[0]
     tok = np.unique(np.concatenate([_sample(cfg.T, 3, 5), dropped_t[:3]]))
-    ref = oracle_out(cfg, u, idx_ref, cap_o.dropped_gates(gate_ref, used), hw, tok, fp8=True)
+    ref = oracle_out(cfg, u, idx_ref, cap_o.dropped_gates(gate_ref, used), tok, fp8=True)
     err = rel_l2(out[tok], ref)
     log("fp8 capped sampled", len(tok), "vs oracle B rel-L2 %.3e" % err)
-    assert err <= 1.5e-2
+    assert err <= 5e-3

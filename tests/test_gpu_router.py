@@ -86,6 +86,33 @@ def test_scores_in_bit_exact(case):
     assert np.array_equal(b1.view(np.uint32), want_b.view(np.uint32))
 
 
+def test_scores_in_nan_and_zero_sum_gates():
+    """Scores-in at the V3 routing shape with degenerate affinities: a NaN
+    affinity ranks after every number (it is never chosen while enough numbers
+    remain), and a token whose selected affinities are all zero gets gates 1/K
+    (the zero-sum reading). Bit-exact against the oracle, as the other cases."""
+    T, N, K, G, Mg, q = 512, 256, 8, 8, 4, 2
+    rng = np.random.default_rng(77)
+    s = rng.uniform(0, 1, (T, N)).astype(np.float32)
+    b = rng.uniform(-0.01, 0.01, N).astype(np.float32)
+    b[:K] = np.float32(0.5)                           # experts 0..K-1 lead on the biased key
+    for t in range(50):                               # 1..3 NaNs, one at the row's best expert
+        cols = rng.choice(N, rng.integers(1, 4), replace=False)
+        s[t, cols] = np.nan
+        s[t, np.nanargmax(s[t] + b)] = np.nan
+    s[50:60] = 0.0                                    # all zero: the bias alone routes
+    s[60:70] = rng.uniform(0, 0.4, (10, N)).astype(np.float32)
+    s[60:70, :K] = 0.0                                # the K selected have zero affinity
+    desc = _desc(T, N, K, G, Mg, q)
+    r = routing.select(s, b, K, G, Mg, q, 1)
+    assert (r.gate[50:70] == 1.0 / K).all() and not np.isnan(r.gate).any()
+    idx, gate, counts, sout, b1 = _gpu_route_scores(desc, s, b)
+    assert np.array_equal(idx, r.idx), np.nonzero((idx != r.idx).any(axis=1))[0][:10]
+    assert np.array_equal(counts, r.counts)
+    assert np.array_equal(gate, r.gate.astype(np.float32))
+    assert np.array_equal(b1.view(np.uint32), routing.bias_step(r.counts, b, T, K, 0.001).view(np.uint32))
+
+
 def test_scores_from_oracle_logits_tiny_and_mid():
     for name in ("tiny", "mid"):
         cfg = get_config(name)

@@ -193,7 +193,8 @@ def _fp8_pin_inputs(R=256, d=256, inter=256):
 def test_fp8_oracle_b_expert_matches_independent_recipe():
     x, w13, w2 = _fp8_pin_inputs()
     # the oracle quantises u once per layer (before the experts), H inside each expert
-    got = ffn._expert(ffn._fp8_act(x), w13.astype(np.float64), w2.astype(np.float64), fp8=True)
+    got = ffn._expert(ffn._fp8_act(x), *ffn.fp8_weights(w13.astype(np.float64), w2.astype(np.float64)),
+                      fp8=True)
     ref = _fp8_expert_torch(x, w13, w2)
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert rel < 1e-12, rel
