@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "moe_workspace_bytes": ([D], SZ),
             "moe_route": ([D, P, P, P, P, P, P, P, P, P], I32),
             "moe_permute": ([D, P, P, P, P, P, P, P, P, SZ, P], I32),
+            "moe_permute_noalloc": ([D, P, P, P, P, P, P, P, P], I32),
             "moe_expert_ffn_workspace_bytes": ([D, I32, I32, I32], SZ),
             "moe_expert_ffn": ([D, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_combine": ([D, P, P, P, P, P, P, P], I32),
@@ -184,6 +185,14 @@ def moe_permute(desc, topk_idx, offsets, row_token, slot_row, ws, counts=None, u
         _ptr(row_token, "row_token"), _ptr(slot_row, "slot_row"), _ptr(counts, "counts", False),
         _ptr(u, "u", False), _ptr(x_perm, "x_perm", False), _ptr(ws, "ws"),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_permute_noalloc(desc, topk_idx, offsets, row_token, slot_row, counts=None, u=None,
+                        x_perm=None, stream=None):
+    _check("moe_permute_noalloc", lib().moe_permute_noalloc(
+        ctypes.byref(desc), _ptr(topk_idx, "topk_idx"), _ptr(offsets, "offsets"),
+        _ptr(row_token, "row_token"), _ptr(slot_row, "slot_row"), _ptr(counts, "counts", False),
+        _ptr(u, "u", False), _ptr(x_perm, "x_perm", False), _stream(stream)))
 
 
 def moe_expert_ffn(desc, n_experts, inter, rows, x, offsets, w13, w2, y, ws, row_token=None,

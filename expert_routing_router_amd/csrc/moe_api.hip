@@ -2,6 +2,7 @@
 // workspace layout, and the launch sequence of each call.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include "common.h"
 #include "moe_internal.h"
 
@@ -284,19 +285,11 @@ extern "C" int moe_route(const moe_desc_t* d, const void* u, const void* E, cons
   return hip_status(launch_route(a, scores_in ? kFrontScoresIn : route_front(d), s));
 }
 
-extern "C" int moe_permute(const moe_desc_t* d, const int32_t* topk_idx, int32_t* offsets, int32_t* row_token,
-                           int32_t* slot_row, int32_t* counts, const void* u, void* x_perm, void* ws,
-                           size_t ws_bytes, moe_stream_t stream) {
-  int st = moe_validate(d);
-  if (st) return st;
-  if (!aligned(topk_idx) || !aligned(offsets) || !aligned(row_token) || !aligned(slot_row)) return MOE_EINVAL;
-  if (!aligned_or_null(counts) || !aligned_or_null(u) || !aligned_or_null(x_perm)) return MOE_EINVAL;
-  if ((u == nullptr) != (x_perm == nullptr)) return MOE_EINVAL;
-  if (!aligned(ws)) return MOE_EINVAL;
-  const Ws w = layout(d);
-  if (ws_bytes < w.total) return MOE_EWORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  uint8_t* base = (uint8_t*)ws;
+// The dispatch layout from topk_idx into caller buffers, with the bitmap and
+// word-prefix scratch at `bitmap` / `wprefix` (sized for ceil(T/64) x N_r words).
+static int permute_into(const moe_desc_t* d, const int32_t* topk_idx, int32_t* offsets, int32_t* row_token,
+                        int32_t* slot_row, int32_t* counts, const void* u, void* x_perm, uint64_t* bitmap,
+                        int32_t* wprefix, hipStream_t s) {
   if (d->T == 0) {
     MOE_TRY(launch_fill_i32(offsets, 0, d->n_routed + 1, s));
     if (counts) MOE_TRY(launch_fill_i32(counts, 0, d->n_routed, s));
@@ -304,8 +297,7 @@ extern "C" int moe_permute(const moe_desc_t* d, const int32_t* topk_idx, int32_t
   }
   PermuteArgs p;
   p.idx = topk_idx; p.T = d->T; p.K = d->top_k; p.n_routed = d->n_routed;
-  p.bitmap = (uint64_t*)(base + w.bitmap); p.wprefix = (int32_t*)(base + w.wprefix);
-  p.counts_ws = (int32_t*)(base + w.counts);
+  p.bitmap = bitmap; p.wprefix = wprefix; p.counts_ws = nullptr;
   p.offsets = offsets; p.row_token = row_token; p.slot_row = slot_row; p.counts_out = counts;
   p.n_extra_seg = 0; p.mtile_prefix = nullptr; p.bm = 0;
   MOE_TRY(launch_permute(p, s));
@@ -313,6 +305,75 @@ extern "C" int moe_permute(const moe_desc_t* d, const int32_t* topk_idx, int32_t
     MOE_TRY(launch_gather_rows(u, d->T, row_token, offsets + d->n_routed, x_perm, (long)d->T * d->top_k,
                                d->d * (int)esize(d->in_dtype), s));
   return MOE_OK;
+}
+
+static int permute_args_ok(const moe_desc_t* d, const int32_t* topk_idx, const int32_t* offsets,
+                           const int32_t* row_token, const int32_t* slot_row, const int32_t* counts,
+                           const void* u, const void* x_perm) {
+  int st = moe_validate(d);
+  if (st) return st;
+  if (!aligned(topk_idx) || !aligned(offsets) || !aligned(row_token) || !aligned(slot_row)) return MOE_EINVAL;
+  if (!aligned_or_null(counts) || !aligned_or_null(u) || !aligned_or_null(x_perm)) return MOE_EINVAL;
+  if ((u == nullptr) != (x_perm == nullptr)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+extern "C" int moe_permute(const moe_desc_t* d, const int32_t* topk_idx, int32_t* offsets, int32_t* row_token,
+                           int32_t* slot_row, int32_t* counts, const void* u, void* x_perm, void* ws,
+                           size_t ws_bytes, moe_stream_t stream) {
+  int st = permute_args_ok(d, topk_idx, offsets, row_token, slot_row, counts, u, x_perm);
+  if (st) return st;
+  if (!aligned(ws)) return MOE_EINVAL;
+  const Ws w = layout(d);
+  if (ws_bytes < w.total) return MOE_EWORKSPACE;
+  uint8_t* base = (uint8_t*)ws;
+  return permute_into(d, topk_idx, offsets, row_token, slot_row, counts, u, x_perm,
+                      (uint64_t*)(base + w.bitmap), (int32_t*)(base + w.wprefix), (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- permute without allocation
+// The scratch of moe_permute_noalloc lives in this file-scope device array.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device with hipGetSymbolAddress and
+// only that address is ever handed to kernels. Each GPU holds its own copy
+// until the process ends.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+}  // namespace
+
+// Device address of `scratch` on the current device (looked up on first use).
+static int scratch_address(void** out) {
+  int dev = 0;
+  MOE_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ENOTSUP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    MOE_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return MOE_EHIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
+extern "C" int moe_permute_noalloc(const moe_desc_t* d, const int32_t* topk_idx, int32_t* offsets,
+                                   int32_t* row_token, int32_t* slot_row, int32_t* counts, const void* u,
+                                   void* x_perm, moe_stream_t stream) {
+  int st = permute_args_ok(d, topk_idx, offsets, row_token, slot_row, counts, u, x_perm);
+  if (st) return st;
+  const size_t words = (size_t)((d->T + 63) / 64) * d->n_routed;
+  const size_t bitmap_bytes = al256(words * 8);
+  if (bitmap_bytes + al256(words * 4) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_EWORKSPACE;
+  void* base = nullptr;
+  if ((st = scratch_address(&base))) return st;
+  // every bitmap word and word prefix in range is written before it is read: nothing to clear
+  return permute_into(d, topk_idx, offsets, row_token, slot_row, counts, u, x_perm, (uint64_t*)base,
+                      (int32_t*)((uint8_t*)base + bitmap_bytes), (hipStream_t)stream);
 }
 
 static GemmArgs gemm_args(const void* x, long x_rows, const float* xs, const int32_t* ridx,

@@ -154,6 +154,22 @@ int moe_permute(const moe_desc_t* desc, const int32_t* topk_idx, int32_t* offset
                 const void* u, void* x_perm, void* ws, size_t ws_bytes,
                 moe_stream_t stream);
 
+/* moe_permute for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments and results as moe_permute without the workspace. Its
+ * bitmap and word-prefix scratch, 12 * ceil(T/64) * N_r bytes (plus
+ * alignment), lives in a device array of MOE_NOALLOC_SCRATCH_BYTES held by
+ * the library on each GPU it runs on until the process ends; the call neither
+ * allocates nor frees anything. MOE_EWORKSPACE when the scratch would not fit
+ * (T above about 174k tokens at N_r = 256). Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (on different streams, or from
+ * different host threads before the first finishes) race, and must be
+ * serialised by the caller. Nothing in the scratch needs to start at zero. */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_permute_noalloc(const moe_desc_t* desc, const int32_t* topk_idx, int32_t* offsets,
+                        int32_t* row_token, int32_t* slot_row, int32_t* counts,
+                        const void* u, void* x_perm, moe_stream_t stream);
+
 /* Grouped SwiGLU experts over `rows` permuted rows in n_experts segments:
  *   y[r] = W2_e (SiLU(W1_e x_r) * (W3_e x_r)) for offsets[e] <= r < offsets[e+1].
  * (xyznot.com guides section 2, output equation; the SwiGLU form is a
