@@ -13,7 +13,8 @@ import re
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe_rocm.so")
+# MOE_ROCM_LIB names another build of the same library (e.g. the host-sanitizer build)
+LIB_PATH = os.environ.get("MOE_ROCM_LIB") or os.path.join(HERE, "libmoe_rocm.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "moe_rocm.h")
 
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
