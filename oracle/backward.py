@@ -19,6 +19,8 @@ tests pin it with central finite differences of the forward oracle.
 import numpy as np
 import torch
 
+from . import numerics as nx
+
 
 def _swiglu(x, w13, w2):
     inter = w13.shape[0] // 2
@@ -79,3 +81,98 @@ def expert_weight_grads(u_rows64, gate_rows64, dout_rows64, w13_64, w2_64):
     out = g * _swiglu(u, W13, W2)
     (out * torch.tensor(dout_rows64, dtype=torch.float64)).sum().backward()
     return W13.grad.numpy(), W2.grad.numpy()
+
+
+# ----------------------------------------------------------------------------- FP8 layer
+# The pages run all three GEMMs of a linear layer in E4M3 (pwwt.cn note section
+# 3: Fprop, Dgrad and Wgrad in FP8, FP8 activations kept for the backward; the
+# guides' key ideas: E4M3 everywhere, 1x128 activation tiles, 128x128 weight
+# blocks). Readings where the pages stop (listed in the design notes):
+#  * every GEMM input that is not a weight is quantised in tiles of 128 along
+#    that GEMM's reduction dimension: Fprop and Dgrad inputs in 1x128 tiles
+#    along their last axis; the two Wgrad inputs (the reduction runs over an
+#    expert's rows) in 128x1 tiles along the rows, starting at the expert's
+#    first row (a partial last tile holds the remaining rows);
+#  * the weights are the layer's E4M3 weights (128x128 blocks), the same
+#    values in Fprop and Dgrad; the weight gradient is taken with respect to
+#    those values;
+#  * the quantisers pass gradients straight through; everything else (router,
+#    gates, SwiGLU) is differentiated exactly, in fp64.
+
+def q_rows(x):
+    """1x128 tiles along the last axis: E4M3 quantise-dequantise, fp64 -> fp64."""
+    x = np.asarray(x, np.float64)
+    return nx.dequant_act(*nx.quant_act_1x128(x.astype(np.float32)))
+
+
+def q_cols(x):
+    """128x1 tiles along the rows (from row 0; the last tile may be partial)."""
+    x = np.asarray(x, np.float64)
+    n = x.shape[0]
+    pad = (-n) % 128
+    xt = np.concatenate([x, np.zeros((pad, x.shape[1]))], axis=0).T
+    return q_rows(xt).T[:n]
+
+
+class _Fp8Linear(torch.autograd.Function):
+    """y = Qr(x) W^T for W on the E4M3 grid; backward as the FP8 Dgrad
+    dx = Qr(dy) W and Wgrad dW = Qc(dy)^T Qc(x)."""
+
+    @staticmethod
+    def forward(ctx, x, w, qr, qc):
+        ctx.save_for_backward(x, w)
+        ctx.qr, ctx.qc = qr, qc
+        return torch.from_numpy(qr(x.detach().numpy())) @ w.T
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, w = ctx.saved_tensors
+        dyn, xn = dy.detach().numpy(), x.detach().numpy()
+        dx = torch.from_numpy(ctx.qr(dyn)) @ w
+        dw = torch.from_numpy(ctx.qc(dyn)).T @ torch.from_numpy(ctx.qc(xn))
+        return dx, dw, None, None
+
+
+def _swiglu_fp8(x, w13, w2, qr, qc):
+    inter = w13.shape[0] // 2
+    ab = _Fp8Linear.apply(x, w13, qr, qc)
+    a, v = ab[:, :inter], ab[:, inter:]
+    return _Fp8Linear.apply(a * torch.sigmoid(a) * v, w2, qr, qc)
+
+
+def layer_grads_fp8(u64, e64, idx, dout64, w13q, w2q, w13sq=(), w2sq=(), experts=None, quantise=True):
+    """layer_grads for the FP8 layer: w13q / w2q (mappings expert -> fp64 arrays)
+    and w13sq / w2sq are the E4M3 weights (ffn.fp8_weights of the masters); each
+    expert's rows go through the FP8 GEMMs above. quantise=False replaces every
+    quantiser by the identity, which must give layer_grads on the same weights."""
+    ident = (lambda a: np.asarray(a, np.float64))
+    qr, qc = (q_rows, q_cols) if quantise else (ident, ident)
+    u = torch.tensor(u64, dtype=torch.float64, requires_grad=True)
+    E = torch.tensor(e64, dtype=torch.float64, requires_grad=True)
+    idx_t = torch.tensor(np.asarray(idx), dtype=torch.long)
+    used = sorted(set(np.asarray(idx).reshape(-1).tolist()))
+    want = used if experts is None else sorted(experts)
+    W13 = {e: torch.tensor(w13q[e], dtype=torch.float64, requires_grad=e in want) for e in used}
+    W2 = {e: torch.tensor(w2q[e], dtype=torch.float64, requires_grad=e in want) for e in used}
+    W13s = [torch.tensor(w, dtype=torch.float64, requires_grad=True) for w in w13sq]
+    W2s = [torch.tensor(w, dtype=torch.float64, requires_grad=True) for w in w2sq]
+
+    s = torch.sigmoid(u @ E.T)
+    sel = torch.gather(s, 1, idx_t)
+    g = sel / sel.sum(dim=1, keepdim=True)
+    out = u
+    for a, b in zip(W13s, W2s):
+        out = out + _swiglu_fp8(u, a, b, qr, qc)
+    routed = torch.zeros_like(u)
+    for e in used:
+        rows, ks = np.nonzero(np.asarray(idx) == e)     # rows in token order
+        rows_t, ks_t = torch.tensor(rows), torch.tensor(ks)
+        y = _swiglu_fp8(u[rows_t], W13[e], W2[e], qr, qc)
+        routed = routed.index_add(0, rows_t, g[rows_t, ks_t][:, None] * y)
+    out = out + routed
+    (out * torch.tensor(dout64, dtype=torch.float64)).sum().backward()
+    return {
+        "du": u.grad.numpy(), "dE": E.grad.numpy(),
+        "dw13": {e: W13[e].grad.numpy() for e in want}, "dw2": {e: W2[e].grad.numpy() for e in want},
+        "dw13s": [w.grad.numpy() for w in W13s], "dw2s": [w.grad.numpy() for w in W2s],
+    }
