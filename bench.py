@@ -88,14 +88,35 @@ def measured_traffic(cfg):
         return None
 
 
-def cpu_baseline(cfg, n_sample_experts, log_fn):
-    """The oracle (unchanged) on a bounded sample of one step, scaled to tokens/s.
+class HostWeights:
+    """The layer's weights drawn once (seeded, host memory), handed to MoELayer
+    with the generator's interface and reused by the CPU oracle."""
 
-    Sample: routing of all T tokens (fp64 logits, sigmoid, group-limited top-K,
-    gates); the SwiGLU of the first `n_sample_experts` routed experts over
-    their routed rows; the shared experts over T/2 tokens. Per-forward time =
-    t_route + t_sample * N_r / n_sample + t_shared * 2.
-    """
+    def __init__(self, cfg, gen):
+        self.gen = gen
+        self.w13, self.w2, self.w13s, self.w2s = gen.all_weights(cfg)
+
+    def centroids(self, cfg):
+        return self.gen.centroids(cfg)
+
+    def expert_w13(self, cfg, e):
+        return self.w13[e]
+
+    def expert_w2(self, cfg, e):
+        return self.w2[e]
+
+    def shared_w13(self, cfg, s):
+        return self.w13s[s]
+
+    def shared_w2(self, cfg, s):
+        return self.w2s[s]
+
+
+def cpu_baseline(cfg, hw, log_fn):
+    """The oracle (unchanged) on one whole step: routing of all T tokens (fp64
+    logits, sigmoid, group-limited top-K, gates) and the layer output over all
+    tokens (every routed expert over its rows, the shared experts over every
+    token). Returns (record, the oracle's route, its fp64 affinities, its output)."""
     import numpy as np
     from oracle import ffn, numerics as nx, routing
     from workloads import gen
@@ -115,37 +136,49 @@ def cpu_baseline(cfg, n_sample_experts, log_fn):
     u = gen.tokens(cfg, 0)
     E = gen.centroids(cfg)
     b = gen.bias_init(cfg)
-    sample = list(range(min(n_sample_experts, cfg.n_routed)))
-    w = {e: (gen.expert_w13(cfg, e), gen.expert_w2(cfg, e)) for e in sample}
-    ws = [(gen.shared_w13(cfg, s), gen.shared_w2(cfg, s)) for s in range(cfg.n_shared)]
-    wdt = "bf16" if cfg.expert_dtype == "bf16" else "f32"
     t0 = time.perf_counter()
-    u64 = nx.to_f64(u, cfg.in_dtype)
-    r, s64, _ = routing.route_tokens(u64, nx.to_f64(E, cfg.router_dtype), b, cfg)
+    r, s64, _ = routing.route_tokens(nx.to_f64(u, cfg.in_dtype), nx.to_f64(E, cfg.router_dtype), b, cfg)
     t_route = time.perf_counter() - t0
     t0 = time.perf_counter()
-    rows_done = 0
-    for e in sample:
-        rows, ks = np.nonzero(r.idx == e)
-        y = ffn.swiglu(u64[rows], nx.to_f64(w[e][0], wdt), nx.to_f64(w[e][1], wdt))
-        _ = r.gate[rows, ks][:, None] * y
-        rows_done += len(rows)
-    t_routed = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    Tsub = max(1, cfg.T // 2)
-    for s in range(cfg.n_shared):
-        ffn.swiglu(u64[:Tsub], nx.to_f64(ws[s][0], wdt), nx.to_f64(ws[s][1], wdt))
-    t_shared = time.perf_counter() - t0
-    per_fwd = t_route + t_routed * cfg.n_routed / len(sample) + t_shared * cfg.T / Tsub
-    log_fn("cpu oracle: route %.2fs, %d experts (%d rows) %.2fs, shared %d rows %.2fs -> %.1fs/forward"
-           % (t_route, len(sample), rows_done, t_routed, Tsub, t_shared, per_fwd))
-    return {"value": cfg.T / per_fwd, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": "one %d-token step: routing of all tokens; SwiGLU of experts 0..%d over their %d "
-                      "routed rows, scaled by %d/%d; shared expert over %d tokens, scaled by %d; fp64 numpy "
-                      "(BLAS %s, %d threads; %s, %d cores available); measured %.1f s of CPU work"
-                      % (cfg.T, len(sample) - 1, rows_done, cfg.n_routed, len(sample), Tsub,
-                         cfg.T // Tsub, blas, cores, cpu_model, len(os.sched_getaffinity(0)),
-                         t_route + t_routed + t_shared)}
+    out = ffn.layer(cfg, u, r.idx, r.gate, hw.w13, hw.w2, hw.w13s, hw.w2s)
+    t_ffn = time.perf_counter() - t0
+    per_fwd = t_route + t_ffn
+    log_fn("cpu oracle: route %.2fs, experts %.2fs -> %.1fs/forward" % (t_route, t_ffn, per_fwd))
+    rec = {"value": cfg.T / per_fwd, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+           "sample": "one whole %d-token step (routing of every token, every routed expert over its rows, "
+                     "the shared experts over every token), fp64 numpy (BLAS %s, %d threads; %s, %d cores "
+                     "available); %.1f s of CPU work"
+                     % (cfg.T, blas, cores, cpu_model, len(os.sched_getaffinity(0)), per_fwd)}
+    return rec, r, s64, out
+
+
+def parity_line(cfg, hw, u, r, s64, out_ref, out_gpu, idx_gpu):
+    """Relative L2 error of the GPU's step-0 output over all [T, d] against the
+    oracle's, with the oracle re-evaluated on the GPU's experts for the tokens
+    that routed differently (near ties of the keys, allowed by the bar)."""
+    import numpy as np
+    from oracle import ffn, numerics as nx
+    same = (np.sort(idx_gpu, 1) == np.sort(r.idx, 1)).all(axis=1)
+    ref = out_ref.copy()
+    diff = np.nonzero(~same)[0]
+    if len(diff):
+        idx_fix = r.idx.copy()
+        gate_fix = r.gate.copy()
+        for t in diff:
+            idx_fix[t] = idx_gpu[t]
+            sel = s64[t, idx_gpu[t]]
+            gate_fix[t] = sel / sel.sum()
+        ref[diff] = ffn.layer(cfg, u, idx_fix, gate_fix, hw.w13, hw.w2, hw.w13s, hw.w2s, tokens=diff)
+    err = float(np.linalg.norm(out_gpu - ref) / np.linalg.norm(ref))
+    u64 = nx.to_f64(u, cfg.in_dtype)
+    err_ffn = float(np.linalg.norm(out_gpu - ref) / np.linalg.norm(ref - u64))
+    bar = {"f32": 1e-5, "bf16": 1e-2, "fp8": 3e-2}[cfg.expert_dtype]
+    rec = {"rel_l2": round(err, 6), "rel_l2_ffn_part": round(err_ffn, 6), "bar": bar, "met": err <= bar,
+           "over": "all %d x %d outputs of step 0" % (cfg.T, cfg.d),
+           "tokens_routed_differently": int(len(diff))}
+    if cfg.expert_dtype == "fp8":
+        rec["against"] = "the unquantised oracle (the E4M3 recipe alone is about 3.2e-2 off on these inputs)"
+    return rec
 
 
 def main():
@@ -155,7 +188,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="v3")
     ap.add_argument("--T", type=int, default=0, help="override tokens per batch")
-    ap.add_argument("--cpu-sample-experts", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", type=int, default=5,
                     help="also time this many moe_backward calls (bf16 layers; reported beside the step; 0: skip)")
@@ -198,7 +230,8 @@ def main():
     torch.cuda.set_device(0)
     t0 = time.time()
     log("building %s layer (weights drawn and uploaded) ..." % cfg.name)
-    layer = MoELayer(cfg, gen, device="cuda:0")
+    hw = HostWeights(cfg, gen)
+    layer = MoELayer(cfg, hw, device="cuda:0")
     log("layer ready in %.1fs" % (time.time() - t0))
     nb = max(1, min(4, args.steps + args.warmup))
     us = [np_to_device(gen.tokens(cfg, s), cfg.in_dtype, "cuda:0") for s in range(nb)]
@@ -236,6 +269,43 @@ def main():
     tokens_per_s = cfg.T * args.steps / elapsed
     log("timed %d steps: %.3f ms/step (events %.3f ms/step), %.0f tokens/s"
         % (args.steps, ms_per_step, ev_ms / args.steps, tokens_per_s))
+
+    # the same steps through the row-major weights the ABI takes (no K-blocked copies)
+    row_major = None
+    if layer.blocked:
+        import ctypes
+        wr = M.MoeWeights.from_buffer_copy(layer.weights)
+        wr.w13_blk = wr.w2_blk = wr.w13_shared_blk = wr.w2_shared_blk = None
+        desc = M.desc_from_config(cfg)
+        b_rm = np_to_device(gen.bias_init(cfg), "f32", "cuda:0")
+
+        def fwd_rm(i):
+            st = M.lib().moe_forward(ctypes.byref(desc), ctypes.byref(wr), us[i % nb].data_ptr(), b_rm.data_ptr(),
+                                     layer.out.data_ptr(), None, 1, layer.ws.data_ptr(), layer.ws.numel(),
+                                     stream.cuda_stream)
+            if st != M.MOE_OK:
+                raise M.MoeError("moe_forward", st, M.lib())
+        for i in range(args.warmup):
+            fwd_rm(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fwd_rm(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        row_major = {"ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4),
+                     "tokens_per_s": round(cfg.T * args.steps / e0.elapsed_time(e1) * 1e3, 1),
+                     "note": "moe_forward on the row-major expert weights of the ABI (no K-blocked copies), "
+                             "same steps"}
+        log("row-major weights: %.3f ms/step" % row_major["ms_per_step"])
+
+    # step 0 from the initial bias, kept for the parity check against the oracle
+    b0 = np_to_device(gen.bias_init(cfg), "f32", "cuda:0")
+    layer.forward(us[0], b0, update_bias=False)
+    torch.cuda.synchronize()
+    out0 = layer.out.float().cpu().numpy().astype("float64")
+    idx0 = layer.idx.cpu().numpy()
 
     # load balance over a few extra (untimed) steps
     loads = []
@@ -406,11 +476,13 @@ def main():
                 "bytes_per_launch": g1["bytes"], "avg_ms": round(g1_ms, 4),
                 "measured_peak": round(read_gbs, 1), "frac_of_measured": round(achieved / read_gbs, 4)}
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
         del layer
         torch.cuda.empty_cache()
-        cpu = cpu_baseline(cfg, args.cpu_sample_experts, log)
+        cpu, r_ref, s64_ref, out_ref = cpu_baseline(cfg, hw, log)
+        parity = parity_line(cfg, hw, gen.tokens(cfg, 0), r_ref, s64_ref, out_ref, out0, idx0)
+        log("parity: step-0 output rel-L2 %.3e against the oracle (bar %.0e)" % (parity["rel_l2"], parity["bar"]))
 
     dtype = {"bf16": "bf16", "fp8": "fp8_e4m3", "f32": "f32"}[cfg.expert_dtype]
     rec = {
@@ -420,14 +492,19 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": "%s: T=%d d=%d N_r=%d K=%d G=%d M=%d q=%d N_s=%d I=%d I_s=%d experts=%s "
-                               "router=%s; forward + bias update per step"
+                               "router=%s; forward + bias update per step%s"
                                % (cfg.name, cfg.T, cfg.d, cfg.n_routed, cfg.top_k, cfg.n_groups,
                                   cfg.topk_groups, cfg.group_topk, cfg.n_shared, cfg.inter,
-                                  cfg.inter_shared, cfg.expert_dtype, cfg.router_dtype),
+                                  cfg.inter_shared, cfg.expert_dtype, cfg.router_dtype,
+                                  "; the timed forward reads K-blocked copies of the expert weights "
+                                  "(moe_pack_expert_weights, made once before timing; the row-major ABI "
+                                  "path is timed in row_major_weights)" if row_major else ""),
                    "T": cfg.T, "d": cfg.d, "n_routed": cfg.n_routed, "top_k": cfg.top_k,
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
+        "row_major_weights": row_major,
         "kernels": kernels,
         "grouped_gemm_mfma_frac": kernels["grouped_gemm"]["mfma_frac"],
         "max_over_mean_load": [round(x, 3) for x in loads],

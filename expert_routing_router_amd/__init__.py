@@ -12,7 +12,7 @@ from ._lib import (  # noqa: F401
     MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_QUANT_ACT_1x128, MOE_QUANT_W_128x128,
     MoeDesc, MoeError, MoeGrads, MoeRouteOut, MoeWeights,
     lib, header_symbols, make_desc, desc_from_config, make_weights,
-    moe_validate, moe_workspace_bytes, moe_expert_ffn_workspace_bytes,
+    moe_validate, moe_workspace_bytes, moe_expert_ffn_workspace_bytes, moe_route_workspace_bytes,
     moe_route, moe_permute, moe_permute_noalloc, moe_expert_ffn, moe_combine, moe_update_bias, moe_forward,
     moe_quantize_fp8, moe_seq_balance_workspace_bytes, moe_seq_balance_loss,
     moe_transpose_expert_weights, moe_pack_expert_weights, moe_backward_workspace_bytes, moe_backward, make_grads,

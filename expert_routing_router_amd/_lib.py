@@ -20,7 +20,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "moe_rocm.h")
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_QUANT_ACT_1x128, MOE_QUANT_W_128x128 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 
 
@@ -72,7 +72,8 @@ def lib() -> ctypes.CDLL:
             "moe_last_hip_error": ([], I32),
             "moe_validate": ([D], I32),
             "moe_workspace_bytes": ([D], SZ),
-            "moe_route": ([D, P, P, P, P, P, P, P, P, P], I32),
+            "moe_route_workspace_bytes": ([D], SZ),
+            "moe_route": ([D, P, P, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_permute": ([D, P, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_permute_noalloc": ([D, P, P, P, P, P, P, P, P], I32),
             "moe_expert_ffn_workspace_bytes": ([D, I32, I32, I32], SZ),
@@ -170,13 +171,22 @@ def moe_expert_ffn_workspace_bytes(desc, n_experts, inter, rows) -> int:
     return lib().moe_expert_ffn_workspace_bytes(ctypes.byref(desc), n_experts, inter, rows)
 
 
+def moe_route_workspace_bytes(desc) -> int:
+    return lib().moe_route_workspace_bytes(ctypes.byref(desc))
+
+
 def moe_route(desc, b, topk_idx, topk_gate, counts, u=None, E=None, scores_in=None,
-              scores_out=None, stream=None):
+              scores_out=None, ws=None, stream=None):
+    """ws: the router's scratch (moe_route_workspace_bytes); allocated here when not given."""
+    if ws is None and scores_in is None:
+        n = moe_route_workspace_bytes(desc)
+        if n:
+            ws = torch.empty(n, dtype=torch.uint8, device=b.device)
     _check("moe_route", lib().moe_route(
         ctypes.byref(desc), _ptr(u, "u", False), _ptr(E, "E", False), _ptr(b, "b"),
         _ptr(scores_in, "scores_in", False), _ptr(scores_out, "scores_out", False),
         _ptr(topk_idx, "topk_idx"), _ptr(topk_gate, "topk_gate"), _ptr(counts, "counts"),
-        _stream(stream)))
+        _ptr(ws, "ws", False), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_permute(desc, topk_idx, offsets, row_token, slot_row, ws, counts=None, u=None,

@@ -95,9 +95,118 @@ __global__ __launch_bounds__(CB_THREADS) void combine_kernel(CombineArgs a) {
   }
 }
 
+// The same sum with one wave per token: the token's row indices and gates are
+// wave-uniform, so they come through the scalar cache (no LDS, no barrier),
+// and every lane handles 8 consecutive elements of CW chunks of 512 elements
+// at once, so a lane has CW * (2 + K) loads in flight. Everything here is read
+// or written once: loads and stores carry the non-temporal hint.
+#ifndef COMBINE_WAVE
+#define COMBINE_WAVE 1
+#endif
+#ifndef COMBINE_CW
+#define COMBINE_CW 8
+#endif
+#ifndef COMBINE_ROWS
+#define COMBINE_ROWS 2
+#endif
+constexpr int CW = COMBINE_CW;
+constexpr int CWR = COMBINE_ROWS;    // routed rows loaded together
+
+template <bool BF>
+__device__ __forceinline__ void combine_load8_nt(const void* base, size_t row, int d, int c, float* v) {
+  if (BF) {
+    const i32x4 q = __builtin_nontemporal_load((const i32x4*)((const uint16_t*)base + row * d + c));
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = __uint_as_float(((uint32_t)q[i]) << 16);
+      v[2 * i + 1] = __uint_as_float(((uint32_t)q[i]) & 0xFFFF0000u);
+    }
+  } else {
+    const f32x4 p0 = __builtin_nontemporal_load((const f32x4*)((const float*)base + row * d + c));
+    const f32x4 p1 = __builtin_nontemporal_load((const f32x4*)((const float*)base + row * d + c + 4));
+#pragma unroll
+    for (int i = 0; i < 4; i++) { v[i] = p0[i]; v[4 + i] = p1[i]; }
+  }
+}
+
+template <bool IO_BF16, bool Y_BF16>
+__global__ __launch_bounds__(64) void combine_wave_kernel(CombineArgs a) {
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const unsigned n_rows = (unsigned)(a.T * a.K);
+  const int32_t* srow = a.slot_row + (size_t)t * a.K;
+  const float* sg = a.gate + (size_t)t * a.K;
+  for (int c0 = lane * 8; c0 < a.d; c0 += 64 * 8 * CW) {
+    float acc[CW][8];
+    bool in[CW];
+#pragma unroll
+    for (int w = 0; w < CW; w++) {
+      const int c = c0 + w * 512;
+      in[w] = c < a.d;
+      combine_load8_nt<IO_BF16>(a.u, t, a.d, in[w] ? c : 0, acc[w]);
+    }
+    for (int k0 = 0; k0 < a.K; k0 += CWR) {
+      float v[CW][CWR][8];
+      bool use[CWR];
+#pragma unroll
+      for (int j = 0; j < CWR; j++) {
+        const int k = k0 + j;
+        const int r = k < a.K ? srow[k] : 0;
+        use[j] = k < a.K && (unsigned)r < n_rows;    // a dropped selection adds nothing
+#pragma unroll
+        for (int w = 0; w < CW; w++)
+          combine_load8_nt<Y_BF16>(a.y, use[j] ? (size_t)r : 0, a.d, in[w] ? c0 + w * 512 : 0, v[w][j]);
+      }
+      if (k0 == 0) {
+        for (int s = 0; s < a.n_shared; s++) {
+#pragma unroll
+          for (int w = 0; w < CW; w++) {
+            float x[8];
+            combine_load8_nt<Y_BF16>(a.y_shared, (size_t)s * a.shared_stride + t, a.d, in[w] ? c0 + w * 512 : 0, x);
+#pragma unroll
+            for (int i = 0; i < 8; i++) acc[w][i] += x[i];
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < CWR; j++) {
+        if (use[j]) {
+          const float g = sg[k0 + j];
+#pragma unroll
+          for (int w = 0; w < CW; w++)
+#pragma unroll
+            for (int i = 0; i < 8; i++) acc[w][i] = fmaf(g, v[w][j][i], acc[w][i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < CW; w++) {
+      if (!in[w]) continue;
+      const int c = c0 + w * 512;
+      if (IO_BF16) {
+        i32x4 q;
+#pragma unroll
+        for (int i = 0; i < 4; i++) q[i] = (int)pack_bf16x2(acc[w][2 * i], acc[w][2 * i + 1]);
+        __builtin_nontemporal_store(q, (i32x4*)((uint16_t*)a.out + (size_t)t * a.d + c));
+      } else {
+        float* o = (float*)a.out + (size_t)t * a.d + c;
+        __builtin_nontemporal_store(f32x4{acc[w][0], acc[w][1], acc[w][2], acc[w][3]}, (f32x4*)o);
+        __builtin_nontemporal_store(f32x4{acc[w][4], acc[w][5], acc[w][6], acc[w][7]}, (f32x4*)(o + 4));
+      }
+    }
+  }
+}
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   const bool io = a.io_dtype == MOE_BF16, yb = a.y_dtype == MOE_BF16;
+  if (COMBINE_WAVE) {
+    if (io && yb) combine_wave_kernel<true, true><<<a.T, 64, 0, s>>>(a);
+    else if (io) combine_wave_kernel<true, false><<<a.T, 64, 0, s>>>(a);
+    else if (yb) combine_wave_kernel<false, true><<<a.T, 64, 0, s>>>(a);
+    else combine_wave_kernel<false, false><<<a.T, 64, 0, s>>>(a);
+    return hipGetLastError();
+  }
   if (io && yb) combine_kernel<true, true><<<a.T, CB_THREADS, 0, s>>>(a);
   else if (io) combine_kernel<true, false><<<a.T, CB_THREADS, 0, s>>>(a);
   else if (yb) combine_kernel<false, true><<<a.T, CB_THREADS, 0, s>>>(a);

@@ -161,9 +161,9 @@ struct Ws {
 static RouteArgs route_args(const moe_desc_t* d, const void* u, const void* E, const float* b,
                             const float* scores_in, float* scores_out, int32_t* idx, float* gate, int32_t* counts);
 
-// moe_forward routes large batches in two phases (tiled logits, then selection)
-static bool two_phase_router(const moe_desc_t* d) {
-  return route_two_phase_ok(route_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr));
+// device scratch of the router for this descriptor (shape-dependent path)
+static size_t route_scratch(const moe_desc_t* d) {
+  return router_scratch_bytes(route_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr));
 }
 
 static bool fused_shared(const moe_desc_t* d) { return d->n_shared == 0 || d->inter == d->inter_shared; }
@@ -218,13 +218,12 @@ static Ws layout(const moe_desc_t* d, bool capacity = false) {
   } else {
     w.qu = w.su = w.qh = w.sh = 0;
   }
-  w.rscratch = two_phase_router(d) ? take(route_two_phase_bytes(d->T, d->n_routed, d->d, d->router_dtype)) : 0;
+  w.rscratch = take(route_scratch(d));
   w.keep = w.dropped = w.scores = 0;
   if (capacity) {
     w.keep = take(T * K * 4);
     w.dropped = take(4);
-    // the two-phase router leaves the affinities at the start of its scratch
-    w.scores = two_phase_router(d) ? w.rscratch : take(T * N * 4);
+    w.scores = take(T * N * 4);      // the router's fp32 affinities, which the cap ranks by
   }
   w.total = o;
   return w;
@@ -248,12 +247,6 @@ extern "C" size_t moe_expert_ffn_workspace_bytes(const moe_desc_t* d, int32_t n_
   return o;
 }
 
-static int route_front(const moe_desc_t* d) {
-  const bool mfma_ok = d->in_dtype == MOE_BF16 && d->n_routed % 16 == 0 && d->d % 128 == 0;
-  if (!mfma_ok) return kFrontF64;
-  return d->router_dtype == MOE_BF16 ? kFrontMfma : kFrontMfmaSplitE;
-}
-
 static RouteArgs route_args(const moe_desc_t* d, const void* u, const void* E, const float* b,
                             const float* scores_in, float* scores_out, int32_t* idx, float* gate,
                             int32_t* counts) {
@@ -268,9 +261,14 @@ static RouteArgs route_args(const moe_desc_t* d, const void* u, const void* E, c
   return a;
 }
 
+extern "C" size_t moe_route_workspace_bytes(const moe_desc_t* d) {
+  if (moe_validate(d) != MOE_OK) return 0;
+  return route_scratch(d);
+}
+
 extern "C" int moe_route(const moe_desc_t* d, const void* u, const void* E, const float* b,
                          const float* scores_in, float* scores_out, int32_t* topk_idx, float* topk_gate,
-                         int32_t* counts, moe_stream_t stream) {
+                         int32_t* counts, void* ws, size_t ws_bytes, moe_stream_t stream) {
   int st = moe_validate(d);
   if (st) return st;
   const bool have_ue = u || E;
@@ -278,11 +276,13 @@ extern "C" int moe_route(const moe_desc_t* d, const void* u, const void* E, cons
   if (have_ue && (!aligned(u) || !aligned(E))) return MOE_EINVAL;
   if (scores_in && !aligned(scores_in)) return MOE_EINVAL;
   if (!aligned(b) || !aligned(topk_idx) || !aligned(topk_gate) || !aligned(counts)) return MOE_EINVAL;
-  if (!aligned_or_null(scores_out)) return MOE_EINVAL;
+  if (!aligned_or_null(scores_out) || !aligned_or_null(ws)) return MOE_EINVAL;
+  const size_t need = scores_in ? 0 : route_scratch(d);
+  if (need && (!ws || ws_bytes < need)) return MOE_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (d->T == 0) return hip_status(launch_fill_i32(counts, 0, d->n_routed, s));
   RouteArgs a = route_args(d, u, E, b, scores_in, scores_out, topk_idx, topk_gate, counts);
-  return hip_status(launch_route(a, scores_in ? kFrontScoresIn : route_front(d), s));
+  return hip_status(run_router(a, ws, s));
 }
 
 // The dispatch layout from topk_idx into caller buffers, with the bitmap and
@@ -548,13 +548,8 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
   prof_mark(-1, s);
   float* scores = capped ? (float*)(base + L.scores) : nullptr;
   // the loads come from the dispatch's bitmaps below, not from the router
-  RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, nullptr, idx, gate, nullptr);
-  if (two_phase_router(d)) {
-    MOE_TRY(launch_route_two_phase(ra, base + L.rscratch, s));
-  } else {
-    ra.scores_out = scores;
-    MOE_TRY(launch_route(ra, route_front(d), s));
-  }
+  RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, scores, idx, gate, nullptr);
+  MOE_TRY(run_router(ra, base + L.rscratch, s));
   prof_mark(MOE_STAGE_ROUTE, s);
 
   // 2. dispatch layout; shared experts become extra identity segments
@@ -719,7 +714,7 @@ static int backward_shape_ok(const moe_desc_t* d) {
 }
 
 struct BwdWs {
-  size_t idx, gate, scores, bitmap, wprefix, offsets, mtile, row_token, slot_row;
+  size_t idx, gate, scores, rscratch, bitmap, wprefix, offsets, mtile, row_token, slot_row;
   size_t ab, h, y, dy, dh, dab, dg, dz, pt, qt, kofs, total;
   long pitch;
 };
@@ -734,6 +729,7 @@ static BwdWs bwd_layout(const moe_desc_t* d) {
   w.idx = take(T * K * 4);
   w.gate = take(T * K * 4);
   w.scores = take(T * N * 4);
+  w.rscratch = take(route_scratch(d));
   w.bitmap = take(W * N * 8);
   w.wprefix = take(W * N * 4);
   w.offsets = take((n_seg + 1) * 4);
@@ -846,10 +842,10 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
   float* dg = (float*)(base + L.dg);
   float* dz = (float*)(base + L.dz);
 
-  // forward recompute: the same routing and dispatch as moe_forward (the fused
-  // router gives bit-identical affinities and selections), then A|B, H, Y
+  // forward recompute: the same routing and dispatch as moe_forward (the same router,
+  // which also keeps the affinities for the gate gradients), then A|B, H, Y
   RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, scores, idx, gate, nullptr);   // loads not needed
-  MOE_TRY(launch_route(ra, route_front(d), s));
+  MOE_TRY(run_router(ra, base + L.rscratch, s));
   const int bm = gemm_bm(d->expert_dtype, (int)(TK / N), d->d, d->inter);
   PermuteArgs p;
   p.idx = idx; p.T = T; p.K = K; p.n_routed = N;

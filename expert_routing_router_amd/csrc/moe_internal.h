@@ -7,18 +7,26 @@
 namespace moe {
 
 // ---------------------------------------------------------------- router
-enum RouterFront { kFrontScoresIn = 0, kFrontMfma = 1, kFrontMfmaSplitE = 2, kFrontF64 = 3 };
+enum RouterFront { kFrontScoresIn = 0, kFrontPartials = 1, kFrontF64 = 3 };
 struct RouteArgs {
   const void* u; const void* E; const float* b; const float* scores_in;
   float* scores_out; int32_t* idx; float* gate;
   int32_t* counts;   // nullable: per-expert loads, counted after the selection by a separate kernel
   int T, d, n_routed, top_k, n_groups, topk_groups, group_topk, group_score_biased;
   int in_dtype, router_dtype;
+  const float* partials = nullptr;   // kFrontPartials: [n_slices][T][n_routed] fp32 slice sums of the logits
+  int n_slices = 0;
 };
 hipError_t launch_route(const RouteArgs& a, int front, hipStream_t s);
-// Two-phase router (tiled logits kernel into a scores buffer, then selection
-// from it); same results as the fused front ends. Needs route_two_phase_bytes
-// of device scratch.
+// The router every entry point uses: the selection alone when scores_in is
+// set, else the split-K router (bf16 u and centroids, 256 experts), the tiled
+// two-phase router (N_r % 64 == 0), or the fp64 front end, by shape. Needs
+// router_scratch_bytes of device scratch (0 for the fp64 front end).
+size_t router_scratch_bytes(const RouteArgs& a);
+hipError_t run_router(const RouteArgs& a, void* scratch, hipStream_t s);
+bool route_splitk_ok(const RouteArgs& a);
+size_t route_splitk_bytes(int T, int d);
+hipError_t launch_route_splitk(const RouteArgs& a, void* scratch, hipStream_t s);
 bool route_two_phase_ok(const RouteArgs& a);
 size_t route_two_phase_bytes(int T, int N, int d, int router_dtype);
 hipError_t launch_route_two_phase(const RouteArgs& a, void* scratch, hipStream_t s);

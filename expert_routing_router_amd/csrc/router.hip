@@ -1,6 +1,6 @@
 // Router of the DeepSeekMoE layer on gfx950: affinities, biased group-limited
-// top-K and normalised gates (route_kernel, with a fused front end or fed by
-// the tiled logits_kernel), and the per-expert loads (count_loads_kernel).
+// top-K and normalised gates (route_kernel, fed by a logits kernel or with an
+// fp64 front end of its own), and the per-expert loads (count_loads_kernel).
 //
 //   s_{i,t} = sigmoid(u_t . e_i)       -- DeepSeek-V3 Technical Report guides
 //                                         (xyznot.com), "Metodo" section 2
@@ -9,20 +9,27 @@
 //   groups ranked by the sum of their   -- pwwt.cn note 1.3 (node-limited
 //   top K_r/M scores, at most M kept       routing; nodes = expert groups here)
 //
-// route_kernel: one workgroup (4 waves) owns 32 tokens and every expert (4
-// tokens when the affinities are handed in). The front end
-// writes the fp32 affinities of its tokens into LDS; the selection back end is
-// one code path whatever the front end was (MFMA logits, fp64 logits, or
-// affinities handed in by the caller), so the scores-in mode exercises exactly
-// the production selection.
+// Paths, by shape (run_router picks one):
+//  * split-K router (bf16 u and centroids, N_r = 256): logits_splitk_kernel
+//    computes 128 tokens x 256 experts over one of S slices of d per
+//    workgroup from centroids packed once per call (pack_centroids_kernel),
+//    writes each slice's sum as fp32, and route_kernel in partials mode adds
+//    the S slices, applies the sigmoid and selects;
+//  * tiled two-phase router (N_r % 64 == 0, bf16 u, bf16 or fp32 centroids):
+//    logits_kernel writes fp32 affinities, route_kernel selects from them;
+//  * any other shape: route_kernel with fp64 VALU logits.
+// The selection back end is one code path whatever the front end was
+// (affinities handed in by the caller included), so the scores-in mode
+// exercises exactly the production selection.
 //
-// Precision: the MFMA front end accumulates bf16 products (exact in fp32) in
-// fp32 over 128-element chunks of d and sums the chunks in fp64; the sigmoid
-// is evaluated in fp64 and rounded once to fp32. fp32 centroids are split into
-// three bf16 terms (hi + mid + lo reproduces the fp32 value exactly), so the
-// products stay exact on the bf16 MFMA path; the hi products and the much
-// smaller mid+lo products go to separate accumulators so the small terms are
-// not rounded against the large running sum.
+// Precision: bf16 products (exact in fp32) are summed by the MFMAs in fp32
+// over 128-element chunks of d, the chunks in fp64; the sigmoid is evaluated
+// in fp64 and rounded once to fp32. The split-K router rounds each slice's
+// fp64 sum to fp32 once before the S slices are added in fp64, in slice order.
+// fp32 centroids are split into three bf16 terms (hi + mid + lo reproduces the
+// fp32 value exactly), so the products stay exact on the bf16 MFMA path; the
+// hi products and the much smaller mid+lo products go to separate accumulators
+// so the small terms are not rounded against the large running sum.
 #include "common.h"
 #include "lds_dma.h"
 #include "moe_internal.h"
@@ -43,7 +50,7 @@ struct RouterLdsT {
   float s[BT][RT_NMAX];
   float b[RT_NMAX];
 };
-using RouterLds = RouterLdsT<RT_BT>;      // the fused front ends work on 32 tokens
+using RouterLds = RouterLdsT<RT_BT>;      // the fp64 front end works on 32 tokens
 
 __device__ __forceinline__ double sigmoid64(double z) {
   if (z >= 0.0) return 1.0 / (1.0 + exp(-z));
@@ -51,150 +58,7 @@ __device__ __forceinline__ double sigmoid64(double z) {
   return ez / (1.0 + ez);
 }
 
-union V16 { i32x4 i; bf16x8 h; uint16_t s[8]; };
-
-__device__ __forceinline__ void split3(const float* x, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
-  V16 a, b, c;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    float v = x[i];
-    uint16_t h = f32_to_bf16(v);
-    float r1 = v - bf16_to_f32(h);          // exact
-    uint16_t m = f32_to_bf16(r1);
-    float r2 = r1 - bf16_to_f32(m);         // exact
-    a.s[i] = h; b.s[i] = m; c.s[i] = f32_to_bf16(r2);
-  }
-  hi = a.h; mid = b.h; lo = c.h;
-}
-
 // ---------------------------------------------------------------- front ends
-// MFMA 16x16x32 bf16: lane l holds A row (l&15), B column (l&15), 8 k-values
-// at k-group (l>>4); D element (4*(l>>4)+r, l&15) in register r.
-// Wave w owns expert blocks w, w+4, ... (16 experts each) for all 32 tokens.
-// Fragments are loaded straight from global memory three k-steps ahead of
-// their MFMAs (four rotating register sets); every four k-steps (128 elements
-// of d) the fp32 MFMA sums are flushed into fp64 accumulators.
-template <bool SPLIT_E>
-struct RouterFrag {
-  bf16x8 a0, a1;
-  typename std::conditional<SPLIT_E, f32x4, bf16x8>::type b[4][SPLIT_E ? 2 : 1];
-};
-
-template <bool SPLIT_E>
-__device__ void front_mfma(const RouteArgs& a, RouterLds& sh, int t0) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r16 = lane & 15, kg = lane >> 4;
-  const int nblk = a.n_routed >> 4;
-  const int nb = nblk > wave ? (nblk - wave + 3) >> 2 : 0;   // blocks wave, wave+4, ...
-  const uint16_t* u = (const uint16_t*)a.u;
-  const int ta0 = min(t0 + r16, a.T - 1), ta1 = min(t0 + 16 + r16, a.T - 1);
-  const uint16_t* pa0 = u + (size_t)ta0 * a.d + kg * 8;
-  const uint16_t* pa1 = u + (size_t)ta1 * a.d + kg * 8;
-  // B rows of this wave's blocks; slots past nb (a wave with fewer blocks, or none when
-  // N_r < 64) re-read block 0, which always exists, so every load stays inside E
-  const uint16_t* pb16[4];
-  const float* pb32[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int blk = j < nb ? wave + 4 * j : 0;
-    const size_t row = (size_t)((blk << 4) + r16) * a.d + kg * 8;
-    pb16[j] = (const uint16_t*)a.E + row;
-    pb32[j] = (const float*)a.E + row;
-  }
-  const int nsteps = a.d >> 5;     // d % 128 == 0 on this path
-
-  RouterFrag<SPLIT_E> f[4];
-  auto load = [&](RouterFrag<SPLIT_E>& g, int step) __attribute__((always_inline)) {
-    const int k = min(step, nsteps - 1) << 5;
-    g.a0 = *(const bf16x8*)(pa0 + k);
-    g.a1 = *(const bf16x8*)(pa1 + k);
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      if (!SPLIT_E) {
-        *(bf16x8*)&g.b[j][0] = *(const bf16x8*)(pb16[j] + k);
-      } else {
-        *(f32x4*)&g.b[j][0] = *(const f32x4*)(pb32[j] + k);
-        *(f32x4*)&g.b[j][1] = *(const f32x4*)(pb32[j] + k + 4);
-      }
-    }
-  };
-
-  double z64[2][4][4];
-#pragma unroll
-  for (int m = 0; m < 2; m++)
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-      for (int r = 0; r < 4; r++) z64[m][j][r] = 0.0;
-  f32x4 acc[2][4], acs[2][4];
-  auto zero_acc = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int m = 0; m < 2; m++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) acc[m][j] = acs[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  };
-  auto flush = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int m = 0; m < 2; m++)
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          z64[m][j][r] += (double)acc[m][j][r];
-          if (SPLIT_E) z64[m][j][r] += (double)acs[m][j][r];
-        }
-  };
-  auto mfma = [&](const RouterFrag<SPLIT_E>& g) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      if (j < nb) {
-        if (!SPLIT_E) {
-          const bf16x8 B = *(const bf16x8*)&g.b[j][0];
-          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a0, B, acc[0][j], 0, 0, 0);
-          acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a1, B, acc[1][j], 0, 0, 0);
-        } else {
-          float x[8];
-          *(f32x4*)&x[0] = *(const f32x4*)&g.b[j][0];
-          *(f32x4*)&x[4] = *(const f32x4*)&g.b[j][1];
-          bf16x8 h, md, lo;
-          split3(x, h, md, lo);
-          acs[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a0, lo, acs[0][j], 0, 0, 0);
-          acs[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a1, lo, acs[1][j], 0, 0, 0);
-          acs[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a0, md, acs[0][j], 0, 0, 0);
-          acs[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a1, md, acs[1][j], 0, 0, 0);
-          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a0, h, acc[0][j], 0, 0, 0);
-          acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a1, h, acc[1][j], 0, 0, 0);
-        }
-      }
-    }
-  };
-
-  load(f[0], 0);
-  load(f[1], 1);
-  load(f[2], 2);
-  for (int s0 = 0; s0 < nsteps; s0 += 4) {      // nsteps % 4 == 0
-    load(f[3], s0 + 3);
-    zero_acc();
-    mfma(f[0]);
-    load(f[0], s0 + 4);
-    mfma(f[1]);
-    load(f[1], s0 + 5);
-    mfma(f[2]);
-    load(f[2], s0 + 6);
-    mfma(f[3]);
-    flush();
-  }
-#pragma unroll
-  for (int m = 0; m < 2; m++)
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-      if (j < nb) {
-        const int e = ((wave + 4 * j) << 4) + r16;
-#pragma unroll
-        for (int r = 0; r < 4; r++) sh.s[m * 16 + 4 * kg + r][e] = (float)sigmoid64(z64[m][j][r]);
-      }
-}
-
 template <bool U_BF16, bool E_BF16>
 __device__ void front_f64(const RouteArgs& a, RouterLds& sh, int t0, int nt) {
   for (int p = threadIdx.x; p < nt * a.n_routed; p += RT_THREADS) {
@@ -367,9 +231,165 @@ __device__ void select_tokens(const RouteArgs& a, RouterLdsT<BT>& sh, int t0, in
   }
 }
 
+// ---------------------------------------------------------------- lane-major selection (N_r = 256)
+// The same selection for 256 experts with lane l holding experts 4l..4l+3, so a
+// group of 32 contiguous experts is 8 adjacent lanes: its top-2 come from a
+// sorting network on each lane's 4 values and three cross-lane merges (DPP), the
+// group ranking from 8 lane reads, and each top-K round is a row-wise DPP max,
+// 4 lane reads and one ballot (the lowest lane, then the lowest of its 4 slots,
+// is the lowest expert index holding the maximum). About 400 instructions per
+// token instead of thousands. Same total orders, same NaN and -0 handling, same
+// fp64 gate sums in selection order as select_tokens.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// maximum over the wave (the same value in every lane)
+__device__ __forceinline__ uint32_t wave_max_lm(uint32_t v) {
+  v = max(v, dpp_u32<DPP_XOR1>(v));
+  v = max(v, dpp_u32<DPP_XOR2>(v));
+  v = max(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
+  v = max(v, dpp_u32<DPP_ROW_MIRROR>(v));                 // each 16-lane row holds its maximum
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+// the two largest of a multiset, merged with another lane's pair
+__device__ __forceinline__ void top2_merge(float& t1, float& t2, float p1, float p2) {
+  const float n1 = fmaxf(t1, p1);
+  t2 = fmaxf(fminf(t1, p1), fmaxf(t2, p2));
+  t1 = n1;
+}
+
+bool route_lm_ok(const RouteArgs& a) {
+  const int S = a.n_groups > 0 ? a.n_routed / a.n_groups : 0;
+  return a.n_routed == RT_NMAX && (a.n_groups == 1 || (S == 32 && a.group_topk <= 2));
+}
+
+// one wave per token; s4: this lane's 4 affinities (experts 4 lane ..), b4: their biases
+__device__ __forceinline__ void select_lane_major(const RouteArgs& a, const float s4[4], const float b4[4], int t) {
+  const int lane = threadIdx.x & 63;
+  const int K = a.top_k, G = a.n_groups, M = a.topk_groups, q = a.group_topk;
+  uint32_t k4[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const float kv = s4[i] + b4[i];
+    k4[i] = kv != kv ? 1u : max(ordered_f32(kv), 1u);     // NaN ranks after every number
+  }
+  if (G > 1) {
+    // each group's q largest (q <= 2) values of s + b (or s), NaN as -inf; fp32 sum, largest first
+    float g[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float v = a.group_score_biased ? s4[i] + b4[i] : s4[i];
+      g[i] = v != v ? -INFINITY : v;
+    }
+    const float h1 = fmaxf(g[0], g[1]), l1 = fminf(g[0], g[1]);
+    const float h2 = fmaxf(g[2], g[3]), l2 = fminf(g[2], g[3]);
+    float t1 = fmaxf(h1, h2), t2 = fmaxf(fminf(h1, h2), fmaxf(l1, l2));
+    top2_merge(t1, t2, dpp_f32<DPP_XOR1>(t1), dpp_f32<DPP_XOR1>(t2));
+    top2_merge(t1, t2, dpp_f32<DPP_XOR2>(t1), dpp_f32<DPP_XOR2>(t2));
+    top2_merge(t1, t2, dpp_f32<DPP_ROW_HALF_MIRROR>(t1), dpp_f32<DPP_ROW_HALF_MIRROR>(t2));
+    const float gs = q >= 2 ? t1 + t2 : t1;
+    const uint32_t mine = max(ordered_f32(gs), 1u);
+    // rank of this lane's group g = lane / 8 among the 8: (score desc, group index asc)
+    const int gi = lane >> 3;
+    int rank = 0;
+#pragma unroll
+    for (int h = 0; h < 8; h++) {
+      const uint32_t o = __builtin_amdgcn_readlane(mine, 8 * h);
+      rank += (o > mine || (o == mine && h < gi)) ? 1 : 0;
+    }
+    if (rank >= M) k4[0] = k4[1] = k4[2] = k4[3] = 0u;
+  }
+  // K rounds: the largest key, then the lowest expert index holding it
+  int my_e = 0;
+  float my_s = 0.f;
+  for (int k = 0; k < K; k++) {
+    const uint32_t lmax = max(max(k4[0], k4[1]), max(k4[2], k4[3]));
+    const uint32_t kmax = wave_max_lm(lmax);
+    const uint64_t hold = __ballot(lmax == kmax);
+    const int L = (int)__builtin_ctzll(hold);
+    int fs = 3;                                             // this lane's lowest slot holding kmax
+    fs = k4[2] == kmax ? 2 : fs;
+    fs = k4[1] == kmax ? 1 : fs;
+    fs = k4[0] == kmax ? 0 : fs;
+    const int slot = __builtin_amdgcn_readlane(fs, L);
+    float sv = s4[0];                                       // selects only: no branch around these
+    sv = slot == 1 ? s4[1] : sv;
+    sv = slot == 2 ? s4[2] : sv;
+    sv = slot == 3 ? s4[3] : sv;
+    const float sel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), L));
+    const bool owner = lane == L;
+#pragma unroll
+    for (int i = 0; i < 4; i++) k4[i] = owner && slot == i ? 0u : k4[i];
+    my_e = lane == k ? 4 * L + slot : my_e;
+    my_s = lane == k ? sel : my_s;
+  }
+  // gate denominator: the selected scores in selection order, summed in fp64
+  double sum = 0.0;
+  for (int k = 0; k < K; k++) sum += (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
+  if (lane < K) {
+    const float gte = sum > 0.0 ? (float)((double)my_s / sum) : 1.0f / (float)K;
+    const size_t o = (size_t)t * K + lane;
+    a.idx[o] = my_e;
+    a.gate[o] = gte;
+  }
+}
+
+// selection of 4 tokens per workgroup (one per wave) from given affinities or from
+// the split-K partial logits
+template <int FRONT>
+__global__ __launch_bounds__(RT_THREADS) void route_lm_kernel(RouteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (RT_THREADS / kWave) + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  float s4[4], b4[4];
+  const f32x4 bv = *(const f32x4*)(a.b + 4 * lane);
+#pragma unroll
+  for (int i = 0; i < 4; i++) b4[i] = bv[i];
+  if constexpr (FRONT == kFrontScoresIn) {
+    const f32x4 v = *(const f32x4*)(a.scores_in + (size_t)t * RT_NMAX + 4 * lane);
+#pragma unroll
+    for (int i = 0; i < 4; i++) s4[i] = v[i];
+  } else {
+    // the S fp32 slice sums, added in fp64 in slice order; 4 slices' loads in flight at a time
+    const size_t slice = (size_t)a.T * RT_NMAX;
+    const float* src = a.partials + (size_t)t * RT_NMAX + 4 * lane;
+    double z[4] = {0.0, 0.0, 0.0, 0.0};
+    int sl = 0;
+    for (; sl + 4 <= a.n_slices; sl += 4) {
+      f32x4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) v[j] = *(const f32x4*)(src + (sl + j) * slice);
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) z[i] += (double)v[j][i];
+    }
+    for (; sl < a.n_slices; sl++) {
+      const f32x4 v = *(const f32x4*)(src + sl * slice);
+#pragma unroll
+      for (int i = 0; i < 4; i++) z[i] += (double)v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) s4[i] = (float)sigmoid64(z[i]);
+  }
+  if (a.scores_out)
+    *(f32x4*)(a.scores_out + (size_t)t * RT_NMAX + 4 * lane) = f32x4{s4[0], s4[1], s4[2], s4[3]};
+  select_lane_major(a, s4, b4, t);
+}
+
 template <int FRONT, bool U_BF16, bool E_BF16, int BT = RT_BT>
 __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
-  static_assert(FRONT == kFrontScoresIn || BT == RT_BT, "the fused front ends work on 32 tokens");
+  static_assert(FRONT == kFrontF64 ? BT == RT_BT : BT == RT_THREADS / kWave,
+                "the fp64 front end works on 32 tokens, the others on one token per wave");
   __shared__ RouterLdsT<BT> sh;
   const int t0 = blockIdx.x * BT;
   const int nt = min(BT, a.T - t0);
@@ -377,14 +397,54 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     sh.b[e] = a.b[e];
   }
   if constexpr (FRONT == kFrontScoresIn) {
-    for (int p = threadIdx.x; p < nt * a.n_routed; p += RT_THREADS) {
-      const int t = p / a.n_routed, e = p - t * a.n_routed;
-      sh.s[t][e] = a.scores_in[(size_t)(t0 + t) * a.n_routed + e];
+    // wave w fills token w's row (one token per wave); every load is issued before any store
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (w < nt) {
+      const float* src = a.scores_in + (size_t)(t0 + w) * a.n_routed;
+      float v[RT_NMAX / 64];
+#pragma unroll
+      for (int j = 0; j < RT_NMAX / 64; j++) {
+        const int e = lane + 64 * j;
+        v[j] = e < a.n_routed ? src[e] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < RT_NMAX / 64; j++)
+        if (lane + 64 * j < a.n_routed) sh.s[w][lane + 64 * j] = v[j];
     }
-  } else if constexpr (FRONT == kFrontMfma) {
-    front_mfma<false>(a, sh, t0);
-  } else if constexpr (FRONT == kFrontMfmaSplitE) {
-    front_mfma<true>(a, sh, t0);
+  } else if constexpr (FRONT == kFrontPartials) {
+    // the split-K logits: S fp32 slice sums per (token, expert), added in fp64 in slice order
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (w < nt) {
+      const size_t slice = (size_t)a.T * a.n_routed;
+      const float* src = a.partials + (size_t)(t0 + w) * a.n_routed;
+      double z[RT_NMAX / 64];
+#pragma unroll
+      for (int j = 0; j < RT_NMAX / 64; j++) z[j] = 0.0;
+      int sl = 0;
+      for (; sl + 4 <= a.n_slices; sl += 4) {          // 4 slices' loads in flight at a time
+        float v[4][RT_NMAX / 64];
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+          for (int j = 0; j < RT_NMAX / 64; j++) {
+            const int e = lane + 64 * j;
+            v[q][j] = e < a.n_routed ? src[(sl + q) * slice + e] : 0.f;
+          }
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+          for (int j = 0; j < RT_NMAX / 64; j++) z[j] += (double)v[q][j];
+      }
+      for (; sl < a.n_slices; sl++)
+#pragma unroll
+        for (int j = 0; j < RT_NMAX / 64; j++) {
+          const int e = lane + 64 * j;
+          z[j] += (double)(e < a.n_routed ? src[sl * slice + e] : 0.f);
+        }
+#pragma unroll
+      for (int j = 0; j < RT_NMAX / 64; j++)
+        if (lane + 64 * j < a.n_routed) sh.s[w][lane + 64 * j] = (float)sigmoid64(z[j]);
+    }
   } else {
     front_f64<U_BF16, E_BF16>(a, sh, t0, nt);
   }
@@ -402,12 +462,10 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
 // For large batches the logits are better tiled over (tokens x experts) than
 // one workgroup per 32 tokens x all experts (which streams the whole centroid
 // matrix through every CU). Phase 1 (logits_kernel) computes the affinities
-// of a 128-token x 64-expert tile and writes them to a scores buffer; phase 2
-// is route_kernel in scores-in mode (the same selection code). Phase 1 does
-// the same arithmetic as front_mfma -- the same 16x16x32 MFMAs on the same
-// operands, fp32 partials over 128-element chunks of d summed in fp64 in chunk
-// order, the split of fp32 centroids into hi/mid/lo bf16 planes, the same
-// sigmoid -- so both routers give bit-identical affinities.
+// of a 128-token x 64-expert tile and writes them to a scores buffer: 16x16x32
+// MFMAs, fp32 partials over 128-element chunks of d summed in fp64 in chunk
+// order, fp32 centroids split into hi/mid/lo bf16 planes. Phase 2 is
+// route_kernel in scores-in mode (the same selection code).
 constexpr int LG_BT = 128;          // tokens per workgroup
 constexpr int LG_BE = 64;           // experts per workgroup
 constexpr int LG_BK = 64;           // bf16 elements per stage row (128 bytes)
@@ -627,6 +685,208 @@ __global__ __launch_bounds__(256, 1) void logits_kernel(const uint16_t* __restri
     }
 }
 
+// ---------------------------------------------------------------- split-K router
+// For N_r = 256 experts with bf16 u and centroids. A workgroup (8 waves) owns
+// 128 tokens x all 256 experts over one slice of d (S slices of d/S elements,
+// each a whole number of 128-element chunks), so each u element is read once
+// and each centroid slice once per 128 tokens. The centroids are first packed
+// (pack_centroids_kernel) into 64-element steps of 256 rows whose 16-byte
+// chunks sit at the LDS slots the MFMA reads want, so every centroid load
+// instruction reads one contiguous kilobyte. Wave (wm, wn) computes tokens
+// 64 wm.. x experts 64 wn.. with v_mfma_f32_32x32x16_bf16 (2 x 2 blocks); its
+// fp32 sums over each 128-element chunk are added into fp64 in chunk order,
+// and the slice's fp64 sum is written once as fp32 to partials[slice][t][e].
+// route_kernel in partials mode adds the S slices in fp64, in slice order.
+constexpr int SK_BT = 128;                 // tokens per workgroup
+constexpr int SK_NE = 256;                 // experts per workgroup (all of them)
+constexpr int SK_BK = 64;                  // elements per stage row (128 bytes)
+constexpr int SK_U_BYTES = SK_BT * SK_BK * 2;                 // 16 KB
+constexpr int SK_STAGE = (SK_BT + SK_NE) * SK_BK * 2;         // 48 KB
+constexpr int SK_STAGES = 3;
+constexpr int SK_U_PER_WAVE = SK_BT / 8 / 8;                  // 1 KB blocks of 8 rows over 8 waves
+constexpr int SK_E_PER_WAVE = SK_NE / 8 / 8;
+constexpr int SK_LOADS = SK_U_PER_WAVE + SK_E_PER_WAVE;
+static_assert(SK_STAGES * SK_STAGE <= 160 * 1024, "LDS budget");
+
+// E [256][d] bf16 -> [d/64 steps][256 rows][8 slots x 16 B], chunk c of row r at slot c ^ (r & 7)
+__global__ void pack_centroids_kernel(const uint16_t* __restrict__ E, uint16_t* __restrict__ out, int d) {
+  const long n = (long)SK_NE * d / 8;     // 16-byte chunks
+  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < n; q += (long)gridDim.x * blockDim.x) {
+    const int slot = (int)(q & 7), r = (int)((q >> 3) & (SK_NE - 1));
+    const long step = q >> 11;
+    const int c = slot ^ (r & 7);
+    *(i32x4*)(out + q * 8) = *(const i32x4*)(E + (size_t)r * d + step * SK_BK + c * 8);
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void logits_splitk_kernel(const uint16_t* __restrict__ u,
+                                                               const uint16_t* __restrict__ epk,
+                                                               float* __restrict__ partials, int T, int d,
+                                                               int n_slices) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int t0 = blockIdx.x * SK_BT, sl = blockIdx.y;
+  const int L = d / n_slices;                  // elements per slice, a multiple of 128
+  const int k_begin = sl * L;
+  const int nk = L / SK_BK;                    // stages, even
+
+  // ---- loads: block i of a stage is 8 rows x 128 bytes; lane l writes row l >> 3, slot l & 7
+  const int brow = lane >> 3;
+  const int bchunk = (lane & 7) ^ brow;        // block rows start at multiples of 8
+  const i32x4 ur = rsrc_words(u, (long)T * d * 2);
+  const i32x4 er = rsrc_words(epk, (long)SK_NE * d * 2);
+  int uoff[SK_U_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < SK_U_PER_WAVE; i++) {
+    const int t = t0 + (wave + 8 * i) * 8 + brow;
+    uoff[i] = t < T ? (t * d + k_begin + bchunk * 8) * 2 : kOutOfRange;
+  }
+  const int ebase = (k_begin / SK_BK) * SK_NE * SK_BK * 2;    // packed steps before this slice
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue_part = [&](auto p_tag, int kt, int buf) __attribute__((always_inline)) {
+    constexpr int P = decltype(p_tag)::value;
+    const uint32_t sb = lds0 + buf * SK_STAGE;
+    if constexpr (P < SK_U_PER_WAVE) {
+      dma_b128(ur, uoff[P], kt * SK_BK * 2, sb + (wave + 8 * P) * 1024);
+    } else {
+      constexpr int Q = P - SK_U_PER_WAVE;
+      dma_b128(er, ebase + (wave + 8 * Q) * 1024 + lane * 16, kt * SK_NE * SK_BK * 2,
+               sb + SK_U_BYTES + (wave + 8 * Q) * 1024);
+    }
+  };
+  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+    static_for<SK_LOADS>([&](auto p) __attribute__((always_inline)) { issue_part(p, kt, buf); });
+  };
+
+  // ---- operand reads: lane l takes row l & 31, 16-byte chunk 2 ks + (l >> 5) of k-substep ks
+  const int l32 = lane & 31, khalf = lane >> 5;
+  int roff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ks++) roff[ks] = l32 * 128 + (((2 * ks + khalf) ^ (l32 & 7)) << 4);
+  const int arow = wm * 64 * 128, brow0 = wn * 64 * 128;
+
+  f32x16 acc[2][2];
+  double z64[2][2][16];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) { acc[i][j][r] = 0.f; z64[i][j][r] = 0.0; }
+
+  // two k-substeps of stage `buf`: their operand reads, then their MFMAs with
+  // loads P0..P1-1 (of step kti into buffer bufi) spread between them
+  auto half = [&](auto h_tag, auto p0_tag, auto p1_tag, int buf, int kti, int bufi) __attribute__((always_inline)) {
+    constexpr int H = decltype(h_tag)::value;
+    constexpr int P0 = decltype(p0_tag)::value, P1 = decltype(p1_tag)::value;
+    const uint8_t* U = lds + buf * SK_STAGE;
+    const uint8_t* Ep = U + SK_U_BYTES;
+    bf16x8 af[2][2], bf[2][2];
+#pragma unroll
+    for (int q = 0; q < 2; q++)
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        af[q][i] = *(const bf16x8*)(U + arow + i * 32 * 128 + roff[H + q]);
+        bf[q][i] = *(const bf16x8*)(Ep + brow0 + i * 32 * 128 + roff[H + q]);
+      }
+    static_for<8>([&](auto m_tag) __attribute__((always_inline)) {
+      constexpr int m = decltype(m_tag)::value;
+      constexpr int q = m / 4, i = (m / 2) & 1, j = m & 1;
+      if constexpr (m % 2 == 0 && P0 + m / 2 < P1) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_part(std::integral_constant<int, P0 + m / 2>{}, kti, bufi);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q][i], bf[q][j], acc[i][j], 0, 0, 0);
+    });
+  };
+  auto fold = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          z64[i][j][r] += (double)acc[i][j][r];
+          acc[i][j][r] = 0.f;
+        }
+  };
+
+  // ring of SK_STAGES buffers, as in the grouped GEMM: wait for this wave's loads of
+  // step kt, barrier, multiply stage kt while refilling the buffer of step kt-1 with
+  // step kt+STAGES-1 (past the last step: re-reads of it, never used)
+  constexpr int S = SK_STAGES;
+#pragma unroll
+  for (int p = 0; p < S - 1; p++) issue(min(p, nk - 1), p);
+  for (int kt = 0; kt < nk; kt++) {
+    wait_vmcnt<(S - 2) * SK_LOADS>();
+    __syncthreads();
+    const int kti = min(kt + S - 1, nk - 1), bufi = (kt + S - 1) % S;
+    half(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+         std::integral_constant<int, SK_LOADS / 2>{}, kt % S, kti, bufi);
+    half(std::integral_constant<int, 2>{}, std::integral_constant<int, SK_LOADS / 2>{},
+         std::integral_constant<int, SK_LOADS>{}, kt % S, kti, bufi);
+    if (kt & 1) fold();                        // a 128-element chunk ends every second stage
+  }
+  wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
+
+  // D element (8*(r>>2) + 4*(lane>>5) + (r&3), lane&31) of each 32x32 block
+  float* out = partials + (size_t)sl * T * SK_NE;
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int t = t0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+      if (t < T) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) out[(size_t)t * SK_NE + wn * 64 + j * 32 + l32] = (float)z64[i][j][r];
+      }
+    }
+}
+
+// slices of d (each a whole number of 128-element chunks) so that the grid has
+// enough workgroups to fill the chip
+static int splitk_slices(int T, int d) {
+  const int tiles = (T + SK_BT - 1) / SK_BT, chunks = d / 128;
+  int best = chunks;
+  for (int sdiv = 1; sdiv <= chunks; sdiv++)
+    if (chunks % sdiv == 0 && (long)tiles * sdiv >= 224) { best = sdiv; break; }
+  return best;
+}
+
+bool route_splitk_ok(const RouteArgs& a) {
+  return a.in_dtype == MOE_BF16 && a.router_dtype == MOE_BF16 && a.n_routed == SK_NE && a.d % 128 == 0 &&
+         a.T > 0;
+}
+
+size_t route_splitk_bytes(int T, int d) {
+  const size_t pk = (((size_t)SK_NE * d * 2) + 255) / 256 * 256;
+  return pk + (size_t)splitk_slices(T, d) * T * SK_NE * 4;
+}
+
+hipError_t launch_route_splitk(const RouteArgs& a, void* scratch, hipStream_t s) {
+  uint16_t* epk = (uint16_t*)scratch;
+  const size_t pk = (((size_t)SK_NE * a.d * 2) + 255) / 256 * 256;
+  float* partials = (float*)((uint8_t*)scratch + pk);
+  const int S = splitk_slices(a.T, a.d);
+  const long chunks = (long)SK_NE * a.d / 8;
+  pack_centroids_kernel<<<(int)std::min<long>(cdiv<long>(chunks, 256), 2048), 256, 0, s>>>(
+      (const uint16_t*)a.E, epk, a.d);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  auto k = logits_splitk_kernel;
+  if ((e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               SK_STAGES * SK_STAGE)) != hipSuccess) return e;
+  k<<<dim3(cdiv(a.T, SK_BT), S), 512, SK_STAGES * SK_STAGE, s>>>((const uint16_t*)a.u, epk, partials, a.T, a.d, S);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  RouteArgs b = a;
+  b.partials = partials;
+  b.n_slices = S;
+  return launch_route(b, kFrontPartials, s);
+}
+
 bool route_two_phase_ok(const RouteArgs& a) {
   return a.in_dtype == MOE_BF16 && (a.router_dtype == MOE_BF16 || a.router_dtype == MOE_F32) &&
          a.n_routed % LG_BE == 0 && a.d % 128 == 0 && a.T > 0;
@@ -665,7 +925,6 @@ hipError_t launch_route_two_phase(const RouteArgs& a, void* scratch, hipStream_t
   if ((e = hipGetLastError()) != hipSuccess) return e;
   RouteArgs b = a;
   b.scores_in = scores;
-  b.scores_out = nullptr;
   return launch_route(b, kFrontScoresIn, s);
 }
 
@@ -716,10 +975,17 @@ hipError_t launch_route(const RouteArgs& a, int front, hipStream_t s) {
   switch (front) {
     case kFrontScoresIn:
       // selection only: 4 tokens per workgroup (one per wave) for more waves in flight
-      route_kernel<kFrontScoresIn, false, false, RT_BT_SEL><<<dim3(cdiv(a.T, RT_BT_SEL)), RT_THREADS, 0, s>>>(a);
+      if (route_lm_ok(a))
+        route_lm_kernel<kFrontScoresIn><<<dim3(cdiv(a.T, RT_BT_SEL)), RT_THREADS, 0, s>>>(a);
+      else
+        route_kernel<kFrontScoresIn, false, false, RT_BT_SEL><<<dim3(cdiv(a.T, RT_BT_SEL)), RT_THREADS, 0, s>>>(a);
       break;
-    case kFrontMfma: route_kernel<kFrontMfma, true, true><<<grid, RT_THREADS, 0, s>>>(a); break;
-    case kFrontMfmaSplitE: route_kernel<kFrontMfmaSplitE, true, false><<<grid, RT_THREADS, 0, s>>>(a); break;
+    case kFrontPartials:
+      if (route_lm_ok(a))
+        route_lm_kernel<kFrontPartials><<<dim3(cdiv(a.T, RT_BT_SEL)), RT_THREADS, 0, s>>>(a);
+      else
+        route_kernel<kFrontPartials, false, false, RT_BT_SEL><<<dim3(cdiv(a.T, RT_BT_SEL)), RT_THREADS, 0, s>>>(a);
+      break;
     default: {
       // fp64 VALU logits, any dtype combination
       const bool eb = a.router_dtype == MOE_BF16;
@@ -732,6 +998,20 @@ hipError_t launch_route(const RouteArgs& a, int front, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.counts) return e;
   return launch_count_loads(a.idx, (long)a.T * a.top_k, a.n_routed, a.counts, s);
+}
+
+// ---------------------------------------------------------------- one router for every entry point
+size_t router_scratch_bytes(const RouteArgs& a) {
+  if (route_splitk_ok(a)) return route_splitk_bytes(a.T, a.d);
+  if (route_two_phase_ok(a)) return route_two_phase_bytes(a.T, a.n_routed, a.d, a.router_dtype);
+  return 0;
+}
+
+hipError_t run_router(const RouteArgs& a, void* scratch, hipStream_t s) {
+  if (a.scores_in) return launch_route(a, kFrontScoresIn, s);
+  if (route_splitk_ok(a)) return launch_route_splitk(a, scratch, s);
+  if (route_two_phase_ok(a)) return launch_route_two_phase(a, scratch, s);
+  return launch_route(a, kFrontF64, s);
 }
 
 }  // namespace moe

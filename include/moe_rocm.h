@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* status codes */
 #define MOE_OK          0
@@ -134,10 +134,17 @@ size_t moe_workspace_bytes(const moe_desc_t* desc);
  *   topk_idx [T,K] int32: selected experts in rank order (key desc, index asc).
  *   topk_gate [T,K] fp32: s / sum(s) over the selected experts (unbiased s;
  *     1/K if the sum is 0).
- *   counts [N_r] int32: overwritten with the number of tokens per expert. */
+ *   counts [N_r] int32: overwritten with the number of tokens per expert.
+ *   ws: scratch of moe_route_workspace_bytes(desc) bytes (the router's
+ *     partial logits and packed centroids); nullable when that is 0 or with
+ *     scores_in. MOE_EWORKSPACE when it is missing or smaller.
+ * moe_forward and moe_backward route with the same kernels, so their
+ * selections equal this call's bit for bit. */
+size_t moe_route_workspace_bytes(const moe_desc_t* desc);
 int moe_route(const moe_desc_t* desc, const void* u, const void* E, const float* b,
               const float* scores_in, float* scores_out, int32_t* topk_idx,
-              float* topk_gate, int32_t* counts, moe_stream_t stream);
+              float* topk_gate, int32_t* counts, void* ws, size_t ws_bytes,
+              moe_stream_t stream);
 
 /* Dispatch layout (single-GPU analog of the pwwt.cn note's section 4
  * dispatch; no capacity, note 1.4).

@@ -22,14 +22,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = L.header_symbols()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     raw = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_strerror(lib):
-    assert lib.moe_abi_version() == L.ABI_VERSION == 2
+    assert lib.moe_abi_version() == L.ABI_VERSION == 3
     for st in (0, -1, -2, -3, -4):
         assert lib.moe_strerror(st)
     assert b"unknown" in lib.moe_strerror(7)
@@ -83,7 +83,7 @@ def test_descriptor_rules(lib, kw, want):
 
 def test_bad_abi_version(lib):
     d = _v3()
-    for v in (1, 3):
+    for v in (1, 2, 4):
         d.abi_version = v
         assert M.moe_validate(d) == M.MOE_EINVAL
     assert lib.moe_validate(None) == M.MOE_EINVAL
@@ -95,7 +95,9 @@ MIS = 0x10004
 
 def test_route_argument_errors(lib):
     d = _v3()
-    r = lambda *a: lib.moe_route(ctypes.byref(d), *a, None)
+    need = lib.moe_route_workspace_bytes(ctypes.byref(d))
+    assert need > 0                            # the V3 shape takes the split-K router
+    r = lambda *a: lib.moe_route(ctypes.byref(d), *a, A, need, None)
     # neither source, both sources
     assert r(None, None, A, None, None, A, A, A) == M.MOE_EINVAL
     assert r(A, A, A, A, None, A, A, A) == M.MOE_EINVAL
@@ -104,6 +106,11 @@ def test_route_argument_errors(lib):
     assert r(A, A, A, None, None, None, A, A) == M.MOE_EINVAL
     assert r(MIS, A, A, None, None, A, A, A) == M.MOE_EINVAL
     assert r(A, A, A, None, MIS, A, A, A) == M.MOE_EINVAL
+    # the router's scratch: missing or short -> MOE_EWORKSPACE; not needed with scores_in
+    rw = lambda ws, n, *a: lib.moe_route(ctypes.byref(d), *a, ws, n, None)
+    assert rw(None, 0, A, A, A, None, None, A, A, A) == M.MOE_EWORKSPACE
+    assert rw(A, need - 1, A, A, A, None, None, A, A, A) == M.MOE_EWORKSPACE
+    assert rw(MIS, need, A, A, A, None, None, A, A, A) == M.MOE_EINVAL
 
 
 def test_permute_workspace_and_pointer_errors(lib):

@@ -228,9 +228,10 @@ def test_bias_trajectory_200_steps_scores_in():
 
 
 @pytest.mark.parametrize("name,T", [("v3", None), ("fp8", 1000), ("mid", 4095), ("skew", 2048)])
-def test_two_phase_router_matches_fused(name, T):
-    """moe_forward routes large batches with the tiled two-phase router; its topk_idx, gates and
-    loads must equal moe_route's fused single-kernel router bit for bit (same arithmetic)."""
+def test_forward_routing_matches_moe_route(name, T):
+    """moe_forward's topk_idx, gates and loads equal moe_route's bit for bit on the same inputs
+    (both run the same router: split-K logits at the V3 shape, the tiled two-phase logits for
+    fp32 centroids and for 64 experts)."""
     from tests.test_gpu_forward import layer_for
     cfg = get_config(name)
     if T is not None:
@@ -249,4 +250,4 @@ def test_two_phase_router_matches_fused(name, T):
     assert np.array_equal(host(layer.idx), host(idx))
     assert np.array_equal(host(layer.gate).view(np.uint32), host(gate).view(np.uint32))
     assert np.array_equal(host(layer.counts), host(counts))
-    log(name, "T=%d two-phase routing == fused routing" % cfg.T)
+    log(name, "T=%d forward routing == moe_route" % cfg.T)
