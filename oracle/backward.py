@@ -176,3 +176,19 @@ def layer_grads_fp8(u64, e64, idx, dout64, w13q, w2q, w13sq=(), w2sq=(), experts
         "dw13": {e: W13[e].grad.numpy() for e in want}, "dw2": {e: W2[e].grad.numpy() for e in want},
         "dw13s": [w.grad.numpy() for w in W13s], "dw2s": [w.grad.numpy() for w in W2s],
     }
+
+
+def expert_weight_grads_fp8(u_rows64, gate_rows64, dout_rows64, w13q, w2q, quantise=True):
+    """expert_weight_grads for one routed expert of the FP8 layer: the rows that chose it
+    (u [n, d], in token order, the order its 128-row Wgrad tiles follow), their gates and
+    upstream gradients, and its E4M3 weights (fp64 values). Equal to layer_grads_fp8's
+    dw13[e], dw2[e] (pinned against it) without the other experts."""
+    ident = (lambda a: np.asarray(a, np.float64))
+    qr, qc = (q_rows, q_cols) if quantise else (ident, ident)
+    u = torch.tensor(u_rows64, dtype=torch.float64)
+    W13 = torch.tensor(w13q, dtype=torch.float64, requires_grad=True)
+    W2 = torch.tensor(w2q, dtype=torch.float64, requires_grad=True)
+    g = torch.tensor(np.asarray(gate_rows64, dtype=np.float64))[:, None]
+    out = g * _swiglu_fp8(u, W13, W2, qr, qc)
+    (out * torch.tensor(dout_rows64, dtype=torch.float64)).sum().backward()
+    return W13.grad.numpy(), W2.grad.numpy()

@@ -181,3 +181,24 @@ def test_fp8_linear_matches_independent_recipe():
                           ("wgrad_tiles_unaligned", wt.grad.numpy(), 2)):
         bad = _fp8_linear_ref(x, w, dy, mutation=mut)[idx]
         assert rel(got, bad) > 1e-3, mut
+
+
+def test_fp8_expert_weight_grads_match_the_layer():
+    """expert_weight_grads_fp8 on one expert's rows (token order) and gates equals that
+    expert's gradients from layer_grads_fp8, whose Wgrad tiles start at the same row."""
+    u, E, idx, w13, w2, w13s, w2s, dout = _problem(8, T=300, d=256, N=3, K=2, inter=128)   # ~200 rows each
+    ref = backward.layer_grads_fp8(u, E, idx, dout, w13, w2, w13s, w2s)
+    s = routing.sigmoid(routing.logits(u, E))
+    sel = np.take_along_axis(s, idx, 1)
+    g = sel / sel.sum(axis=1, keepdims=True)
+    for e in range(3):
+        rows, ks = np.nonzero(idx == e)
+        assert len(rows) > 0
+        d13, d2 = backward.expert_weight_grads_fp8(u[rows], g[rows, ks], dout[rows], w13[e], w2[e])
+        assert np.allclose(d13, ref["dw13"][e], rtol=1e-10, atol=1e-12), e
+        assert np.allclose(d2, ref["dw2"][e], rtol=1e-10, atol=1e-12), e
+    # quantise=False is the exact per-expert gradient
+    rows, ks = np.nonzero(idx == 0)
+    a = backward.expert_weight_grads(u[rows], g[rows, ks], dout[rows], w13[0], w2[0])
+    b = backward.expert_weight_grads_fp8(u[rows], g[rows, ks], dout[rows], w13[0], w2[0], quantise=False)
+    assert np.allclose(a[0], b[0], rtol=1e-12, atol=1e-14) and np.allclose(a[1], b[1], rtol=1e-12, atol=1e-14)
