@@ -115,38 +115,52 @@ def q_cols(x):
 
 
 class _Fp8Linear(torch.autograd.Function):
-    """y = Qr(x) W^T for W on the E4M3 grid; backward as the FP8 Dgrad
-    dx = Qr(dy) W and Wgrad dW = Qc(dy)^T Qc(x)."""
+    """y = st(Qr(st(x)) W^T) for W on the E4M3 grid; backward as the FP8 Dgrad
+    dx = st(Qr(st(dy)) W) and Wgrad dW = Qc(st(dy))^T Qc(st(x)). st is the storage
+    rounding of the tensors around the GEMMs (the identity, or bf16); the rounding
+    passes gradients straight through, like the quantisers."""
 
     @staticmethod
-    def forward(ctx, x, w, qr, qc):
-        ctx.save_for_backward(x, w)
-        ctx.qr, ctx.qc = qr, qc
-        return torch.from_numpy(qr(x.detach().numpy())) @ w.T
+    def forward(ctx, x, w, qr, qc, st):
+        xs = torch.from_numpy(st(x.detach().numpy()))
+        ctx.save_for_backward(xs, w)
+        ctx.qr, ctx.qc, ctx.st = qr, qc, st
+        return torch.from_numpy(st((torch.from_numpy(qr(xs.numpy())) @ w.T).detach().numpy()))
 
     @staticmethod
     def backward(ctx, dy):
-        x, w = ctx.saved_tensors
-        dyn, xn = dy.detach().numpy(), x.detach().numpy()
-        dx = torch.from_numpy(ctx.qr(dyn)) @ w
+        xs, w = ctx.saved_tensors
+        dyn, xn = ctx.st(dy.detach().numpy()), xs.detach().numpy()
+        dx = torch.from_numpy(ctx.st((torch.from_numpy(ctx.qr(dyn)) @ w).numpy()))
         dw = torch.from_numpy(ctx.qc(dyn)).T @ torch.from_numpy(ctx.qc(xn))
-        return dx, dw, None, None
+        return dx, dw, None, None, None
 
 
-def _swiglu_fp8(x, w13, w2, qr, qc):
+def _swiglu_fp8(x, w13, w2, qr, qc, st):
     inter = w13.shape[0] // 2
-    ab = _Fp8Linear.apply(x, w13, qr, qc)
+    ab = _Fp8Linear.apply(x, w13, qr, qc, st)
     a, v = ab[:, :inter], ab[:, inter:]
-    return _Fp8Linear.apply(a * torch.sigmoid(a) * v, w2, qr, qc)
+    return _Fp8Linear.apply(a * torch.sigmoid(a) * v, w2, qr, qc, st)
 
 
-def layer_grads_fp8(u64, e64, idx, dout64, w13q, w2q, w13sq=(), w2sq=(), experts=None, quantise=True):
+def _rules(quantise, store):
+    ident = (lambda a: np.asarray(a, np.float64))
+    qr, qc = (q_rows, q_cols) if quantise else (ident, ident)
+    if store not in (None, "bf16"):
+        raise ValueError("store must be None or 'bf16'")
+    return qr, qc, (nx.bf16_round_f64 if store == "bf16" else ident)
+
+
+def layer_grads_fp8(u64, e64, idx, dout64, w13q, w2q, w13sq=(), w2sq=(), experts=None, quantise=True,
+                    store=None):
     """layer_grads for the FP8 layer: w13q / w2q (mappings expert -> fp64 arrays)
     and w13sq / w2sq are the E4M3 weights (ffn.fp8_weights of the masters); each
     expert's rows go through the FP8 GEMMs above. quantise=False replaces every
-    quantiser by the identity, which must give layer_grads on the same weights."""
-    ident = (lambda a: np.asarray(a, np.float64))
-    qr, qc = (q_rows, q_cols) if quantise else (ident, ident)
+    quantiser by the identity, which must give layer_grads on the same weights.
+    store="bf16" rounds to bf16 every tensor a GEMM reads before quantising it and
+    every Fprop and Dgrad output (the pages' GEMMs take FP8 inputs and give BF16 or
+    FP32 results: pwwt.cn note section 3); None keeps them in fp64."""
+    qr, qc, st = _rules(quantise, store)
     u = torch.tensor(u64, dtype=torch.float64, requires_grad=True)
     E = torch.tensor(e64, dtype=torch.float64, requires_grad=True)
     idx_t = torch.tensor(np.asarray(idx), dtype=torch.long)
@@ -162,12 +176,12 @@ def layer_grads_fp8(u64, e64, idx, dout64, w13q, w2q, w13sq=(), w2sq=(), experts
     g = sel / sel.sum(dim=1, keepdim=True)
     out = u
     for a, b in zip(W13s, W2s):
-        out = out + _swiglu_fp8(u, a, b, qr, qc)
+        out = out + _swiglu_fp8(u, a, b, qr, qc, st)
     routed = torch.zeros_like(u)
     for e in used:
         rows, ks = np.nonzero(np.asarray(idx) == e)     # rows in token order
         rows_t, ks_t = torch.tensor(rows), torch.tensor(ks)
-        y = _swiglu_fp8(u[rows_t], W13[e], W2[e], qr, qc)
+        y = _swiglu_fp8(u[rows_t], W13[e], W2[e], qr, qc, st)
         routed = routed.index_add(0, rows_t, g[rows_t, ks_t][:, None] * y)
     out = out + routed
     (out * torch.tensor(dout64, dtype=torch.float64)).sum().backward()
@@ -178,17 +192,17 @@ def layer_grads_fp8(u64, e64, idx, dout64, w13q, w2q, w13sq=(), w2sq=(), experts
     }
 
 
-def expert_weight_grads_fp8(u_rows64, gate_rows64, dout_rows64, w13q, w2q, quantise=True):
+def expert_weight_grads_fp8(u_rows64, gate_rows64, dout_rows64, w13q, w2q, quantise=True, store=None):
     """expert_weight_grads for one routed expert of the FP8 layer: the rows that chose it
     (u [n, d], in token order, the order its 128-row Wgrad tiles follow), their gates and
     upstream gradients, and its E4M3 weights (fp64 values). Equal to layer_grads_fp8's
-    dw13[e], dw2[e] (pinned against it) without the other experts."""
-    ident = (lambda a: np.asarray(a, np.float64))
-    qr, qc = (q_rows, q_cols) if quantise else (ident, ident)
+    dw13[e], dw2[e] (pinned against it) without the other experts; quantise and store as
+    there."""
+    qr, qc, st = _rules(quantise, store)
     u = torch.tensor(u_rows64, dtype=torch.float64)
     W13 = torch.tensor(w13q, dtype=torch.float64, requires_grad=True)
     W2 = torch.tensor(w2q, dtype=torch.float64, requires_grad=True)
     g = torch.tensor(np.asarray(gate_rows64, dtype=np.float64))[:, None]
-    out = g * _swiglu_fp8(u, W13, W2, qr, qc)
+    out = g * _swiglu_fp8(u, W13, W2, qr, qc, st)
     (out * torch.tensor(dout_rows64, dtype=torch.float64)).sum().backward()
     return W13.grad.numpy(), W2.grad.numpy()

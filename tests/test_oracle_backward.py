@@ -138,7 +138,14 @@ def _q_torch(x, tr, tc):
     return (q.to(torch.float64) * sc.to(torch.float64)).reshape(R, C).numpy()
 
 
-def _fp8_linear_ref(x, w, dy, mutation=None):
+def _bf16_torch(a):
+    import torch
+    return torch.from_numpy(np.asarray(a, np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _fp8_linear_ref(x, w, dy, mutation=None, store=False):
+    st = _bf16_torch if store else (lambda a: a)
+    x, dy = st(x), st(dy)
     n = x.shape[0]
     pad = (-n) % 128
     if mutation == "wgrad_tiles_unaligned":
@@ -147,8 +154,8 @@ def _fp8_linear_ref(x, w, dy, mutation=None):
         pad_front = 0
     padr = lambda a: np.concatenate([np.zeros((pad_front, a.shape[1])), a,
                                      np.zeros(((-(n + pad_front)) % 128, a.shape[1]))], axis=0)
-    y = _q_torch(x, 1, 128) @ w.T
-    dx = (dy if mutation == "dgrad_unquantised" else _q_torch(dy, 1, 128)) @ w
+    y = st(_q_torch(x, 1, 128) @ w.T)
+    dx = st((dy if mutation == "dgrad_unquantised" else _q_torch(dy, 1, 128)) @ w)
     if mutation == "wgrad_tiles_along_columns":
         dw = _q_torch(dy, 1, 128).T @ _q_torch(x, 1, 128)
     else:
@@ -167,7 +174,7 @@ def test_fp8_linear_matches_independent_recipe():
     w = _q_torch(rng.standard_normal((m, k)) / 16, 128, 128)      # weights on the E4M3 grid
     xt = torch.tensor(x, requires_grad=True)
     wt = torch.tensor(w, requires_grad=True)
-    y = backward._Fp8Linear.apply(xt, wt, backward.q_rows, backward.q_cols)
+    y = backward._Fp8Linear.apply(xt, wt, backward.q_rows, backward.q_cols, lambda a: np.asarray(a, np.float64))
     y.backward(torch.from_numpy(dy))
     y_ref, dx_ref, dw_ref = _fp8_linear_ref(x, w, dy)
     rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)
@@ -202,3 +209,49 @@ def test_fp8_expert_weight_grads_match_the_layer():
     a = backward.expert_weight_grads(u[rows], g[rows, ks], dout[rows], w13[0], w2[0])
     b = backward.expert_weight_grads_fp8(u[rows], g[rows, ks], dout[rows], w13[0], w2[0], quantise=False)
     assert np.allclose(a[0], b[0], rtol=1e-12, atol=1e-14) and np.allclose(a[1], b[1], rtol=1e-12, atol=1e-14)
+
+
+def test_fp8_linear_bf16_storage_matches_independent_recipe():
+    """store="bf16": the GEMM inputs are bf16 tensors (rounded before quantising) and the Fprop
+    and Dgrad outputs are rounded to bf16; compared with torch's own bf16 cast around the same
+    float8 recipe, and far from the fp64-storage gradients on inputs that are not on the bf16 grid."""
+    import torch
+    rng = np.random.default_rng(22)
+    n, k, m = 200, 256, 256
+    x = rng.standard_normal((n, k)) * (2.0 ** (np.arange(n) % 9 - 4))[:, None]
+    dy = rng.standard_normal((n, m))
+    w = _q_torch(rng.standard_normal((m, k)) / 16, 128, 128)
+    _, _, st = backward._rules(True, "bf16")
+    xt = torch.tensor(x, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    y = backward._Fp8Linear.apply(xt, wt, backward.q_rows, backward.q_cols, st)
+    y.backward(torch.from_numpy(dy))
+    y_ref, dx_ref, dw_ref = _fp8_linear_ref(x, w, dy, store=True)
+    rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)
+    # torch casts fp64 to bf16 through fp32; the oracle rounds fp64 to bf16 directly. They
+    # differ only where the fp32 value is an exact bf16 tie that the fp64 value was not.
+    xb, dyb = _bf16_torch(x), _bf16_torch(dy)
+    for got, ref, pre in ((y.detach().numpy(), y_ref, _q_torch(xb, 1, 128) @ w.T),
+                          (xt.grad.numpy(), dx_ref, _q_torch(dyb, 1, 128) @ w)):
+        diff = got != ref
+        f32 = pre[diff].astype(np.float32)
+        assert diff.sum() <= 1e-3 * diff.size
+        assert ((f32.view(np.uint32) & 0xFFFF) == 0x8000).all() and (f32 != pre[diff]).all()
+    assert rel(wt.grad.numpy(), dw_ref) < 1e-12
+    _, dx64, dw64 = _fp8_linear_ref(x, w, dy)
+    assert rel(xt.grad.numpy(), dx64) > 1e-3 and rel(wt.grad.numpy(), dw64) > 1e-3
+    # bf16 values are left as they are
+    v = _bf16_torch(rng.standard_normal(1000))
+    assert np.array_equal(st(v), v)
+
+
+def test_fp8_layer_bf16_storage_without_quantisers_is_near_the_exact_backward():
+    """With the quantisers off, bf16 storage only adds bf16 rounding: the gradients stay within a
+    few bf16 units of layer_grads, and the structure is unchanged."""
+    u, E, idx, w13, w2, w13s, w2s, dout = _problem(9, T=9, d=256, inter=128)
+    a = backward.layer_grads(u, E, idx, dout, w13, w2, w13s, w2s)
+    b = backward.layer_grads_fp8(u, E, idx, dout, w13, w2, w13s, w2s, quantise=False, store="bf16")
+    rel = lambda p, q: np.linalg.norm(p - q) / np.linalg.norm(q)
+    assert 1e-5 < rel(b["du"], a["du"]) < 1e-2
+    for e in a["dw13"]:
+        assert rel(b["dw13"][e], a["dw13"][e]) < 1e-2 and rel(b["dw2"][e], a["dw2"][e]) < 1e-2
