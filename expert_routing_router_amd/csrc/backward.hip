@@ -360,8 +360,8 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a) {
 // tile's loads and MFMAs run.
 constexpr int WT_PAD = 64;
 
-// kofs[e] = sum over e' < e of roundup(n_e', 64); kofs[n_seg] = padded total
-__global__ __launch_bounds__(64) void wg_kofs_kernel(const int32_t* __restrict__ offsets, int n_seg,
+// kofs[e] = sum over e' < e of roundup(n_e', pad); kofs[n_seg] = padded total
+__global__ __launch_bounds__(64) void wg_kofs_kernel(const int32_t* __restrict__ offsets, int n_seg, int pad,
                                                      int32_t* __restrict__ kofs) {
   __shared__ int32_t so[512];
   for (int i = threadIdx.x; i <= n_seg; i += 64) so[i] = offsets[i];
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(64) void wg_kofs_kernel(const int32_t* __restrict__
     int acc = 0;
     for (int e = 0; e < n_seg; e++) {
       kofs[e] = acc;
-      acc += (so[e + 1] - so[e] + WT_PAD - 1) / WT_PAD * WT_PAD;
+      acc += (so[e + 1] - so[e] + pad - 1) / pad * pad;
     }
     kofs[n_seg] = acc;
   }
@@ -534,11 +534,170 @@ __global__ __launch_bounds__(512, 1) void wgrad_dma_kernel(WgradDmaArgs a) {
   }
 }
 
-long wgrad_pitch(long rows, int n_seg) { return (rows + (long)WT_PAD * n_seg + WT_PAD - 1) / WT_PAD * WT_PAD; }
+// ---------------------------------------------------------------- FP8 weight gradients
+// C_e = PT_e QT_e^T over segment e's rows with E4M3 operands (the pages' Wgrad in
+// FP8): PT [M][pitch] and QT [Nn][pitch] hold each segment's transposed rows
+// padded with zeros to a multiple of 128 (kofs, from wg_kofs_kernel with pad
+// 128), quantised in 1x128 tiles along pitch, i.e. 128-row tiles of the
+// original rows aligned at the segment's first row; their fp32 scales are stored
+// transposed, SPT [pitch/128][M] and SQT [pitch/128][Nn], so a stage's 256
+// scales are one contiguous kilobyte. 256x256 tiles, 8 waves (each 128x64 as
+// 4x2 blocks of 32x32), K = 128 per stage (one scale tile) in a two-stage ring
+// of LDS-DMA loads; per block and stage two v_mfma_scale_f32_32x32x64_f8f6f4
+// make a fresh fp32 partial p, folded as acc += p * s_P[row] * s_Q[col].
+// Persistent over super-tiles as wgrad_dma_kernel; no atomics, deterministic.
+struct WgF8 {
+  static constexpr int THREADS = 512, BM = 256, BN = 256, BK = 128;
+  static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, S_BYTES = 1024;
+  static constexpr int STAGE = A_BYTES + B_BYTES + 2 * S_BYTES, BYTES = 2 * STAGE;
+  static constexpr int PER_OP = BM / 8 / 8;           // 1 KB blocks of 8 rows per operand per wave
+  static constexpr int GRID = 256;
+  static constexpr int SUPER = GRID / 8;
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+struct WgradF8Args {
+  const uint8_t* PT; const uint8_t* QT; const float* SPT; const float* SQT; long pitch; const int32_t* kofs;
+  int n_seg, M, Nn, sm, sn;
+  float* out0; float* out1; long ostride0, ostride1; int n_first;
+};
+
+__global__ __launch_bounds__(512, 1) void wgrad_f8_kernel(WgradF8Args a) {
+  using C = WgF8;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int MT = a.M / C::BM, NT = a.Nn / C::BN;
+  const int smt = (MT + a.sm - 1) / a.sm, snt = (NT + a.sn - 1) / a.sn;
+  const int per_seg = smt * snt, n_super = a.n_seg * per_seg;
+  const uint32_t lds0 = lds_addr(lds);
+  // block b of a stage holds rows 8b..8b+7; lane l writes row l >> 3, slot l & 7 and fetches
+  // chunk slot ^ ((row >> 1) & 7): blocks b = wave + 8i share b's parity with the wave
+  const int brow = lane >> 3;
+  const int bchunk = (lane & 7) ^ ((((wave & 1) << 2) + (lane >> 4)) & 7);
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int sw = (l32 >> 1) & 7;
+  int roff[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; h++)
+#pragma unroll
+    for (int c = 0; c < 2; c++) roff[h][c] = l32 * 128 + (((h * 4 + khalf * 2 + c) ^ sw) << 4);
+  const long kb_total = a.pitch / C::BK;
+  const i32x4 pr = rsrc_words(a.PT, (long)a.M * a.pitch);
+  const i32x4 qr = rsrc_words(a.QT, (long)a.Nn * a.pitch);
+  const i32x4 spr = rsrc_words(a.SPT, kb_total * a.M * 4);
+  const i32x4 sqr = rsrc_words(a.SQT, kb_total * a.Nn * 4);
+
+  for (int sidx = 0;; sidx++) {
+    const int st = xcd + 8 * sidx;
+    if (st >= n_super) break;
+    const int seg = st / per_seg, srem = st - seg * per_seg;
+    const int mt = (srem / snt) * a.sm + q / a.sn, nt = (srem % snt) * a.sn + q % a.sn;
+    if (mt >= MT || nt >= NT) continue;
+    const int k0 = a.kofs[seg];
+    const int nkb = (a.kofs[seg + 1] - k0) / C::BK;
+    int aoff[C::PER_OP], boff[C::PER_OP];
+#pragma unroll
+    for (int i = 0; i < C::PER_OP; i++) {
+      const int r = (wave + 8 * i) * 8 + brow;
+      aoff[i] = (int)((long)(mt * C::BM + r) * a.pitch + k0 + bchunk * 16);
+      boff[i] = (int)((long)(nt * C::BN + r) * a.pitch + k0 + bchunk * 16);
+    }
+    const int soff = (int)(((long)(k0 / C::BK) * (wave == 0 ? a.M : a.Nn) + (wave == 0 ? mt * C::BM : nt * C::BN)) * 4
+                           + lane * 16);
+    auto issue = [&](int kb, int buf) __attribute__((always_inline)) {
+      const uint32_t sbase = lds0 + buf * C::STAGE;
+#pragma unroll
+      for (int i = 0; i < C::PER_OP; i++) dma_b128(pr, aoff[i], kb * C::BK, sbase + (wave + 8 * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < C::PER_OP; i++)
+        dma_b128(qr, boff[i], kb * C::BK, sbase + C::A_BYTES + (wave + 8 * i) * 1024);
+      // the stage's 256 row scales of each operand: one kilobyte each
+      if (wave == 0) dma_b128(spr, soff, kb * a.M * 4, sbase + C::A_BYTES + C::B_BYTES);
+      if (wave == 1) dma_b128(sqr, soff, kb * a.Nn * 4, sbase + C::A_BYTES + C::B_BYTES + C::S_BYTES);
+    };
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+    __syncthreads();   // every wave is done reading the previous tile's stages
+    if (nkb > 0) {
+      issue(0, 0);
+      for (int kb = 0; kb < nkb; kb++) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        issue(min(kb + 1, nkb - 1), (kb + 1) & 1);
+        const uint8_t* A = lds + (kb & 1) * C::STAGE;
+        const uint8_t* B = A + C::A_BYTES;
+        const float* SA = (const float*)(B + C::B_BYTES);
+        const float* SB = SA + C::S_BYTES / 4;
+        i32x8 bfr[2][2];
+        float sb[2];
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+          const int brow0 = wn * 64 + j * 32;
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+            const i32x4 lo = *(const i32x4*)(B + brow0 * 128 + roff[h][0]);
+            const i32x4 hi = *(const i32x4*)(B + brow0 * 128 + roff[h][1]);
+            bfr[j][h] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+          sb[j] = SB[brow0 + l32];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int mrow = (2 * i + wm) * 32;
+          i32x8 afr[2];
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+            const i32x4 lo = *(const i32x4*)(A + mrow * 128 + roff[h][0]);
+            const i32x4 hi = *(const i32x4*)(A + mrow * 128 + roff[h][1]);
+            afr[h] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+          // this lane's 16 accumulator rows: 8*qq + 4*khalf + e
+          f32x4 sa[4];
+#pragma unroll
+          for (int qq = 0; qq < 4; qq++) sa[qq] = *(const f32x4*)(SA + mrow + 8 * qq + 4 * khalf);
+#pragma unroll
+          for (int j = 0; j < 2; j++) {
+            f32x16 p;
+#pragma unroll
+            for (int r = 0; r < 16; r++) p[r] = 0.f;
+            // cbsz = blgp = 0: both operands E4M3; scale exponents 127 = 2^0
+            p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[0], bfr[j][0], p, 0, 0, 0, 127, 0, 127);
+            p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[1], bfr[j][1], p, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = fmaf(p[r], sa[r >> 2][r & 3] * sb[j], acc[i][j][r]);
+          }
+        }
+      }
+      wait_vmcnt<0>();   // no LDS write may land after the tile's reads
+    }
+    float* out = seg < a.n_first ? a.out0 + (size_t)seg * a.ostride0
+                                 : a.out1 + (size_t)(seg - a.n_first) * a.ostride1;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int m = mt * C::BM + (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+          const int n = nt * C::BN + wn * 64 + j * 32 + l32;
+          out[(size_t)m * a.Nn + n] = acc[i][j][r];
+        }
+  }
+}
+
+long wgrad_pitch(long rows, int n_seg, int pad) { return (rows + (long)pad * n_seg + pad - 1) / pad * pad; }
 
 static hipError_t launch_wgrad_dma(const WgradArgs& a, hipStream_t s) {
   hipError_t e;
-  wg_kofs_kernel<<<1, 64, 0, s>>>(a.offsets, a.n_seg, a.kofs);
+  wg_kofs_kernel<<<1, 64, 0, s>>>(a.offsets, a.n_seg, WT_PAD, a.kofs);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 gp(a.M / 256, (unsigned)(a.pitch / WT_PAD)), gq(a.Nn / 256, (unsigned)(a.pitch / WT_PAD));
   seg_transpose_kernel<<<gp, 256, 0, s>>>(a.P, nullptr, a.offsets, a.kofs, a.n_seg, a.M, a.pitch, a.pt);
@@ -581,7 +740,7 @@ __global__ __launch_bounds__(256) void wgrad_f32_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------- transposes
-// dst[b][c][r] = src[b][r][c] for [batch][rows][cols] of 2- or 4-byte elements, 64x64 tiles via LDS
+// dst[b][c][r] = src[b][r][c] for [batch][rows][cols] of 1-, 2- or 4-byte elements, 64x64 tiles via LDS
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst,
                                                         int rows, int cols) {
@@ -674,11 +833,41 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_wgrad_f8(const WgradArgs& a, const WgradF8Scratch& f, hipStream_t s) {
+  if (a.M % 256 || a.Nn % 256 || !f.pt8 || !f.qt8 || !f.spt || !f.sqt) return hipErrorInvalidValue;
+  hipError_t e;
+  wg_kofs_kernel<<<1, 64, 0, s>>>(a.offsets, a.n_seg, 128, a.kofs);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // transposed bf16 copies (segments padded to 128 rows), then their 1x128 tiles in E4M3
+  const dim3 gp(a.M / 256, (unsigned)(a.pitch / WT_PAD)), gq(a.Nn / 256, (unsigned)(a.pitch / WT_PAD));
+  seg_transpose_kernel<<<gp, 256, 0, s>>>(a.P, nullptr, a.offsets, a.kofs, a.n_seg, a.M, a.pitch, a.pt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  seg_transpose_kernel<<<gq, 256, 0, s>>>(a.Q, a.q_row, a.offsets, a.kofs, a.n_seg, a.Nn, a.pitch, a.qt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_quant_act_tscale(a.pt, a.M, (int)a.pitch, f.pt8, f.spt, s)) != hipSuccess) return e;
+  if ((e = launch_quant_act_tscale(a.qt, a.Nn, (int)a.pitch, f.qt8, f.sqt, s)) != hipSuccess) return e;
+  WgradF8Args g;
+  g.PT = f.pt8; g.QT = f.qt8; g.SPT = f.spt; g.SQT = f.sqt; g.pitch = a.pitch; g.kofs = a.kofs;
+  g.n_seg = a.n_seg; g.M = a.M; g.Nn = a.Nn;
+  const int NT = a.Nn / 256;
+  g.sn = NT % 8 == 0 ? 8 : NT % 4 == 0 ? 4 : NT >= 8 ? 8 : (NT >= 4 ? 4 : (NT >= 2 ? 2 : 1));
+  g.sm = WgF8::SUPER / g.sn;
+  g.out0 = a.out0; g.out1 = a.out1; g.ostride0 = a.ostride0; g.ostride1 = a.ostride1; g.n_first = a.n_first;
+  auto k = wgrad_f8_kernel;
+  if ((e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, WgF8::BYTES)) !=
+      hipSuccess)
+    return e;
+  k<<<WgF8::GRID, WgF8::THREADS, WgF8::BYTES, s>>>(g);
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose(const void* src, void* dst, int batch, int rows, int cols, int dtype, hipStream_t s) {
   if (batch <= 0 || rows <= 0 || cols <= 0) return hipSuccess;
   const dim3 grid(cdiv(cols, 64), cdiv(rows, 64), batch);
   if (dtype == MOE_F32)
     transpose_kernel<float><<<grid, 256, 0, s>>>((const float*)src, (float*)dst, rows, cols);
+  else if (dtype == MOE_FP8_E4M3)
+    transpose_kernel<uint8_t><<<grid, 256, 0, s>>>((const uint8_t*)src, (uint8_t*)dst, rows, cols);
   else
     transpose_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, rows, cols);
   return hipGetLastError();

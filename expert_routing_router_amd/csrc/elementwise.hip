@@ -267,7 +267,8 @@ template <int OFF>
 __device__ __forceinline__ float swz_xor(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (OFF << 10)));
 }
-template <bool BF>
+// TS: scales stored transposed, scale[c / 128][r]
+template <bool BF, bool TS = false>
 __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__ src, long rows, int cols,
                                                         const int32_t* __restrict__ row_index,
                                                         uint8_t* __restrict__ q, float* __restrict__ scale) {
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
     hi |= e4m3_encode(v[4 + i] / sc) << (8 * i);
   }
   *(uint2*)(q + (size_t)r * cols + c0) = make_uint2(lo, hi);
-  if (sub == 0) scale[(size_t)r * tpr + c0 / 128] = sc;
+  if (sub == 0) scale[TS ? (size_t)(c0 / 128) * rows + r : (size_t)r * tpr + c0 / 128] = sc;
 }
 
 // One workgroup per 128x128 block.
@@ -345,6 +346,14 @@ hipError_t launch_quant_act(const void* src, int src_dtype, long rows, int cols,
   const unsigned grid = (unsigned)cdiv<long>(tiles, 16);
   if (src_dtype == MOE_BF16) quant_act_kernel<true><<<grid, 256, 0, s>>>(src, rows, cols, row_index, q, scale);
   else quant_act_kernel<false><<<grid, 256, 0, s>>>(src, rows, cols, row_index, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_tscale(const uint16_t* src, long rows, int cols, uint8_t* q, float* scale_t,
+                                   hipStream_t s) {
+  const long tiles = rows * (cols / 128);
+  if (tiles <= 0) return hipSuccess;
+  quant_act_kernel<true, true><<<(unsigned)cdiv<long>(tiles, 16), 256, 0, s>>>(src, rows, cols, nullptr, q, scale_t);
   return hipGetLastError();
 }
 

@@ -700,22 +700,33 @@ extern "C" int moe_quantize_fp8(int32_t kind, const void* src, int32_t src_dtype
 }
 
 // ---------------------------------------------------------------- backward
-// Supported: bf16 u and experts, I (and I_s) a multiple of 128, shared
-// experts of the routed experts' size (or none), T > 0 handled, T == 0 no-op.
-// bf16 layers (I % 128 == 0) and fp32 layers; shared experts of the routed size
+// Supported, with shared experts of the routed experts' size (or none); T == 0 is a no-op:
+//   bf16 layers (I % 128 == 0), fp32 layers (I % 8 == 0), and FP8 layers with bf16 u,
+//   d % 256 == 0 and I % 256 == 0 (every product of the FP8 backward on the 256-row
+//   LDS-DMA kernels) whose padded weight-gradient operands stay under 2^31 bytes.
+static long bwd_rows(const moe_desc_t* d) { return (long)d->T * d->top_k + (long)d->n_shared * d->T; }
+static long bwd_f8_pitch(const moe_desc_t* d) {
+  return wgrad_pitch(bwd_rows(d), d->n_routed + d->n_shared, 128);
+}
 static int backward_shape_ok(const moe_desc_t* d) {
   const bool bf = d->in_dtype == MOE_BF16 && d->expert_dtype == MOE_BF16;
   const bool f32 = d->in_dtype == MOE_F32 && d->expert_dtype == MOE_F32;
-  if (!bf && !f32) return MOE_ENOTSUP;
+  const bool f8 = d->in_dtype == MOE_BF16 && d->expert_dtype == MOE_FP8_E4M3;
+  if (!bf && !f32 && !f8) return MOE_ENOTSUP;
   if (bf && d->inter % 128) return MOE_ENOTSUP;
   if (f32 && d->inter % 8) return MOE_ENOTSUP;
+  if (f8) {
+    if (d->d % 256 || d->inter % 256) return MOE_ENOTSUP;
+    const long wide = std::max<long>(d->d, 2L * d->inter);
+    if (wide * bwd_f8_pitch(d) >= (1L << 31) || bwd_rows(d) * wide >= (1L << 31)) return MOE_ENOTSUP;
+  }
   if (d->n_shared && d->inter_shared != d->inter) return MOE_ENOTSUP;
   return MOE_OK;
 }
 
 struct BwdWs {
   size_t idx, gate, scores, rscratch, bitmap, wprefix, offsets, mtile, row_token, slot_row;
-  size_t ab, h, y, dy, dh, dab, dg, dz, pt, qt, kofs, total;
+  size_t ab, h, y, dy, dh, dab, dg, dz, pt, qt, kofs, q8, qs, pt8, qt8, spt, sqt, total;
   long pitch;
 };
 
@@ -723,6 +734,7 @@ static BwdWs bwd_layout(const moe_desc_t* d) {
   BwdWs w;
   const size_t T = d->T, K = d->top_k, N = d->n_routed, Ns = d->n_shared, I = d->inter, D = d->d;
   const size_t W = (T + 63) / 64, n_seg = N + Ns, R = T * K + Ns * T;
+  const bool f8 = d->expert_dtype == MOE_FP8_E4M3;
   const size_t es = d->expert_dtype == MOE_F32 ? 4 : 2;     // activations A|B, H, Y, dY, dH, dA|dB
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += al256(bytes); return at; };
@@ -744,12 +756,21 @@ static BwdWs bwd_layout(const moe_desc_t* d) {
   w.dab = take(R * 2 * I * es);
   w.dg = take(T * K * 4);
   w.dz = take(T * K * 4);
-  // transposed, padded operands of the weight-gradient GEMMs (d a multiple of 256)
-  w.pitch = D % 256 == 0 && es == 2 ? wgrad_pitch((long)R, (int)n_seg) : 0;
+  // transposed, padded operands of the weight-gradient GEMMs (d a multiple of 256; FP8:
+  // segments padded to 128 rows, one scale tile)
+  w.pitch = f8 ? bwd_f8_pitch(d) : D % 256 == 0 && es == 2 ? wgrad_pitch((long)R, (int)n_seg) : 0;
   const size_t wide = D > 2 * I ? D : 2 * I;
   w.pt = w.pitch ? take(wide * (size_t)w.pitch * 2) : 0;
   w.qt = w.pitch ? take(wide * (size_t)w.pitch * 2) : 0;
   w.kofs = w.pitch ? take((n_seg + 1) * 4) : 0;
+  // FP8: E4M3 copy of the activation each product reads (u, H, dY, dA|dB in turn) and its
+  // 1x128 scales; the weight-gradient operands' codes and transposed scales
+  w.q8 = f8 ? take(R * wide) : 0;
+  w.qs = f8 ? take(R * (wide / 128) * 4) : 0;
+  w.pt8 = f8 ? take(wide * (size_t)w.pitch) : 0;
+  w.qt8 = f8 ? take(wide * (size_t)w.pitch) : 0;
+  w.spt = f8 ? take((size_t)w.pitch / 128 * wide * 4) : 0;
+  w.sqt = f8 ? take((size_t)w.pitch / 128 * wide * 4) : 0;
   w.total = o;
   return w;
 }
@@ -770,6 +791,23 @@ extern "C" int moe_transpose_expert_weights(const moe_desc_t* d, const moe_weigh
     return MOE_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   const int I = d->inter, D = d->d, dt = d->expert_dtype;
+  if (dt == MOE_FP8_E4M3) {
+    // the transpose of an E4M3 matrix with 128x128 block scales is its codes and its scale grid
+    // transposed: exactly the same values
+    if (!aligned(w->w13_scale) || !aligned(w->w2_scale) || !aligned(wt->w13_scale) || !aligned(wt->w2_scale))
+      return MOE_EINVAL;
+    if (d->n_shared && (!aligned(w->w13_shared_scale) || !aligned(w->w2_shared_scale) ||
+                        !aligned(wt->w13_shared_scale) || !aligned(wt->w2_shared_scale)))
+      return MOE_EINVAL;
+    MOE_TRY(launch_transpose(w->w13_scale, (void*)wt->w13_scale, d->n_routed, 2 * I / 128, D / 128, MOE_F32, s));
+    MOE_TRY(launch_transpose(w->w2_scale, (void*)wt->w2_scale, d->n_routed, D / 128, I / 128, MOE_F32, s));
+    if (d->n_shared) {
+      MOE_TRY(launch_transpose(w->w13_shared_scale, (void*)wt->w13_shared_scale, d->n_shared, 2 * I / 128, D / 128,
+                               MOE_F32, s));
+      MOE_TRY(launch_transpose(w->w2_shared_scale, (void*)wt->w2_shared_scale, d->n_shared, D / 128, I / 128,
+                               MOE_F32, s));
+    }
+  }
   MOE_TRY(launch_transpose(w->w13, (void*)wt->w13, d->n_routed, 2 * I, D, dt, s));
   MOE_TRY(launch_transpose(w->w2, (void*)wt->w2, d->n_routed, D, I, dt, s));
   if (d->n_shared) {
@@ -817,6 +855,12 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
   if (d->n_shared && (!aligned(w->w13_shared) || !aligned(w->w2_shared) || !aligned(wt->w13_shared) ||
                       !aligned(wt->w2_shared) || !aligned(g->dw13_shared) || !aligned(g->dw2_shared)))
     return MOE_EINVAL;
+  const bool f8 = d->expert_dtype == MOE_FP8_E4M3;
+  if (f8 && (!aligned(w->w13_scale) || !aligned(w->w2_scale) || !aligned(wt->w13_scale) || !aligned(wt->w2_scale)))
+    return MOE_EINVAL;
+  if (f8 && d->n_shared && (!aligned(w->w13_shared_scale) || !aligned(w->w2_shared_scale) ||
+                            !aligned(wt->w13_shared_scale) || !aligned(wt->w2_shared_scale)))
+    return MOE_EINVAL;
   const BwdWs L = bwd_layout(d);
   if (ws_bytes < L.total) return MOE_EWORKSPACE;
   if (d->T == 0) return MOE_OK;
@@ -825,7 +869,8 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
   const int T = d->T, K = d->top_k, N = d->n_routed, Ns = d->n_shared, I = d->inter, D = d->d;
   const long TK = (long)T * K, R = TK + (long)Ns * T;
   const int n_seg = N + Ns;
-  const int dt = d->expert_dtype;                    // MOE_BF16 or MOE_F32 (activations and weights)
+  const int wdt = d->expert_dtype;
+  const int dt = f8 ? MOE_BF16 : wdt;                // activations: bf16 (bf16 and FP8 layers) or fp32
   int32_t* idx = (int32_t*)(base + L.idx);
   float* gate = (float*)(base + L.gate);
   float* scores = (float*)(base + L.scores);
@@ -846,32 +891,48 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
   // which also keeps the affinities for the gate gradients), then A|B, H, Y
   RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, scores, idx, gate, nullptr);   // loads not needed
   MOE_TRY(run_router(ra, base + L.rscratch, s));
-  const int bm = gemm_bm(d->expert_dtype, (int)(TK / N), d->d, d->inter);
+  const int bm = f8 ? 256 : gemm_bm(d->expert_dtype, (int)(TK / N), d->d, d->inter);
   PermuteArgs p;
   p.idx = idx; p.T = T; p.K = K; p.n_routed = N;
   p.bitmap = (uint64_t*)(base + L.bitmap); p.wprefix = (int32_t*)(base + L.wprefix);
   p.counts_ws = nullptr; p.offsets = offsets; p.row_token = row_token; p.slot_row = slot_row;
   p.counts_out = nullptr; p.n_extra_seg = Ns; p.mtile_prefix = mtile; p.bm = bm;
   MOE_TRY(launch_permute(p, s));
-  auto grouped = [&](const void* x, long x_rows, const int32_t* ridx, const void* w0, const void* w1, long wstride,
-                     void* out, int Nout, int Kred) -> hipError_t {
-    GemmArgs ga = gemm_args(x, x_rows, nullptr, ridx, offsets, mtile, n_seg, w0, nullptr, wstride, 0, out, Nout,
-                            Kred, (int)R);
+  // out = x W^T per segment (W = w0[e], or w1[e - N] for the shared segments); FP8 layers
+  // first quantise x per 1x128 tile (the activation operand of each FP8 product) and
+  // multiply E4M3 by E4M3 with both scales applied per 128-long block of the reduction
+  uint8_t* q8 = f8 ? base + L.q8 : nullptr;
+  float* qs = f8 ? (float*)(base + L.qs) : nullptr;
+  auto grouped = [&](const void* x, long x_rows, const int32_t* ridx, const void* w0, const void* w1,
+                     const float* sc0, const float* sc1, long wstride, void* out, int Nout,
+                     int Kred) -> hipError_t {
+    const long sstride = f8 ? wstride / (128L * 128) : 0;
+    if (f8) {
+      hipError_t e = launch_quant_act(x, MOE_BF16, x_rows, Kred, nullptr, q8, qs, s);
+      if (e != hipSuccess) return e;
+    }
+    GemmArgs ga = gemm_args(f8 ? q8 : x, x_rows, qs, ridx, offsets, mtile, n_seg, w0, sc0, wstride, sstride, out,
+                            Nout, Kred, (int)R);
     ga.w1 = Ns ? w1 : w0;
+    ga.ws1 = Ns ? sc1 : sc0;
     ga.n_first = N;
-    return launch_gemm_down(ga, dt, bm, s);
+    return launch_gemm_down(ga, wdt, bm, s);
   };
   const long s13 = 2L * I * D, s2 = (long)D * I;
-  MOE_TRY(grouped(u, T, row_token, w->w13, w->w13_shared, s13, AB, 2 * I, D));      // [A|B] = X W13^T
+  MOE_TRY(grouped(u, T, row_token, w->w13, w->w13_shared, w->w13_scale, w->w13_shared_scale, s13, AB, 2 * I,
+                  D));                                                                // [A|B] = X W13^T
   MOE_TRY(launch_swiglu_fwd(AB, H, R, I, dt, s));                                     // H = SiLU(A) B
-  MOE_TRY(grouped(H, R, nullptr, w->w2, w->w2_shared, s2, Y, D, I));                // Y = H W2^T
+  MOE_TRY(grouped(H, R, nullptr, w->w2, w->w2_shared, w->w2_scale, w->w2_shared_scale, s2, Y, D,
+                  I));                                                                // Y = H W2^T
 
   // backward
   MOE_TRY(launch_dgate_dy(dout, Y, slot_row, gate, T, D, K, Ns, TK, T, dg, dY, dt, s));   // dg, dY
-  MOE_TRY(grouped(dY, R, nullptr, wt->w2, wt->w2_shared, s2, dH, I, D));             // dH = dY W2
+  MOE_TRY(grouped(dY, R, nullptr, wt->w2, wt->w2_shared, wt->w2_scale, wt->w2_shared_scale, s2, dH, I,
+                  D));                                                                // dH = dY W2
   MOE_TRY(launch_swiglu_bwd(dH, AB, dAB, R, I, dt, s));                               // dA | dB
   void* dX = Y;                                                                       // Y is no longer needed
-  MOE_TRY(grouped(dAB, R, nullptr, wt->w13, wt->w13_shared, s13, dX, D, 2 * I));     // dX = [dA dB] W13
+  MOE_TRY(grouped(dAB, R, nullptr, wt->w13, wt->w13_shared, wt->w13_scale, wt->w13_shared_scale, s13, dX, D,
+                  2 * I));                                                            // dX = [dA dB] W13
   MOE_TRY(launch_router_bwd(scores, idx, dg, dout, dX, slot_row, w->centroids, d->router_dtype, u, offsets,
                             row_token, T, N, D, K, Ns, TK, T, dz, g->du, g->dE, dt, s));  // dz, du, dE
   WgradArgs wa;
@@ -880,14 +941,19 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
     wa.pt = (uint16_t*)(base + L.pt); wa.qt = (uint16_t*)(base + L.qt); wa.kofs = (int32_t*)(base + L.kofs);
     wa.pitch = L.pitch;
   }
+  // FP8: both operands quantised in 128-row tiles along each expert's rows
+  WgradF8Scratch f8s{f8 ? base + L.pt8 : nullptr, f8 ? base + L.qt8 : nullptr,
+                     f8 ? (float*)(base + L.spt) : nullptr, f8 ? (float*)(base + L.sqt) : nullptr};
+  auto wgrad = [&](const void* P, const void* Q) -> hipError_t {
+    if (dt == MOE_F32) return launch_wgrad_f32(wa, (const float*)P, (const float*)Q, s);
+    return f8 ? launch_wgrad_f8(wa, f8s, s) : launch_wgrad(wa, s);
+  };
   wa.P = (const uint16_t*)dY; wa.Q = (const uint16_t*)H; wa.q_row = nullptr; wa.q_rows = R; wa.M = D; wa.Nn = I;
   wa.out0 = g->dw2; wa.ostride0 = s2; wa.out1 = Ns ? g->dw2_shared : g->dw2; wa.ostride1 = s2;
-  if (dt == MOE_F32) MOE_TRY(launch_wgrad_f32(wa, (const float*)dY, (const float*)H, s));
-  else MOE_TRY(launch_wgrad(wa, s));                                                  // dW2 = dY^T H
+  MOE_TRY(wgrad(dY, H));                                                              // dW2 = dY^T H
   wa.P = (const uint16_t*)dAB; wa.Q = (const uint16_t*)u; wa.q_row = row_token; wa.q_rows = T; wa.M = 2 * I;
   wa.Nn = D;
   wa.out0 = g->dw13; wa.ostride0 = s13; wa.out1 = Ns ? g->dw13_shared : g->dw13; wa.ostride1 = s13;
-  if (dt == MOE_F32) MOE_TRY(launch_wgrad_f32(wa, (const float*)dAB, (const float*)u, s));
-  else MOE_TRY(launch_wgrad(wa, s));                                                  // dW13 = [dA dB]^T X
+  MOE_TRY(wgrad(dAB, u));                                                             // dW13 = [dA dB]^T X
   return MOE_OK;
 }

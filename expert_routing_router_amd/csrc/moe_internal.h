@@ -122,8 +122,13 @@ struct WgradArgs {
   // qt [Nn][pitch] bf16, kofs [n_seg+1]; pitch = wgrad_pitch(rows of P, n_seg)
   uint16_t* pt = nullptr; uint16_t* qt = nullptr; int32_t* kofs = nullptr; long pitch = 0;
 };
-long wgrad_pitch(long rows, int n_seg);
+long wgrad_pitch(long rows, int n_seg, int pad = 64);
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
+// FP8 weight gradients (E4M3 operands in 128-row tiles along each segment's rows): needs the
+// WgradArgs' pt/qt/kofs with pitch = wgrad_pitch(rows, n_seg, 128) and these E4M3 copies and
+// transposed scales: pt8 [M][pitch], qt8 [Nn][pitch], spt [pitch/128][M], sqt [pitch/128][Nn]
+struct WgradF8Scratch { uint8_t* pt8; uint8_t* qt8; float* spt; float* sqt; };
+hipError_t launch_wgrad_f8(const WgradArgs& a, const WgradF8Scratch& f, hipStream_t s);
 // fp32 layers: P, Q fp32 (the args' P/Q/pt/qt are ignored)
 hipError_t launch_wgrad_f32(const WgradArgs& a, const float* P, const float* Q, hipStream_t s);
 // element-wise backward pieces; dtype MOE_BF16 or MOE_F32 for the activations they read and write
@@ -145,6 +150,9 @@ hipError_t launch_seq_balance(const float* s, const int32_t* idx, int T, int N, 
                               float* f, float* P, float* loss, void* ws, hipStream_t st);
 hipError_t launch_quant_act(const void* src, int src_dtype, long rows, int cols,
                             const int32_t* row_index, uint8_t* q, float* scale, hipStream_t s);
+// bf16 rows [rows][cols] in 1x128 tiles, scales stored transposed: scale_t [cols/128][rows]
+hipError_t launch_quant_act_tscale(const uint16_t* src, long rows, int cols, uint8_t* q, float* scale_t,
+                                   hipStream_t s);
 hipError_t launch_quant_w(const void* src, int src_dtype, long rows, int cols, uint8_t* q,
                           float* scale, hipStream_t s);
 

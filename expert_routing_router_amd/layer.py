@@ -143,14 +143,23 @@ class MoELayer:
         cfg, dev = self.cfg, self.device
         if getattr(self, "_wt", None) is None:
             I, d, N, ns = cfg.inter, cfg.d, cfg.n_routed, max(cfg.n_shared, 1)
-            wdt = self.w13.dtype                          # bf16 or fp32, as the experts
+            wdt = self.w13.dtype                          # bf16, fp32 or E4M3 codes, as the experts
             self._w13t = torch.empty((N, d, 2 * I), dtype=wdt, device=dev)
             self._w2t = torch.empty((N, I, d), dtype=wdt, device=dev)
             self._w13st = torch.empty((ns, d, 2 * I), dtype=wdt, device=dev)
             self._w2st = torch.empty((ns, I, d), dtype=wdt, device=dev)
             sh = cfg.n_shared > 0
+            sc = [None] * 4
+            if cfg.expert_dtype == "fp8":                 # the block-scale grids, transposed with the codes
+                f32 = torch.float32
+                sc = [torch.empty((N, d // 128, 2 * I // 128), dtype=f32, device=dev),
+                      torch.empty((N, I // 128, d // 128), dtype=f32, device=dev),
+                      torch.empty((ns, d // 128, 2 * I // 128), dtype=f32, device=dev),
+                      torch.empty((ns, I // 128, d // 128), dtype=f32, device=dev)]
+                self._wt_scales = sc
             self._wt = L.make_weights(None, self._w13t, self._w2t, self._w13st if sh else None,
-                                      self._w2st if sh else None)
+                                      self._w2st if sh else None, sc[0], sc[1],
+                                      sc[2] if sh else None, sc[3] if sh else None)
             L.moe_transpose_expert_weights(self.desc, self.weights, self._wt, stream=stream)
             f32 = torch.float32
             self.grads = {

@@ -196,21 +196,31 @@ def test_capacity_arg_errors(lib):
 
 
 def test_backward_support_matrix(lib):
-    """moe_backward covers bf16 layers with I % 128 == 0 and fp32 layers; the workspace size is 0
-    (and the call MOE_ENOTSUP) otherwise."""
+    """moe_backward covers bf16 layers with I % 128 == 0, fp32 layers, and FP8 layers (bf16 u) with
+    d % 256 == 0 and I % 256 == 0; the workspace size is 0 (and the call MOE_ENOTSUP) otherwise.
+    FP8 layers need their block scales, original and transposed (MOE_EINVAL without them)."""
     bf = M.make_desc(T=64, d=512, n_routed=16, top_k=4, n_shared=1, inter=256)
     f32 = M.make_desc(T=64, d=256, n_routed=16, top_k=4, n_shared=1, inter=128, in_dtype="f32",
                       router_dtype="f32", expert_dtype="f32")
     f8 = M.make_desc(T=64, d=512, n_routed=16, top_k=4, n_shared=1, inter=256, router_dtype="f32",
                      expert_dtype="fp8")
+    f8_odd = M.make_desc(T=64, d=512, n_routed=16, top_k=4, n_shared=1, inter=128, router_dtype="f32",
+                         expert_dtype="fp8")
     odd = M.make_desc(T=64, d=512, n_routed=16, top_k=4, n_shared=1, inter=192)
-    assert M.moe_backward_workspace_bytes(bf) > 0 and M.moe_backward_workspace_bytes(f32) > 0
-    assert M.moe_backward_workspace_bytes(f8) == 0 and M.moe_backward_workspace_bytes(odd) == 0
+    for ok in (bf, f32, f8):
+        assert M.moe_backward_workspace_bytes(ok) > 0
+    assert M.moe_backward_workspace_bytes(f8_odd) == 0 and M.moe_backward_workspace_bytes(odd) == 0
+    # the FP8 workspace holds the E4M3 operand copies on top of the bf16 layer's
+    assert M.moe_backward_workspace_bytes(f8) > M.moe_backward_workspace_bytes(bf)
     w = M.MoeWeights(A, A, A, A, A, None, None, None, None)
+    ws8 = M.MoeWeights(A, A, A, A, A, A, A, A, A)
     g = M.MoeGrads(A, A, A, A, A, A)
-    st = lib.moe_backward(ctypes.byref(f8), ctypes.byref(w), ctypes.byref(w), A, A, A, ctypes.byref(g), A,
-                          1 << 40, None)
-    assert st == M.MOE_ENOTSUP
+    call = lambda d, w, wt: lib.moe_backward(ctypes.byref(d), ctypes.byref(w), ctypes.byref(wt), A, A, A,
+                                             ctypes.byref(g), A, 1 << 40, None)
+    assert call(f8_odd, ws8, ws8) == M.MOE_ENOTSUP
+    assert call(f8, w, ws8) == M.MOE_EINVAL and call(f8, ws8, w) == M.MOE_EINVAL
+    tr = lambda d, w, wt: lib.moe_transpose_expert_weights(ctypes.byref(d), ctypes.byref(w), ctypes.byref(wt), None)
+    assert tr(f8, w, ws8) == M.MOE_EINVAL and tr(f8, ws8, w) == M.MOE_EINVAL and tr(f8_odd, ws8, ws8) == M.MOE_ENOTSUP
 
 
 def test_pack_arg_errors(lib):
