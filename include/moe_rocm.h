@@ -227,7 +227,10 @@ typedef struct moe_grads {
 
 /* Transposed expert weights for moe_backward: fills wt->w13 [N_r, d, 2I] and
  * wt->w2 [N_r, I, d] (and the shared ones) from the weights in w, in the
- * experts' dtype (bf16 or fp32). Other members of wt are ignored. */
+ * experts' dtype (bf16, fp32 or E4M3 codes). FP8 layers: also the block
+ * scales, transposed: wt->w13_scale [N_r, d/128, 2I/128], wt->w2_scale
+ * [N_r, I/128, d/128] (and the shared ones), so wt holds exactly the values
+ * of the transposed E4M3 matrices. Other members of wt are ignored. */
 int moe_transpose_expert_weights(const moe_desc_t* desc, const moe_weights_t* w, moe_weights_t* wt,
                                  moe_stream_t stream);
 
@@ -258,9 +261,15 @@ int moe_pack_expert_weights(const moe_desc_t* desc, const moe_weights_t* w, moe_
  *   dg = <dout, Y>, dY = g dout, dH = dY W2, dA|dB from SwiGLU, dX = [dA dB] W13,
  *   ds = (dg - sum g dg) / sum s, dz = ds s (1 - s), dE = dz^T u.
  * The forward is recomputed inside (intermediates in the experts' dtype,
- * fp32 accumulation). Supported: bf16 u and experts with I % 128 == 0, or
- * fp32 u and experts with I % 8 == 0; N_s == 0 or I_s == I; MOE_ENOTSUP
- * otherwise. wt: moe_transpose_expert_weights of w.
+ * bf16 for FP8 layers; fp32 accumulation). Supported: bf16 u and experts
+ * with I % 128 == 0; fp32 u and experts with I % 8 == 0; bf16 u and FP8
+ * experts with d % 256 == 0 and I % 256 == 0 (and the padded weight-gradient
+ * operands under 2^31 bytes); N_s == 0 or I_s == I; MOE_ENOTSUP otherwise.
+ * FP8 layers run Fprop, Dgrad and Wgrad as E4M3 GEMMs (pwwt.cn note section
+ * 3): each activation operand quantised per 1x128 tile along the product's
+ * reduction dimension (for Wgrad: 128-row tiles starting at each expert's
+ * first row), the layer's 128x128-block weights; gradients with respect to
+ * the E4M3 weight values. wt: moe_transpose_expert_weights of w.
  * ws: moe_backward_workspace_bytes(desc) bytes (0 when unsupported). */
 size_t moe_backward_workspace_bytes(const moe_desc_t* desc);
 int moe_backward(const moe_desc_t* desc, const moe_weights_t* w, const moe_weights_t* wt, const void* u,
@@ -285,9 +294,14 @@ int moe_seq_balance_loss(const moe_desc_t* desc, int32_t seq_len, float alpha, c
                          const int32_t* topk_idx, float* f, float* P, float* loss, void* ws,
                          size_t ws_bytes, moe_stream_t stream);
 
-/* Whole layer: route -> permute -> grouped experts (routed + shared) ->
- * combine -> (update_bias != 0) bias update. b is read by the router and, if
- * update_bias, updated in place after the loads are known.
+/* Whole layer, the output equation of the xyznot.com guides ("Método" §2):
+ *   out_t = u_t + sum_s FFN_s(u_t) + sum_k g_{k,t} FFN_{idx_k}(u_t)
+ * with the gates of the gating equation (same section; pwwt.cn note 1.1.2,
+ * 1.3) and, when update_bias != 0, the end-of-step bias update (pwwt.cn note
+ * 1.1.3). The steps run as route -> permute -> grouped experts (routed +
+ * shared) -> combine -> bias update, with the kernels of the calls above.
+ * b is read by the router and, if update_bias, updated in place after the
+ * loads are known.
  *   u, out [T,d] in_dtype. dbg nullable. ws: moe_workspace_bytes(desc). */
 int moe_forward(const moe_desc_t* desc, const moe_weights_t* w, const void* u, float* b,
                 void* out, moe_route_out_t* dbg, int32_t update_bias, void* ws,
