@@ -521,13 +521,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 }
 
 int gemm_bm(int dtype, int mean_rows, int dmodel, int inter) {
-  // FP8: 256-row tiles of the LDS-DMA kernel when the down GEMM's width is a
-  // multiple of its 256-row weight tile, else the register-staged 192-row kernel.
-  if (dtype == MOE_FP8_E4M3) return dmodel % 256 == 0 ? 256 : 192;
   // one m-tile per expert when the mean load (+4 sigma of a binomial load) fits;
   // 64- and 128-row tiles (deeper load ring) for small loads when every product's
   // width suits the LDS-DMA kernel
   const int need = mean_rows + 4 * (int)std::sqrt((double)(mean_rows > 0 ? mean_rows : 1));
+  // FP8: 256- or 320-row tiles of the LDS-DMA kernel when the down GEMM's width is a
+  // multiple of its 256-row weight tile, else the register-staged 192-row kernel.
+  if (dtype == MOE_FP8_E4M3) return dmodel % 256 != 0 ? 192 : need <= 256 ? 256 : 320;
   const bool dma_all = dmodel % 256 == 0 && inter % 256 == 0;
   if (dma_all && need <= 64) return 64;
   if (dma_all && need <= 128) return 128;

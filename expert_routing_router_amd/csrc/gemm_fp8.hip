@@ -237,18 +237,29 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------- LDS-DMA path
-// 8 waves (2 along M x 4 along N), tile 64*MB rows x 256 weight rows, one
-// 128-wide K block (= one scale block) per stage, two stages. Buffer loads
-// write the E4M3 rows and the rows' activation scales straight into LDS. The
-// two weight-block scales a workgroup needs per K block (gate and up rows for
-// SwiGLU, the two 128-row halves of the tile for the down GEMM) are staged in
-// LDS once, for all K blocks.
+// 8 waves (2 along M x 4 along N), tile 64*MB rows x 256 weight rows. A stage
+// holds 64 elements of K (half a scale block) of both operands and the tile
+// rows' activation scales of that stage's 128-element block; four stages in a
+// ring, three in flight while one is multiplied. Buffer loads write the E4M3
+// rows and the row scales straight into LDS. The two weight-block scales a
+// workgroup needs per K block (gate and up rows for SwiGLU, the two 128-row
+// halves of the tile for the down GEMM) are staged in LDS once, for all K.
 //
-// A stage row is 128 bytes = 8 chunks of 16; one load instruction of a wave
-// fills 8 rows (1 KB): lane l writes row l>>3, slot l&7 and fetches chunk
-// slot ^ ((row >> 1) & 7), so the MFMA operand reads (16 lanes = 16
+// The MFMA takes the weight rows as its first operand and the activation rows
+// as its second, so each lane's 16 results belong to one activation row (its
+// column) and 16 rows of one 32-row weight block, which share one weight
+// scale: the fold of a 64-wide partial p is acc += p * (s_act * s_w) with one
+// scale product per lane and block. (The pages promote every 128 elements;
+// folding each half with the same block scale gives the same sum up to fp32
+// rounding.)
+//
+// A stage row is 64 bytes = 4 chunks of 16; one load instruction of a wave
+// fills 16 rows (1 KB): lane l writes row l>>2, slot l&3 and fetches chunk
+// slot ^ ((row >> 2) & 3), so the MFMA operand reads (16 lanes = 16
 // consecutive rows, one chunk) hit 16 distinct 4-bank groups.
-constexpr int F8_BK = 128;
+constexpr int F8_BK = 128;              // scale block along K
+constexpr int F8_SK = 64;               // K elements per stage
+constexpr int F8_STAGES = 4;
 constexpr int F8_MAX_KB = 256;          // K <= 32768
 
 template <int MB>
@@ -256,18 +267,19 @@ struct F8DmaCfg {
   static constexpr int THREADS = 512;
   static constexpr int BM = 64 * MB;
   static constexpr int BN = 256;
-  static constexpr int A_BLOCKS = BM / 8;            // 1 KB blocks
-  static constexpr int B_BLOCKS = BN / 8;
-  static constexpr int A_BYTES = BM * F8_BK;
-  static constexpr int B_BYTES = BN * F8_BK;
+  static constexpr int A_LOADS = BM / 16;            // 1 KB loads per stage
+  static constexpr int B_LOADS = BN / 16;
+  static constexpr int A_BYTES = BM * F8_SK;
+  static constexpr int B_BYTES = BN * F8_SK;
   static constexpr int SA_BYTES = BM * 4;
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
-  static constexpr int BYTES = 2 * STAGE;
-  static constexpr int A_PER_WAVE = A_BLOCKS / 8;
-  static constexpr int B_PER_WAVE = B_BLOCKS / 8;
+  static constexpr int BYTES = F8_STAGES * STAGE;
+  static constexpr int A_MAX = (A_LOADS + 7) / 8;    // A loads of waves 0 .. (A_LOADS % 8) - 1 (or all)
+  static constexpr int A_MIN = A_LOADS / 8;
+  static constexpr int B_PER_WAVE = B_LOADS / 8;
   static constexpr int SA_WAVES = BM / 64;           // waves that load 64 row scales each
-  static_assert(A_BLOCKS % 8 == 0 && B_BLOCKS % 8 == 0, "blocks split evenly over 8 waves");
-  static_assert(SA_WAVES <= 8, "row scales");
+  static_assert(B_LOADS % 8 == 0 && SA_WAVES <= 8, "loads split over 8 waves");
+  static_assert(STAGE % 16 == 0, "stage alignment");
   static_assert(BYTES + 2 * F8_MAX_KB * 4 + 2048 <= 160 * 1024, "LDS budget");
 };
 
@@ -296,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
 
   const int row0 = a.offsets[seg] + mtile * BM;
   const int mvalid = min(BM, a.offsets[seg + 1] - row0);
-  const int K = a.K, KB = K / F8_BK;
+  const int K = a.K, KB = K / F8_BK, KS = K / F8_SK;
   const bool first = seg < a.n_first;
   const uint8_t* wbase = first ? (const uint8_t*)a.w0 + (size_t)seg * a.wstride0
                                : (const uint8_t*)a.w1 + (size_t)(seg - a.n_first) * a.wstride1;
@@ -310,24 +322,27 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
     ssw[1][i] = wsc[(size_t)blk1 * KB + i];
   }
 
-  // ---- per-lane global offsets of this wave's blocks (fixed over K)
-  const int brow = lane >> 3;
-  const int bchunk = (lane & 7) ^ ((((wave & 1) << 2) + (lane >> 4)) & 7);   // block parity = wave parity
+  // ---- per-lane global offsets of this wave's loads (fixed over K)
+  const int lrow = lane >> 2;                                  // row within a 16-row load
+  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);           // chunk its slot holds
   const i32x4 xr = rsrc_words(a.x, a.x_rows * (long)K);
   const i32x4 sr = rsrc_words(a.x_scale, a.x_rows * (long)KB * 4);
-  // K-blocked weights (moe_pack_expert_weights): the tile's 256 rows per 128-element block are one
-  // contiguous 32 KB with this kernel's chunk swizzle applied, so block i of a stage is its kilobyte i
+  // K-blocked weights (moe_pack_expert_weights): the tile's 256 rows per 64-element step are
+  // one contiguous 16 KB with this kernel's chunk swizzle applied, so load i of a stage reads
+  // its kilobyte i
   const bool wblk = a.w_blocked;
   const i32x4 wr = wblk ? rsrc_words(wbase + (size_t)ntile * BN * K, (long)BN * K)
                         : rsrc_words(wbase, (long)(SWIGLU ? 2 * a.N : a.N) * K);
-  const int bstep = wblk ? BN * F8_BK : F8_BK;
-  int aoff[C::A_PER_WAVE];
+  const int bstep = wblk ? BN * F8_SK : F8_SK;
+  // wave w loads A blocks w, w + 8, ...: waves below A_LOADS % 8 take one more
+  const int n_a = (C::A_LOADS % 8 == 0 || wave < C::A_LOADS % 8) ? C::A_MAX : C::A_MIN;
+  int aoff[C::A_MAX];
 #pragma unroll
-  for (int i = 0; i < C::A_PER_WAVE; i++) {
-    const int r = (wave + 8 * i) * 8 + brow;
+  for (int i = 0; i < C::A_MAX; i++) {
+    const int r = (wave + 8 * i) * 16 + lrow;
     const int rr = min(max(row0 + min(r, mvalid - 1), 0), a.rows_bound - 1);   // in range for any offsets
     const int src = a.row_index ? a.row_index[rr] : rr;
-    aoff[i] = r < mvalid ? src * K + bchunk * 16 : kOutOfRange;
+    aoff[i] = r < mvalid ? src * K + lchunk * 16 : kOutOfRange;
   }
   int soff_row;
   {
@@ -339,21 +354,30 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
   int boff[C::B_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::B_PER_WAVE; i++) {
-    const int r = (wave + 8 * i) * 8 + brow;
+    const int r = (wave + 8 * i) * 16 + lrow;
     const int wrow = SWIGLU ? (r < HN ? ntile * HN + r : a.N + ntile * HN + (r - HN)) : ntile * BN + r;
-    boff[i] = wblk ? (wave + 8 * i) * 1024 + lane * 16 : wrow * K + bchunk * 16;
+    boff[i] = wblk ? (wave + 8 * i) * 1024 + lane * 16 : wrow * K + lchunk * 16;
   }
   const uint32_t lds0 = lds_addr(lds);
   const bool sa_wave = wave < C::SA_WAVES;
-  auto issue = [&](int kb, int buf) __attribute__((always_inline)) {
-    const int koff = kb * F8_BK;
+  // loads per stage of this wave (wave-uniform): its waits count them
+  const int n_loads = n_a + C::B_PER_WAVE + (sa_wave ? 1 : 0);
+  auto issue = [&](int ks, int buf) __attribute__((always_inline)) {
     const uint32_t sbase = lds0 + buf * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < C::A_PER_WAVE; i++) dma_b128(xr, aoff[i], koff, sbase + (wave + 8 * i) * 1024);
+    for (int i = 0; i < C::A_MAX; i++)
+      if (i < C::A_MIN || n_a == C::A_MAX) dma_b128(xr, aoff[i], ks * F8_SK, sbase + (wave + 8 * i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::B_PER_WAVE; i++)
-      dma_b128(wr, boff[i], kb * bstep, sbase + C::A_BYTES + (wave + 8 * i) * 1024);
-    if (sa_wave) dma_b32(sr, soff_row, kb * 4, sbase + C::A_BYTES + C::B_BYTES + wave * 256);
+      dma_b128(wr, boff[i], ks * bstep, sbase + C::A_BYTES + (wave + 8 * i) * 1024);
+    if (sa_wave) dma_b32(sr, soff_row, (ks >> 1) * 4, sbase + C::A_BYTES + C::B_BYTES + wave * 256);
+  };
+  // this wave's loads of stage ks are done when at most those of the two later stages are pending
+  auto wait_stage = [&]() __attribute__((always_inline)) {
+    if (n_loads == 6) wait_vmcnt<12>();
+    else if (n_loads == 5) wait_vmcnt<10>();
+    else if (n_loads == 4) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
   };
 
   f32x16 acc[MB][2];
@@ -368,73 +392,83 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
   for (int i = 0; i < MB; i++)
     if ((2 * i + wm) * 32 < mvalid) mb_active = i + 1;
 
-  // operand reads: rows block*32 + l32 share (row >> 1) & 7 == (l32 >> 1) & 7
+  // operand reads: lane l32 reads row block*32 + l32 (whose (row >> 2) & 3 is (l32 >> 2) & 3),
+  // the 32 bytes of K half khalf: chunks 2*khalf and 2*khalf + 1
   const int l32 = lane & 31, khalf = lane >> 5;
-  const int sw = (l32 >> 1) & 7;
-  int roff[2][2];
-#pragma unroll
-  for (int h = 0; h < 2; h++)
-#pragma unroll
-    for (int c = 0; c < 2; c++) roff[h][c] = l32 * 128 + (((h * 4 + khalf * 2 + c) ^ sw) << 4);
-  const int bro[2] = {(SWIGLU ? wn * 32 : wn * 64) * 128, (SWIGLU ? HN + wn * 32 : wn * 64 + 32) * 128};
-  // which staged weight-scale row each of this wave's two n-blocks uses
+  const int sw = (l32 >> 2) & 3;
+  const int roff0 = l32 * F8_SK + (((2 * khalf) ^ sw) << 4);
+  const int roff1 = l32 * F8_SK + (((2 * khalf + 1) ^ sw) << 4);
+  const int bro[2] = {(SWIGLU ? wn * 32 : wn * 64) * F8_SK, (SWIGLU ? HN + wn * 32 : wn * 64 + 32) * F8_SK};
+  // which staged weight-scale row each of this wave's two weight blocks uses
   const int wsel0 = SWIGLU ? 0 : (wn >> 1), wsel1 = SWIGLU ? 1 : (wn >> 1);
 
-  // One K block from stage `buf`: per 32x32 block two MFMAs into a fresh fp32
-  // partial, then acc += partial * (s_act[row] * s_w).
-  auto compute_na = [&](auto na_tag, int buf, int kb) __attribute__((always_inline)) {
+  // One stage: per 32x32 block one MFMA into a fresh fp32 partial, then
+  // acc += partial * (s_act[this lane's row] * s_w[block]). The blocks are
+  // software-pipelined: each block's MFMA is issued before the fold of the
+  // block before it, so the matrix core and the VALU work side by side (with
+  // one partial register set the fold and the next MFMA would serialise).
+  auto compute_na = [&](auto na_tag, int buf, int ks) __attribute__((always_inline)) {
     constexpr int NA = decltype(na_tag)::value;
-    const uint8_t* A = lds + buf * C::STAGE;
-    const uint8_t* B = A + C::A_BYTES;
-    const float* SA = (const float*)(B + C::B_BYTES);
-    const float swj[2] = {ssw[wsel0][kb], ssw[wsel1][kb]};
-    i32x8 bfr[2][2];
-#pragma unroll
-    for (int j = 0; j < 2; j++)
-#pragma unroll
-      for (int h = 0; h < 2; h++) {
-        const i32x4 lo = *(const i32x4*)(B + bro[j] + roff[h][0]);
-        const i32x4 hi = *(const i32x4*)(B + bro[j] + roff[h][1]);
-        bfr[j][h] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-#pragma unroll
-    for (int i = 0; i < NA; i++) {
-      const int mrow = (2 * i + wm) * 32;
-      i32x8 afr[2];
-#pragma unroll
-      for (int h = 0; h < 2; h++) {
-        const i32x4 lo = *(const i32x4*)(A + mrow * 128 + roff[h][0]);
-        const i32x4 hi = *(const i32x4*)(A + mrow * 128 + roff[h][1]);
-        afr[h] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-      // this lane's 16 accumulator rows: 8*q + 4*khalf + e, q, e in 0..3
-      f32x4 sa[4];
-#pragma unroll
-      for (int q = 0; q < 4; q++) sa[q] = *(const f32x4*)(SA + mrow + 8 * q + 4 * khalf);
+    if constexpr (NA > 0) {
+      const uint8_t* A = lds + buf * C::STAGE;
+      const uint8_t* B = A + C::A_BYTES;
+      const float* SA = (const float*)(B + C::B_BYTES);
+      const float swj[2] = {ssw[wsel0][ks >> 1], ssw[wsel1][ks >> 1]};
+      i32x8 bfr[2];
 #pragma unroll
       for (int j = 0; j < 2; j++) {
-        f32x16 p;
-#pragma unroll
-        for (int r = 0; r < 16; r++) p[r] = 0.f;
-        // cbsz = blgp = 0: both operands E4M3; scale exponents 127 = 2^0
-        p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[0], bfr[j][0], p, 0, 0, 0, 127, 0, 127);
-        p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[1], bfr[j][1], p, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-        for (int r = 0; r < 16; r++) acc[i][j][r] = fmaf(p[r], sa[r >> 2][r & 3] * swj[j], acc[i][j][r]);
+        const i32x4 lo = *(const i32x4*)(B + bro[j] + roff0);
+        const i32x4 hi = *(const i32x4*)(B + bro[j] + roff1);
+        bfr[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
+      auto load_a = [&](int i, i32x8& afr, float& sa) __attribute__((always_inline)) {
+        const int mrow = (2 * i + wm) * 32;
+        const i32x4 lo = *(const i32x4*)(A + mrow * F8_SK + roff0);
+        const i32x4 hi = *(const i32x4*)(A + mrow * F8_SK + roff1);
+        afr = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        sa = SA[mrow + l32];
+      };
+      // cbsz = blgp = 0: both operands E4M3; scale exponents 127 = 2^0
+      auto mma = [&](const i32x8& w, const i32x8& x) __attribute__((always_inline)) {
+        f32x16 z;
+#pragma unroll
+        for (int r = 0; r < 16; r++) z[r] = 0.f;
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, z, 0, 0, 0, 127, 0, 127);
+      };
+      auto fold = [&](f32x16& c, const f32x16& p, float sc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) c[r] = fmaf(p[r], sc, c[r]);
+      };
+      i32x8 afr;
+      float sa;
+      load_a(0, afr, sa);
+      f32x16 p0 = mma(bfr[0], afr);
+      static_for<NA>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        const f32x16 p1 = mma(bfr[1], afr);             // block (i, 1)
+        const float sc0 = sa * swj[0], sc1 = sa * swj[1];
+        if constexpr (i + 1 < NA) load_a(i + 1, afr, sa);
+        fold(acc[i][0], p0, sc0);                         // block (i, 0) while (i, 1) runs
+        if constexpr (i + 1 < NA) p0 = mma(bfr[0], afr);   // block (i + 1, 0)
+        fold(acc[i][1], p1, sc1);
+      });
     }
   };
 
-  // Two-stage ring: wait for this wave's loads of stage kb, barrier (every
-  // wave's data for kb is in LDS, every wave is done with kb-1), refill the
-  // other buffer with kb+1, multiply kb.
+  // Four-stage ring: wait for this wave's loads of stage ks, barrier (every
+  // wave's data for ks is in LDS, every wave is done with ks-1), refill ks-1's
+  // buffer with ks+3, multiply ks. Past the last stage the refills repeat it
+  // into buffers no later stage reads, so every wave issues the same loads per stage.
   auto k_loop = [&](auto na_tag) __attribute__((always_inline)) {
+    const int last = KS - 1;
     issue(0, 0);
-    for (int kb = 0; kb < KB; kb++) {
-      wait_vmcnt<0>();
+    issue(min(1, last), 1);
+    issue(min(2, last), 2);
+    for (int ks = 0; ks < KS; ks++) {
+      wait_stage();
       __syncthreads();
-      issue(min(kb + 1, KB - 1), (kb + 1) & 1);
-      compute_na(na_tag, kb & 1, kb);
+      issue(min(ks + 3, last), (ks + 3) & 3);
+      compute_na(na_tag, ks & 3, ks);
     }
     wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
   };
@@ -443,25 +477,33 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
     case 1: k_loop(std::integral_constant<int, 1>{}); break;
     case 2: k_loop(std::integral_constant<int, 2>{}); break;
     case 3: k_loop(std::integral_constant<int, (MB >= 3 ? 3 : MB)>{}); break;
+    case 4: k_loop(std::integral_constant<int, (MB >= 4 ? 4 : MB)>{}); break;
     default: k_loop(std::integral_constant<int, MB>{}); break;
   }
 
+  // Each lane holds one activation row (its column in the MFMA layout) and, per block,
+  // 16 weight rows 8q + 4*khalf + e: 4 consecutive output columns per q.
   // GEMM1 writes H in fp32 (re-quantised per 1x128 tile next); GEMM2 writes Y in bf16.
 #pragma unroll
   for (int i = 0; i < MB; i++) {
-    if (i < mb_active) {
+    const int row = (2 * i + wm) * 32 + l32;
+    if (i < mb_active && row < mvalid && (unsigned)(row0 + row) < (unsigned)a.rows_bound) {
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-        if (row < mvalid && (unsigned)(row0 + row) < (unsigned)a.rows_bound) {
-          if (SWIGLU) {
-            float* orow = (float*)a.out + (size_t)(row0 + row) * a.N;
-            orow[ntile * HN + wn * 32 + l32] = silu_mul(acc[i][0][r], acc[i][1][r]);
-          } else {
-            uint16_t* orow = (uint16_t*)a.out + (size_t)(row0 + row) * a.N;
-            const int col = ntile * BN + wn * 64 + l32;
-            orow[col] = f32_to_bf16(acc[i][0][r]);
-            orow[col + 32] = f32_to_bf16(acc[i][1][r]);
+      for (int q = 0; q < 4; q++) {
+        const int m = 8 * q + 4 * khalf;
+        if (SWIGLU) {
+          float* orow = (float*)a.out + (size_t)(row0 + row) * a.N + ntile * HN + wn * 32 + m;
+          f32x4 h;
+#pragma unroll
+          for (int e = 0; e < 4; e++) h[e] = silu_mul(acc[i][0][4 * q + e], acc[i][1][4 * q + e]);
+          *(f32x4*)orow = h;
+        } else {
+          uint16_t* orow = (uint16_t*)a.out + (size_t)(row0 + row) * a.N + ntile * BN + wn * 64 + m;
+#pragma unroll
+          for (int j = 0; j < 2; j++) {
+            const uint32_t lo = f32_to_bf16(acc[i][j][4 * q]) | ((uint32_t)f32_to_bf16(acc[i][j][4 * q + 1]) << 16);
+            const uint32_t hi = f32_to_bf16(acc[i][j][4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[i][j][4 * q + 3]) << 16);
+            *(uint2*)(orow + 32 * j) = make_uint2(lo, hi);
           }
         }
       }
@@ -496,23 +538,23 @@ static hipError_t launch_fp8_t(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// dst[mat][tile][block][256 rows][128 bytes]: row r's 16-byte chunk c of a
-// 128-element block sits at slot c ^ ((r >> 1) & 7), where the LDS-DMA kernel's
+// dst[mat][tile][step][256 rows][64 bytes]: row r's 16-byte chunk c of a
+// 64-element step sits at slot c ^ ((r >> 2) & 3), where the LDS-DMA kernel's
 // lane for that slot fetches it from a row-major operand
 __global__ void pack_blocked_f8_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, long n_chunks,
                                        int rows, int K, int swiglu_i) {
-  const int blocks = K / F8_BK, tiles = rows / 256;
+  const int steps = K / F8_SK, tiles = rows / 256;
   for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < n_chunks; q += (long)gridDim.x * blockDim.x) {
-    const int slot = (int)(q & 7);
-    const int r = (int)((q >> 3) & 255);
-    long rest = q >> 11;
-    const int kb = (int)(rest % blocks);
-    rest /= blocks;
+    const int slot = (int)(q & 3);
+    const int r = (int)((q >> 2) & 255);
+    long rest = q >> 10;
+    const int ks = (int)(rest % steps);
+    rest /= steps;
     const int t = (int)(rest % tiles);
     const long mat = rest / tiles;
     const int srow = swiglu_i > 0 ? (r < 128 ? t * 128 + r : swiglu_i + t * 128 + (r - 128)) : t * 256 + r;
-    const int c = slot ^ ((r >> 1) & 7);
-    *(i32x4*)(dst + (size_t)q * 16) = *(const i32x4*)(src + ((size_t)mat * rows + srow) * K + kb * F8_BK + c * 16);
+    const int c = slot ^ ((r >> 2) & 3);
+    *(i32x4*)(dst + (size_t)q * 16) = *(const i32x4*)(src + ((size_t)mat * rows + srow) * K + ks * F8_SK + c * 16);
   }
 }
 
@@ -528,9 +570,10 @@ hipError_t launch_pack_blocked_f8(const uint8_t* src, uint8_t* dst, int n_mat, i
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, bool swiglu, int bm, hipStream_t s) {
   // K-blocked weights only on the LDS-DMA kernel; blocked activations are a bf16 feature
-  if (a.x_blocked || a.out_blocked || (a.w_blocked && bm != 256)) return hipErrorInvalidValue;
-  // 256-row tiles: the LDS-DMA kernel (needs the down GEMM's width a multiple of 256)
+  if (a.x_blocked || a.out_blocked || (a.w_blocked && bm != 256 && bm != 320)) return hipErrorInvalidValue;
+  // 256- and 320-row tiles: the LDS-DMA kernel (needs the down GEMM's width a multiple of 256)
   if (bm == 256) return swiglu ? launch_fp8_dma<4, true>(a, s) : launch_fp8_dma<4, false>(a, s);
+  if (bm == 320) return swiglu ? launch_fp8_dma<5, true>(a, s) : launch_fp8_dma<5, false>(a, s);
   if (bm == 192) return swiglu ? launch_fp8_t<3, true>(a, s) : launch_fp8_t<3, false>(a, s);
   return hipErrorInvalidValue;
 }
