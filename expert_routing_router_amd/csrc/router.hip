@@ -52,10 +52,11 @@ struct RouterLdsT {
 };
 using RouterLds = RouterLdsT<RT_BT>;      // the fp64 front end works on 32 tokens
 
+// One formula for every z (no divergent branches across a wave): for z < 0,
+// exp(-z) is large and 1 / (1 + exp(-z)) keeps full fp64 relative accuracy
+// (it underflows to 0 only below z = -709, far under fp32's smallest affinity).
 __device__ __forceinline__ double sigmoid64(double z) {
-  if (z >= 0.0) return 1.0 / (1.0 + exp(-z));
-  double ez = exp(z);
-  return ez / (1.0 + ez);
+  return 1.0 / (1.0 + exp(-z));
 }
 
 // ---------------------------------------------------------------- front ends
@@ -321,11 +322,13 @@ __device__ __forceinline__ void select_lane_major(const RouteArgs& a, const floa
     fs = k4[1] == kmax ? 1 : fs;
     fs = k4[0] == kmax ? 0 : fs;
     const int slot = __builtin_amdgcn_readlane(fs, L);
-    float sv = s4[0];                                       // selects only: no branch around these
-    sv = slot == 1 ? s4[1] : sv;
-    sv = slot == 2 ? s4[2] : sv;
-    sv = slot == 3 ? s4[3] : sv;
-    const float sel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), L));
+    // lane L's four affinities as wave-uniform values, then a scalar pick (indexing s4
+    // by slot would send the array through LDS)
+    const int c0 = __builtin_amdgcn_readlane(__float_as_int(s4[0]), L);
+    const int c1 = __builtin_amdgcn_readlane(__float_as_int(s4[1]), L);
+    const int c2 = __builtin_amdgcn_readlane(__float_as_int(s4[2]), L);
+    const int c3 = __builtin_amdgcn_readlane(__float_as_int(s4[3]), L);
+    const float sel = __int_as_float(slot == 0 ? c0 : slot == 1 ? c1 : slot == 2 ? c2 : c3);
     const bool owner = lane == L;
 #pragma unroll
     for (int i = 0; i < 4; i++) k4[i] = owner && slot == i ? 0u : k4[i];
