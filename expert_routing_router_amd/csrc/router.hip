@@ -23,7 +23,7 @@
 // exercises exactly the production selection.
 //
 // Precision: bf16 products (exact in fp32) are summed by the MFMAs in fp32
-// over 128-element chunks of d, the chunks in fp64; the sigmoid is evaluated
+// over chunks of d of at most 128 elements, the chunks in fp64; the sigmoid is evaluated
 // in fp64 and rounded once to fp32. The split-K router rounds each slice's
 // fp64 sum to fp32 once before the S slices are added in fp64, in slice order.
 // fp32 centroids are split into three bf16 terms (hi + mid + lo reproduces the
@@ -697,8 +697,9 @@ __global__ __launch_bounds__(256, 1) void logits_kernel(const uint16_t* __restri
 // chunks sit at the LDS slots the MFMA reads want, so every centroid load
 // instruction reads one contiguous kilobyte. Wave (wm, wn) computes tokens
 // 64 wm.. x experts 64 wn.. with v_mfma_f32_32x32x16_bf16 (2 x 2 blocks); its
-// fp32 sums over each 128-element chunk are added into fp64 in chunk order,
-// and the slice's fp64 sum is written once as fp32 to partials[slice][t][e].
+// fp32 sums over chunks of at most 128 elements are added into fp64 in chunk
+// order, and the slice's fp64 sum is written once as fp32 to
+// partials[slice][t][e].
 // route_kernel in partials mode adds the S slices in fp64, in slice order.
 constexpr int SK_BT = 128;                 // tokens per workgroup
 constexpr int SK_NE = 256;                 // experts per workgroup (all of them)
@@ -779,11 +780,30 @@ __global__ __launch_bounds__(512, 1) void logits_splitk_kernel(const uint16_t* _
 #pragma unroll
       for (int r = 0; r < 16; r++) { acc[i][j][r] = 0.f; z64[i][j][r] = 0.0; }
 
-  // two k-substeps of stage `buf`: their operand reads, then their MFMAs with
-  // loads P0..P1-1 (of step kti into buffer bufi) spread between them
-  auto half = [&](auto h_tag, auto p0_tag, auto p1_tag, int buf, int kti, int bufi) __attribute__((always_inline)) {
+  // The fp32 sums of token block i go into fp64 when one of its chunks ends:
+  // block 0's chunks are the 128-element chunks [128 c, 128 c + 128), block 1's
+  // are shifted by 64 (64 elements first and last), so every stage ends exactly
+  // one block's chunk and its fold (cvt + fp64 add of 32 sums) is interleaved
+  // with the MFMAs of the other block instead of stalling the matrix core.
+  auto fold_piece = [&](auto x_tag, auto p_tag) __attribute__((always_inline)) {
+    constexpr int X = decltype(x_tag)::value, P = decltype(p_tag)::value;
+    constexpr int j = P >> 1, r0 = (P & 1) * 8;
+#pragma unroll
+    for (int r = r0; r < r0 + 8; r++) {
+      z64[X][j][r] += (double)acc[X][j][r];
+      acc[X][j][r] = 0.f;
+    }
+  };
+  // two k-substeps of stage `buf`: their operand reads, then their MFMAs (token
+  // block X first) with loads P0..P1-1 (of step kti into buffer bufi) spread
+  // between them; FOLD: block X's chunk ends with these substeps, and its fold
+  // pieces go between block 1-X's MFMAs
+  auto half = [&](auto h_tag, auto p0_tag, auto p1_tag, auto x_tag, auto fold_tag, int buf, int kti, int bufi)
+      __attribute__((always_inline)) {
     constexpr int H = decltype(h_tag)::value;
     constexpr int P0 = decltype(p0_tag)::value, P1 = decltype(p1_tag)::value;
+    constexpr int X = decltype(x_tag)::value;
+    constexpr bool FOLD = decltype(fold_tag)::value;
     const uint8_t* U = lds + buf * SK_STAGE;
     const uint8_t* Ep = U + SK_U_BYTES;
     bf16x8 af[2][2], bf[2][2];
@@ -796,43 +816,48 @@ __global__ __launch_bounds__(512, 1) void logits_splitk_kernel(const uint16_t* _
       }
     static_for<8>([&](auto m_tag) __attribute__((always_inline)) {
       constexpr int m = decltype(m_tag)::value;
-      constexpr int q = m / 4, i = (m / 2) & 1, j = m & 1;
+      constexpr int i = m < 4 ? X : 1 - X, q = (m >> 1) & 1, j = m & 1;
       if constexpr (m % 2 == 0 && P0 + m / 2 < P1) {
         __builtin_amdgcn_sched_barrier(0);
         issue_part(std::integral_constant<int, P0 + m / 2>{}, kti, bufi);
         __builtin_amdgcn_sched_barrier(0);
       }
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q][i], bf[q][j], acc[i][j], 0, 0, 0);
+      if constexpr (FOLD && m >= 4) {
+        __builtin_amdgcn_sched_barrier(0);
+        fold_piece(x_tag, std::integral_constant<int, m - 4>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
     });
   };
-  auto fold = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-      for (int j = 0; j < 2; j++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          z64[i][j][r] += (double)acc[i][j][r];
-          acc[i][j][r] = 0.f;
-        }
+  // one stage; X: the token block whose chunk ends with it
+  auto stage = [&](auto x_tag, int buf, int kti, int bufi) __attribute__((always_inline)) {
+    half(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+         std::integral_constant<int, SK_LOADS / 2>{}, x_tag, std::false_type{}, buf, kti, bufi);
+    half(std::integral_constant<int, 2>{}, std::integral_constant<int, SK_LOADS / 2>{},
+         std::integral_constant<int, SK_LOADS>{}, x_tag, std::true_type{}, buf, kti, bufi);
   };
 
   // ring of SK_STAGES buffers, as in the grouped GEMM: wait for this wave's loads of
   // step kt, barrier, multiply stage kt while refilling the buffer of step kt-1 with
-  // step kt+STAGES-1 (past the last step: re-reads of it, never used)
+  // step kt+STAGES-1 (past the last step: re-reads of it, never used). Even stages end
+  // a chunk of token block 1, odd stages one of block 0 (nk is even).
   constexpr int S = SK_STAGES;
 #pragma unroll
   for (int p = 0; p < S - 1; p++) issue(min(p, nk - 1), p);
-  for (int kt = 0; kt < nk; kt++) {
-    wait_vmcnt<(S - 2) * SK_LOADS>();
-    __syncthreads();
-    const int kti = min(kt + S - 1, nk - 1), bufi = (kt + S - 1) % S;
-    half(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
-         std::integral_constant<int, SK_LOADS / 2>{}, kt % S, kti, bufi);
-    half(std::integral_constant<int, 2>{}, std::integral_constant<int, SK_LOADS / 2>{},
-         std::integral_constant<int, SK_LOADS>{}, kt % S, kti, bufi);
-    if (kt & 1) fold();                        // a 128-element chunk ends every second stage
+  for (int kt = 0; kt < nk; kt += 2) {
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+      const int k = kt + e;
+      wait_vmcnt<(S - 2) * SK_LOADS>();
+      __syncthreads();
+      const int kti = min(k + S - 1, nk - 1), bufi = (k + S - 1) % S;
+      if (e == 0) stage(std::integral_constant<int, 1>{}, k % S, kti, bufi);
+      else stage(std::integral_constant<int, 0>{}, k % S, kti, bufi);
+    }
   }
+  // block 1's last chunk: the final stage
+  static_for<4>([&](auto p) __attribute__((always_inline)) { fold_piece(std::integral_constant<int, 1>{}, p); });
   wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
 
   // D element (8*(r>>2) + 4*(lane>>5) + (r&3), lane&31) of each 32x32 block
