@@ -388,7 +388,7 @@ def main():
         log("seq balance loss: %.4f ms for %d sequences" % (sb_ms, cfg.T // seq_len))
 
     bwd = None
-    if args.backward and cfg.expert_dtype == "bf16" and cfg.in_dtype == "bf16":
+    if args.backward and cfg.expert_dtype in ("bf16", "fp8") and cfg.in_dtype == "bf16":
         rng = torch.Generator(device="cuda:0").manual_seed(5)
         dout = torch.randn((cfg.T, cfg.d), generator=rng, device="cuda:0").to(torch.bfloat16)
         t0 = time.time()
@@ -406,11 +406,15 @@ def main():
         w13 = (cfg.n_routed + cfg.n_shared) * 2 * cfg.inter * cfg.d
         w2 = (cfg.n_routed + cfg.n_shared) * cfg.inter * cfg.d
         # forward recompute (A|B, Y) + dH + dX + dW2 + dW13: six products of the experts' shape
+        # (bf16 MFMAs, or E4M3 ones for the FP8 layer)
         flops = 3.0 * 2.0 * R * cfg.d * 3 * cfg.inter
-        # weights read twice (W, W^T), fp32 weight gradients written once, u / dout / du
-        byts = 2 * 2 * (w13 + w2) + 4 * (w13 + w2) + cfg.T * cfg.d * (2 + 2 + 4)
+        bwd_peak = PEAK_TFLOPS[cfg.expert_dtype]
+        # weights read twice (W, W^T: 2 bytes, or 1 byte of E4M3 code), fp32 weight gradients
+        # written once, u / dout / du
+        wbytes = 2 if cfg.expert_dtype == "bf16" else 1
+        byts = 2 * wbytes * (w13 + w2) + 4 * (w13 + w2) + cfg.T * cfg.d * (2 + 2 + 4)
         bwd = {"ms": round(bwd_ms, 3), "tokens_per_s": round(cfg.T / bwd_ms * 1e3, 1),
-               "TFLOP/s": round(flops / bwd_ms / 1e9, 1), "mfma_frac": round(flops / bwd_ms / 1e9 / 2500.0, 4),
+               "TFLOP/s": round(flops / bwd_ms / 1e9, 1), "mfma_frac": round(flops / bwd_ms / 1e9 / bwd_peak, 4),
                "GB/s": round(byts / bwd_ms / 1e6, 1), "hbm_frac": round(byts / bwd_ms / 1e6 / PEAK_HBM_GBS, 4),
                "algorithmic_flops": flops, "algorithmic_bytes": byts, "calls": args.backward}
         log("backward: %.3f ms/call (%.0f TFLOP/s, %.0f GB/s algorithmic)" % (bwd_ms, flops / bwd_ms / 1e9,
