@@ -237,13 +237,12 @@ int moe_transpose_expert_weights(const moe_desc_t* desc, const moe_weights_t* w,
 /* K-blocked copies of the expert weights, the layout the grouped GEMMs' LDS
  * rings consume: for each matrix, tiles of 256 rows (SwiGLU w13: W1 rows
  * 128t..128t+127 then W3 rows I+128t..), then steps of the reduction, then
- * the tile's 256 rows of one step each. bf16: 32-element steps (64-byte
- * rows), a row's four 16-byte chunks c stored at slot c ^ ((row >> 2) & 3).
- * FP8 codes: 128-element steps (128-byte rows), chunk c of eight at slot
- * c ^ ((row >> 1) & 7); the block scales keep their layout. A tile's step is
- * then one contiguous block, so every 1 KB load instruction of the kernels
- * reads one contiguous kilobyte instead of pieces of 16 (bf16) or 8 (FP8)
- * different rows (a layout choice for gfx950's load path; the products are
+ * the tile's 256 rows of one step each. Steps are 64 bytes of a row: 32
+ * bf16 elements or 64 FP8 codes, a row's four 16-byte chunks c stored at
+ * slot c ^ ((row >> 2) & 3); FP8 block scales keep their layout. A tile's
+ * step is then one contiguous block, so every 1 KB load instruction of the
+ * kernels reads one contiguous kilobyte instead of pieces of 16 different
+ * rows (a layout choice for gfx950's load path; the products are
  * unchanged). Fills wb->w13, wb->w2 (and wb->w13_shared, wb->w2_shared when
  * N_s > 0), each the size of its source, from w; other members of wb are
  * ignored; the caller then passes them as w13_blk ... in moe_weights_t.

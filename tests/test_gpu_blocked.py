@@ -22,14 +22,14 @@ pytestmark = pytest.mark.gpu
 
 def pack_ref(w, swiglu_i, fp8=False):
     """[n, rows, K] -> [n, tiles, steps, 256, step]: tiles of 256 rows (SwiGLU: gate rows 128t.. then
-    up rows swiglu_i + 128t..), steps of 32 bf16 / 128 FP8 elements, row r's 16-byte chunk c at slot
-    c ^ ((r >> 2) & 3) (bf16, 4 chunks) or c ^ ((r >> 1) & 7) (FP8, 8 chunks)."""
+    up rows swiglu_i + 128t..), steps of 64 bytes (32 bf16 / 64 FP8 elements), row r's 16-byte chunk
+    c of 4 at slot c ^ ((r >> 2) & 3)."""
     n, rows, K = w.shape
-    step, nch = (128, 8) if fp8 else (32, 4)
+    step, nch = (64, 4) if fp8 else (32, 4)
     per = 16 // w.dtype.itemsize                                              # elements per chunk
     tiles, steps = rows // 256, K // step
     r = np.arange(256)
-    swz = ((r >> 1) & 7) if fp8 else ((r >> 2) & 3)
+    swz = (r >> 2) & 3
     slot_chunk = np.arange(nch)[None, :] ^ swz[:, None]                      # [256, nch]: chunk held by each slot
     out = np.empty((n, tiles, steps, 256, step), w.dtype)
     for t in range(tiles):

@@ -14,14 +14,14 @@ from tests.test_gpu_blocked import pack_ref
 def test_pack_ref_matches_definition(fp8, swiglu_i):
     rng = np.random.default_rng(3 + int(fp8) + swiglu_i)
     dt = np.uint8 if fp8 else np.uint16
-    step, per = (128, 16) if fp8 else (32, 8)
+    step, per = (64, 16) if fp8 else (32, 8)
     n, rows, K = 2, 512, 256
     w = rng.integers(0, 200, size=(n, rows, K)).astype(dt)
     out = pack_ref(w, swiglu_i, fp8)
     assert out.shape == (n, rows // 256, K // step, 256, step)
     for _ in range(3000):
         m, t, s, r, e = (int(rng.integers(x)) for x in (n, rows // 256, K // step, 256, step))
-        swz = ((r >> 1) & 7) if fp8 else ((r >> 2) & 3)
+        swz = (r >> 2) & 3
         c = (e // per) ^ swz
         if swiglu_i:
             srow = t * 128 + r if r < 128 else swiglu_i + t * 128 + (r - 128)
