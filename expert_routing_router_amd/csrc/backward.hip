@@ -529,7 +529,7 @@ __global__ __launch_bounds__(512, 1) void wgrad_dma_kernel(WgradDmaArgs a) {
         for (int r = 0; r < 16; r++) {
           const int m = mt * C::BM + (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
           const int n = nt * C::BN + wn * 64 + j * 32 + l32;
-          out[(size_t)m * a.Nn + n] = acc[i][j][r];
+          __builtin_nontemporal_store(acc[i][j][r], out + (size_t)m * a.Nn + n);
         }
   }
 }
@@ -688,7 +688,7 @@ __global__ __launch_bounds__(512, 1) void wgrad_f8_kernel(WgradF8Args a) {
         for (int r = 0; r < 16; r++) {
           const int m = mt * C::BM + (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
           const int n = nt * C::BN + wn * 64 + j * 32 + l32;
-          out[(size_t)m * a.Nn + n] = acc[i][j][r];
+          __builtin_nontemporal_store(acc[i][j][r], out + (size_t)m * a.Nn + n);
         }
   }
 }
