@@ -227,6 +227,53 @@ def test_bias_trajectory_200_steps_scores_in():
     assert np.mean(ratio[-20:]) < np.mean(ratio[:20])
 
 
+def test_skew_200_steps_v3_fresh_batches():
+    """The skewed router at the V3 shape (8192 tokens, a fresh seeded batch every step) for 200
+    forward+update steps through moe_route's split-K path. At every step the oracle selects from
+    the GPU's fp32 affinities: selections, loads and the updated bias equal the oracle's bit for
+    bit. At steps 0 and 199 the affinities themselves are compared with the oracle's fp64 ones."""
+    from concurrent.futures import ThreadPoolExecutor
+    cfg = get_config("skew")
+    T, N, K, steps = cfg.T, cfg.n_routed, cfg.top_k, 200
+    desc = M.desc_from_config(cfg)
+    E_host = gen.centroids(cfg)
+    Ed = dev(E_host, cfg.router_dtype)
+    b_ref = gen.bias_init(cfg)
+    b_dev = dev(b_ref, "f32")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    counts = torch.empty(N, dtype=torch.int32, device="cuda")
+    scores = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, M.moe_route_workspace_bytes(desc)), dtype=torch.uint8, device="cuda")
+    ratio = []
+    with ThreadPoolExecutor(8) as ex:                  # batches drawn ahead, 8 in memory at most
+        fut = {s: ex.submit(gen.tokens, cfg, s) for s in range(min(8, steps))}
+        for step in range(steps):
+            u = fut.pop(step).result()
+            if step + 8 < steps:
+                fut[step + 8] = ex.submit(gen.tokens, cfg, step + 8)
+            M.moe_route(desc, b_dev, idx, gate, counts, u=dev(u, cfg.in_dtype), E=Ed, scores_out=scores, ws=ws)
+            M.moe_update_bias(desc, counts, b_dev)
+            torch.cuda.synchronize()
+            s32 = host(scores)
+            r = routing.select(s32, b_ref, K, cfg.n_groups, cfg.topk_groups, cfg.group_topk,
+                               cfg.group_score_biased)
+            c = host(counts)
+            assert np.array_equal(host(idx), r.idx), step
+            assert np.array_equal(c, r.counts), step
+            b_ref = routing.bias_step(r.counts, b_ref, T, K, cfg.gamma)
+            assert np.array_equal(host(b_dev).view(np.uint32), b_ref.view(np.uint32)), step
+            if step in (0, steps - 1):
+                s64 = routing.sigmoid(routing.logits(nx.to_f64(u, cfg.in_dtype), nx.to_f64(E_host, cfg.router_dtype)))
+                err = np.abs(s32.astype(np.float64) - s64).max()
+                log("skew V3 step %d: max |s_gpu - s_oracle| %.3e" % (step, err))
+                assert err < 2.5e-7
+            ratio.append(c.max() / c.mean())
+    log("skew V3 max/mean load: step 0 %.2f, 50 %.2f, 100 %.2f, 150 %.2f, 199 %.2f"
+        % tuple(ratio[i] for i in (0, 50, 100, 150, 199)))
+    assert np.mean(ratio[-20:]) < np.mean(ratio[:20])
+
+
 @pytest.mark.parametrize("name,T", [("v3", None), ("fp8", 1000), ("mid", 4095), ("skew", 2048)])
 def test_forward_routing_matches_moe_route(name, T):
     """moe_forward's topk_idx, gates and loads equal moe_route's bit for bit on the same inputs
