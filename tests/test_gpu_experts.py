@@ -63,10 +63,13 @@ def test_grouped_swiglu(dtype, d, inter):
     assert worst < (1e-2 if dtype == "bf16" else 1e-5)
 
 
-def test_grouped_swiglu_direct_rows_and_fp8():
-    """x read directly (row_token NULL), and the FP8 path against oracle B."""
+@pytest.mark.parametrize("d", [512, 384])
+def test_grouped_swiglu_direct_rows_and_fp8(d):
+    """x read directly (row_token NULL), and the FP8 path against oracle B: d = 512 runs the
+    LDS-DMA kernel (256-row tiles), d = 384 (not a multiple of the 256-row weight tile) the
+    register-staged 192-row kernel."""
     rng = np.random.default_rng(5)
-    d, inter = 512, 256
+    inter = 256
     counts = [3, 0, 300, 64, 129]
     n, rows = len(counts), sum(counts)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
