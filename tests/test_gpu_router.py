@@ -148,10 +148,17 @@ def _e2e(cfg, step=0, b=None, T=None):
     return r, s64, s32, kgap, ggap, host(idx), host(gate), host(counts), host(sout)
 
 
+# V3-shaped routers outside the lane-major selection's fast cases: 4 groups of 64 with the
+# top-3 group score (the split-K logits, then the one-expert-per-lane selection on the slice
+# partials), and no group limit (the lane-major selection with G = 1)
+_ROUTER_VARIANTS = {"v3_g4q3": dict(n_groups=4, topk_groups=2, group_topk=3),
+                    "v3_g1": dict(n_groups=1, topk_groups=1, group_topk=8)}
+
+
 @pytest.mark.parametrize("name,T", [("tiny", None), ("mid", None), ("v3", None), ("fp8", 2048),
-                                    ("skew", 4096), ("v3", 77)])
+                                    ("skew", 4096), ("v3", 77), ("v3_g4q3", 2048), ("v3_g1", 1000)])
 def test_end_to_end_routing(name, T):
-    cfg = get_config(name)
+    cfg = get_config("v3").with_(**_ROUTER_VARIANTS[name]) if name in _ROUTER_VARIANTS else get_config(name)
     r, s64, s32, kgap, ggap, idx, gate, counts, sout = _e2e(cfg, T=T)
     # the GPU's fp32 affinities: logit error ~1e-7 absolute, one rounding of the fp64 sigmoid
     serr = np.abs(sout.astype(np.float64) - s64)
