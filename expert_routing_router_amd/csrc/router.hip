@@ -12,8 +12,7 @@
 // Paths, by shape (run_router picks one):
 //  * split-K router (bf16 u and centroids, N_r = 256): logits_splitk_kernel
 //    computes 128 tokens x 256 experts over one of S slices of d per
-//    workgroup from centroids packed once per call (pack_centroids_kernel),
-//    writes each slice's sum as fp32, and route_kernel in partials mode adds
+//    workgroup, writes each slice's sum as fp32, and route_kernel in partials mode adds
 //    the S slices, applies the sigmoid and selects;
 //  * tiled two-phase router (N_r % 64 == 0, bf16 u, bf16 or fp32 centroids):
 //    logits_kernel writes fp32 affinities, route_kernel selects from them;
@@ -692,10 +691,10 @@ __global__ __launch_bounds__(256, 1) void logits_kernel(const uint16_t* __restri
 // For N_r = 256 experts with bf16 u and centroids. A workgroup (8 waves) owns
 // 128 tokens x all 256 experts over one slice of d (S slices of d/S elements,
 // each a whole number of 128-element chunks), so each u element is read once
-// and each centroid slice once per 128 tokens. The centroids are first packed
-// (pack_centroids_kernel) into 64-element steps of 256 rows whose 16-byte
-// chunks sit at the LDS slots the MFMA reads want, so every centroid load
-// instruction reads one contiguous kilobyte. Wave (wm, wn) computes tokens
+// and each centroid slice once per 128 tokens. u and the centroids are read
+// in place: a load instruction takes 128 bytes (one cache line) of each of 8
+// rows, and each lane picks the 16-byte chunk that its LDS slot holds under
+// the XOR swizzle of the MFMA operand reads. Wave (wm, wn) computes tokens
 // 64 wm.. x experts 64 wn.. with v_mfma_f32_32x32x16_bf16 (2 x 2 blocks); its
 // fp32 sums over chunks of at most 128 elements are added into fp64 in chunk
 // order, and the slice's fp64 sum is written once as fp32 to
@@ -712,19 +711,8 @@ constexpr int SK_E_PER_WAVE = SK_NE / 8 / 8;
 constexpr int SK_LOADS = SK_U_PER_WAVE + SK_E_PER_WAVE;
 static_assert(SK_STAGES * SK_STAGE <= 160 * 1024, "LDS budget");
 
-// E [256][d] bf16 -> [d/64 steps][256 rows][8 slots x 16 B], chunk c of row r at slot c ^ (r & 7)
-__global__ void pack_centroids_kernel(const uint16_t* __restrict__ E, uint16_t* __restrict__ out, int d) {
-  const long n = (long)SK_NE * d / 8;     // 16-byte chunks
-  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < n; q += (long)gridDim.x * blockDim.x) {
-    const int slot = (int)(q & 7), r = (int)((q >> 3) & (SK_NE - 1));
-    const long step = q >> 11;
-    const int c = slot ^ (r & 7);
-    *(i32x4*)(out + q * 8) = *(const i32x4*)(E + (size_t)r * d + step * SK_BK + c * 8);
-  }
-}
-
 __global__ __launch_bounds__(512, 1) void logits_splitk_kernel(const uint16_t* __restrict__ u,
-                                                               const uint16_t* __restrict__ epk,
+                                                               const uint16_t* __restrict__ E,
                                                                float* __restrict__ partials, int T, int d,
                                                                int n_slices) {
   extern __shared__ __align__(16) uint8_t lds[];
@@ -740,14 +728,16 @@ __global__ __launch_bounds__(512, 1) void logits_splitk_kernel(const uint16_t* _
   const int brow = lane >> 3;
   const int bchunk = (lane & 7) ^ brow;        // block rows start at multiples of 8
   const i32x4 ur = rsrc_words(u, (long)T * d * 2);
-  const i32x4 er = rsrc_words(epk, (long)SK_NE * d * 2);
+  const i32x4 er = rsrc_words(E, (long)SK_NE * d * 2);
+  int eoff[SK_E_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < SK_E_PER_WAVE; i++) eoff[i] = (((wave + 8 * i) * 8 + brow) * d + k_begin + bchunk * 8) * 2;
   int uoff[SK_U_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < SK_U_PER_WAVE; i++) {
     const int t = t0 + (wave + 8 * i) * 8 + brow;
     uoff[i] = t < T ? (t * d + k_begin + bchunk * 8) * 2 : kOutOfRange;
   }
-  const int ebase = (k_begin / SK_BK) * SK_NE * SK_BK * 2;    // packed steps before this slice
   const uint32_t lds0 = lds_addr(lds);
   auto issue_part = [&](auto p_tag, int kt, int buf) __attribute__((always_inline)) {
     constexpr int P = decltype(p_tag)::value;
@@ -756,8 +746,7 @@ __global__ __launch_bounds__(512, 1) void logits_splitk_kernel(const uint16_t* _
       dma_b128(ur, uoff[P], kt * SK_BK * 2, sb + (wave + 8 * P) * 1024);
     } else {
       constexpr int Q = P - SK_U_PER_WAVE;
-      dma_b128(er, ebase + (wave + 8 * Q) * 1024 + lane * 16, kt * SK_NE * SK_BK * 2,
-               sb + SK_U_BYTES + (wave + 8 * Q) * 1024);
+      dma_b128(er, eoff[Q], kt * SK_BK * 2, sb + SK_U_BYTES + (wave + 8 * Q) * 1024);
     }
   };
   auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
@@ -890,24 +879,17 @@ bool route_splitk_ok(const RouteArgs& a) {
 }
 
 size_t route_splitk_bytes(int T, int d) {
-  const size_t pk = (((size_t)SK_NE * d * 2) + 255) / 256 * 256;
-  return pk + (size_t)splitk_slices(T, d) * T * SK_NE * 4;
+  return (size_t)splitk_slices(T, d) * T * SK_NE * 4;
 }
 
 hipError_t launch_route_splitk(const RouteArgs& a, void* scratch, hipStream_t s) {
-  uint16_t* epk = (uint16_t*)scratch;
-  const size_t pk = (((size_t)SK_NE * a.d * 2) + 255) / 256 * 256;
-  float* partials = (float*)((uint8_t*)scratch + pk);
+  float* partials = (float*)scratch;
   const int S = splitk_slices(a.T, a.d);
-  const long chunks = (long)SK_NE * a.d / 8;
-  pack_centroids_kernel<<<(int)std::min<long>(cdiv<long>(chunks, 256), 2048), 256, 0, s>>>(
-      (const uint16_t*)a.E, epk, a.d);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
   auto k = logits_splitk_kernel;
   if ((e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                SK_STAGES * SK_STAGE)) != hipSuccess) return e;
-  k<<<dim3(cdiv(a.T, SK_BT), S), 512, SK_STAGES * SK_STAGE, s>>>((const uint16_t*)a.u, epk, partials, a.T, a.d, S);
+  k<<<dim3(cdiv(a.T, SK_BT), S), 512, SK_STAGES * SK_STAGE, s>>>((const uint16_t*)a.u, (const uint16_t*)a.E, partials, a.T, a.d, S);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   RouteArgs b = a;
   b.partials = partials;

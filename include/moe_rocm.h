@@ -136,7 +136,7 @@ size_t moe_workspace_bytes(const moe_desc_t* desc);
  *     1/K if the sum is 0).
  *   counts [N_r] int32: overwritten with the number of tokens per expert.
  *   ws: scratch of moe_route_workspace_bytes(desc) bytes (the router's
- *     partial logits and packed centroids); nullable when that is 0 or with
+ *     partial logits); nullable when that is 0 or with
  *     scores_in. MOE_EWORKSPACE when it is missing or smaller.
  * moe_forward and moe_backward route with the same kernels, so their
  * selections equal this call's bit for bit. */
