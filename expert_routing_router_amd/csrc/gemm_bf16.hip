@@ -368,80 +368,90 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
   const int bro0 = (SWIGLU ? wn * 32 : wn * 64) * RB;
   const int bro1 = (SWIGLU ? HN + wn * 32 : wn * 64 + 32) * RB;
 
-  // Two k-substeps (h, h+1) of stage `buf`: all their operand reads, then the
-  // MFMAs in groups with one of the stage loads P0..P1-1 for step kti (into
-  // buffer bufi) in front of each group. Spreading the loads over the step
-  // keeps the texture unit's queues from filling, which otherwise stalls the
-  // issuing wave (and its MFMAs) right after the barrier.
-  auto compute_half = [&](auto na_tag, auto h_tag, auto p0_tag, auto p1_tag, int buf, int kti, int bufi)
-      __attribute__((always_inline)) {
-    constexpr int NA = decltype(na_tag)::value;
-    constexpr int NA1 = NA > 0 ? NA : 1;
-    constexpr int H = decltype(h_tag)::value;
-    constexpr int P0 = decltype(p0_tag)::value, P1 = decltype(p1_tag)::value;
-    const uint8_t* A = lds + buf * C::STAGE;
-    const uint8_t* B = A + C::A_BYTES;
-    bf16x8 bf[2][2], af[2][NA1];
-#pragma unroll
-    for (int s = 0; s < 2; s++) {
-      bf[s][0] = *(const bf16x8*)(B + bro0 + roff[H + s]);
-      bf[s][1] = *(const bf16x8*)(B + bro1 + roff[H + s]);
-#pragma unroll
-      for (int i = 0; i < NA; i++) af[s][i] = *(const bf16x8*)(A + (2 * i + wm) * 32 * RB + roff[H + s]);
-    }
-    // 2*NA (k-substep, m-block) pairs of two MFMAs; a load before every PER pairs
-    constexpr int NP = P1 - P0;
-    constexpr int PAIRS = 2 * NA;
-    constexpr int PER = PAIRS > 0 && NP > 0 ? (PAIRS + NP - 1) / NP : 1;
-    if constexpr (NP > 0) issue_part(std::integral_constant<int, P0>{}, kti, bufi);
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<2 * MB>([&](auto q_tag) __attribute__((always_inline)) {
-      constexpr int q = decltype(q_tag)::value;
-      if constexpr (q < PAIRS) {
-        constexpr int s = q / NA1, i = q % NA1;
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bf[s][0], acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bf[s][1], acc[i][1], 0, 0, 0);
-        if constexpr ((q + 1) % PER == 0 && (q + 1) / PER < NP) {
-          __builtin_amdgcn_sched_barrier(0);
-          issue_part(std::integral_constant<int, P0 + (q + 1) / PER>{}, kti, bufi);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    });
-    // loads left over when few m-blocks are active
-    static_for<NPARTS>([&](auto p_tag) __attribute__((always_inline)) {
-      constexpr int P = decltype(p_tag)::value;
-      if constexpr (P > P0 && P < P1 && P - P0 > PAIRS / PER) issue_part(p_tag, kti, bufi);
-    });
-  };
-  // one stage = SUB/2 halves; the loads split evenly between them
-  auto compute_na = [&](auto na_tag, int buf, int kti, int bufi) __attribute__((always_inline)) {
-    constexpr int HALVES = C::SUB / 2;
-    static_for<HALVES>([&](auto hh) __attribute__((always_inline)) {
-      constexpr int X = decltype(hh)::value;
-      compute_half(na_tag, std::integral_constant<int, 2 * X>{},
-                   std::integral_constant<int, NPARTS * X / HALVES>{},
-                   std::integral_constant<int, NPARTS * (X + 1) / HALVES>{}, buf, kti, bufi);
-    });
-  };
-
-  // Ring protocol for step kt: wait for this wave's loads of stage kt (the
-  // STAGES-2 younger stages may stay outstanding), barrier (every wave's
-  // stage-kt data is in LDS and every wave is done reading stage kt-1), then
-  // multiply stage kt while refilling stage kt-1's buffer with step
-  // kt+STAGES-1. Loads past the last step re-read it into a buffer that is
-  // never read again, so the count per step is fixed.
+  // Operand reads run half a stage ahead of the MFMAs, across the barrier.
+  // Iteration kt enters with k-substep 0 of stage kt in registers. It
+  // multiplies that substep while reading substep 1 of stage kt, waits for
+  // stage kt+1 and meets the barrier, reads substep 0 of stage kt+1, then
+  // multiplies substep 1 of stage kt. The matrix core thus holds queued work
+  // while the waves meet at the barrier, and the first MFMAs after it need no
+  // read. Stage kt's buffer is free at that barrier (every wave has read it,
+  // and the barrier waits for the reads), so stage kt+S is loaded into it:
+  // its first PA loads between the MFMAs of substep 1, the rest between those
+  // of substep 0 of the next iteration, before its barrier.
+  static_assert(C::SUB == 2, "two 16-element k-substeps per stage");
   constexpr int S = C::STAGES;
+  constexpr int PA = NPARTS / 2;
   const int nk = K / C::BK;
   auto k_loop = [&](auto na_tag) __attribute__((always_inline)) {
+    constexpr int NA = decltype(na_tag)::value;
+    constexpr int NA1 = NA > 0 ? NA : 1;
+    bf16x8 ra[2][NA1], rb[2][2];             // [k-substep]
+    auto read_sub = [&](auto s_tag, int buf) __attribute__((always_inline)) {
+      constexpr int SS = decltype(s_tag)::value;
+      const uint8_t* A = lds + buf * C::STAGE;
+      const uint8_t* B = A + C::A_BYTES;
+      rb[SS][0] = *(const bf16x8*)(B + bro0 + roff[SS]);
+      rb[SS][1] = *(const bf16x8*)(B + bro1 + roff[SS]);
+#pragma unroll
+      for (int i = 0; i < NA; i++) ra[SS][i] = *(const bf16x8*)(A + (2 * i + wm) * 32 * RB + roff[SS]);
+    };
+    // the NA MFMA pairs of k-substep SS, with loads P0..P1-1 of step kti into buffer
+    // bufi spread between them (the rest after them when few m-blocks are active)
+    auto mma_sub = [&](auto s_tag, auto p0_tag, auto p1_tag, int kti, int bufi) __attribute__((always_inline)) {
+      constexpr int SS = decltype(s_tag)::value;
+      constexpr int P0 = decltype(p0_tag)::value, P1 = decltype(p1_tag)::value;
+      constexpr int NP = P1 - P0;
+      constexpr int PER = NA > 0 && NP > 0 ? (NA + NP - 1) / NP : 1;
+      if constexpr (NP > 0) issue_part(std::integral_constant<int, P0>{}, kti, bufi);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<MB>([&](auto q_tag) __attribute__((always_inline)) {
+        constexpr int q = decltype(q_tag)::value;
+        if constexpr (q < NA) {
+          acc[q][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[SS][q], rb[SS][0], acc[q][0], 0, 0, 0);
+          acc[q][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[SS][q], rb[SS][1], acc[q][1], 0, 0, 0);
+          if constexpr ((q + 1) % PER == 0 && (q + 1) / PER < NP) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_part(std::integral_constant<int, P0 + (q + 1) / PER>{}, kti, bufi);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      });
+      static_for<NPARTS>([&](auto p_tag) __attribute__((always_inline)) {
+        constexpr int P = decltype(p_tag)::value;
+        if constexpr (P > P0 && P < P1 && P - P0 > NA / PER) issue_part(p_tag, kti, bufi);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using PAc = std::integral_constant<int, PA>;
+    // prologue: stages 0..S-2 whole and the first part of stage S-1 (clamped re-reads of
+    // the last step past it, into buffers never read again), then substep 0 of stage 0
 #pragma unroll
     for (int p = 0; p < S - 1; p++) issue(min(p, nk - 1), p);
-    for (int kt = 0; kt < nk; kt++) {
+    static_for<PA>([&](auto p) __attribute__((always_inline)) { issue_part(p, min(S - 1, nk - 1), S - 1); });
+    if (a_full) wait_vmcnt<(S - 2) * NPARTS + PA>();
+    else wait_vmcnt<(S - 2) * (NPARTS - 1) + (PA > C::A_PER_WAVE - 1 ? PA - 1 : PA)>();
+    __syncthreads();
+    read_sub(S0{}, 0);
+    for (int kt = 0; kt < nk - 1; kt++) {
+      // substep 0 of stage kt, with the second part of stage kt+S-1's loads
+      mma_sub(S0{}, PAc{}, std::integral_constant<int, NPARTS>{}, min(kt + S - 1, nk - 1), (kt + S - 1) % S);
+      read_sub(S1{}, kt % S);
+      // stage kt+1 has landed once this wave's loads of it are done (the S-2 younger
+      // stages may stay outstanding) and every wave has passed the barrier
       if (a_full) wait_vmcnt<(S - 2) * NPARTS>();
       else wait_vmcnt<(S - 2) * (NPARTS - 1)>();
       __syncthreads();
-      compute_na(na_tag, kt % S, min(kt + S - 1, nk - 1), (kt + S - 1) % S);
+      read_sub(S0{}, (kt + 1) % S);
+      __builtin_amdgcn_sched_barrier(0);
+      // substep 1 of stage kt, with the first part of stage kt+S's loads into stage kt's buffer
+      mma_sub(S1{}, S0{}, PAc{}, min(kt + S, nk - 1), kt % S);
     }
+    // the last stage: no further stage to wait for, read or load
+    mma_sub(S0{}, S0{}, S0{}, 0, 0);
+    read_sub(S1{}, (nk - 1) % S);
+    mma_sub(S1{}, S0{}, S0{}, 0, 0);
     wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
   };
   switch (__builtin_amdgcn_readfirstlane(mb_active)) {
