@@ -150,13 +150,18 @@ def _e2e(cfg, step=0, b=None, T=None):
 
 # V3-shaped routers outside the lane-major selection's fast cases: 4 groups of 64 with the
 # top-3 group score (the split-K logits, then the one-expert-per-lane selection on the slice
-# partials), and no group limit (the lane-major selection with G = 1)
+# partials), and no group limit (the lane-major selection with G = 1). Two other widths take
+# the split-K logits through other slicings of d: 1024 over 8 slices of one 128-element chunk
+# (two stages each) for 300 tokens, 384 over 3 slices for 1000 tokens (a ragged token block).
 _ROUTER_VARIANTS = {"v3_g4q3": dict(n_groups=4, topk_groups=2, group_topk=3),
-                    "v3_g1": dict(n_groups=1, topk_groups=1, group_topk=8)}
+                    "v3_g1": dict(n_groups=1, topk_groups=1, group_topk=8),
+                    "v3_d1024": dict(d=1024),
+                    "v3_d384": dict(d=384)}
 
 
 @pytest.mark.parametrize("name,T", [("tiny", None), ("mid", None), ("v3", None), ("fp8", 2048),
-                                    ("skew", 4096), ("v3", 77), ("v3_g4q3", 2048), ("v3_g1", 1000)])
+                                    ("skew", 4096), ("v3", 77), ("v3_g4q3", 2048), ("v3_g1", 1000),
+                                    ("v3_d1024", 300), ("v3_d384", 1000)])
 def test_end_to_end_routing(name, T):
     cfg = get_config("v3").with_(**_ROUTER_VARIANTS[name]) if name in _ROUTER_VARIANTS else get_config(name)
     r, s64, s32, kgap, ggap, idx, gate, counts, sout = _e2e(cfg, T=T)
