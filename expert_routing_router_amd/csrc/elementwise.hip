@@ -1,6 +1,7 @@
 // Memory-bound kernels of the layer: the gated combine, the bias update and
 // the FP8 quantisers.
 #include "common.h"
+#include "fp8_codec.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -234,26 +235,6 @@ hipError_t launch_update_bias(const int32_t* counts, float* b, int n_routed, lon
 }
 
 // ---------------------------------------------------------------- FP8 quantisers
-// OCP E4M3FN encoding of an fp32 value: round to nearest even on 3 mantissa
-// bits, subnormal step 2^-9, saturation to +-448 (no infinities).
-__device__ __forceinline__ uint32_t e4m3_encode(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float ax = fabsf(x);
-  if (ax != ax) return sign | 0x7Fu;
-  if (ax >= 448.0f) return sign | 0x7Eu;
-  if (ax < 0.015625f) {                                  // below 2^-6: multiples of 2^-9
-    const uint32_t m = (uint32_t)rintf(ax * 512.0f);     // exact scaling, ties to even
-    return sign | m;                                     // m == 8 is the code of 2^-6
-  }
-  int e = (int)((u >> 23) & 0xFFu) - 127;                // -6 .. 8
-  uint32_t m3 = (u >> 20) & 7u;
-  const uint32_t rem = u & 0xFFFFFu;
-  if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) m3++;
-  if (m3 == 8u) { m3 = 0; e++; }
-  return sign | ((uint32_t)(e + 7) << 3) | m3;
-}
-
 __device__ __forceinline__ float load_src(const void* p, size_t i, bool bf) {
   return bf ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
 }
@@ -301,12 +282,8 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
   m = fmaxf(m, swz_xor<4>(m));
   m = fmaxf(m, swz_xor<8>(m));
   const float sc = m == 0.0f ? 1.0f : m / 448.0f;
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    lo |= e4m3_encode(v[i] / sc) << (8 * i);
-    hi |= e4m3_encode(v[4 + i] / sc) << (8 * i);
-  }
+  const uint32_t lo = e4m3_encode4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+  const uint32_t hi = e4m3_encode4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
   *(uint2*)(q + (size_t)r * cols + c0) = make_uint2(lo, hi);
   if (sub == 0) scale[TS ? (size_t)(c0 / 128) * rows + r : (size_t)r * tpr + c0 / 128] = sc;
 }

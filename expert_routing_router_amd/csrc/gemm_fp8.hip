@@ -10,6 +10,7 @@
 // The per-row activation scales of the tile are staged in LDS beside A.
 // Tiling, ragged segments and the SwiGLU epilogue follow the bf16 kernel.
 #include "common.h"
+#include "fp8_codec.h"
 #include "lds_dma.h"
 #include "tile_order.h"
 #include "moe_internal.h"
@@ -280,7 +281,7 @@ struct F8DmaCfg {
   static constexpr int SA_WAVES = BM / 64;           // waves that load 64 row scales each
   static_assert(B_LOADS % 8 == 0 && SA_WAVES <= 8, "loads split over 8 waves");
   static_assert(STAGE % 16 == 0, "stage alignment");
-  static_assert(BYTES + 2 * F8_MAX_KB * 4 + 2048 <= 160 * 1024, "LDS budget");
+  static_assert(BYTES + 2 * F8_MAX_KB * 4 + 2048 + 4 * BM * 4 <= 160 * 1024, "LDS budget");
 };
 
 template <int MB, bool SWIGLU>
@@ -486,7 +487,45 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
 
   // Each lane holds one activation row (its column in the MFMA layout) and, per block,
   // 16 weight rows 8q + 4*khalf + e: 4 consecutive output columns per q.
-  // GEMM1 writes H in fp32 (re-quantised per 1x128 tile next); GEMM2 writes Y in bf16.
+  if constexpr (SWIGLU) {
+    if (a.out_q) {
+      // H quantised here, in 1x128 tiles along I: a tile is this n-tile's 128 H columns of
+      // one row, 32 per wave wn and 16 per lane. Its amax over the lane pair (khalf) and
+      // the 4 waves goes through LDS; scale and codes as the activation quantiser makes them.
+      __shared__ float samax[4][BM];
+      // H values once, for every block (inactive ones hold zeros): the accumulators die here
+      float hv[MB][16];
+#pragma unroll
+      for (int i = 0; i < MB; i++) {
+        float m = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          hv[i][r] = silu_mul(acc[i][0][r], acc[i][1][r]);
+          m = fmaxf(m, fabsf(hv[i][r]));
+        }
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (i < mb_active && khalf == 0) samax[wn][(2 * i + wm) * 32 + l32] = m;
+      }
+      __syncthreads();
+      const int tpr = a.N / 128;
+#pragma unroll
+      for (int i = 0; i < MB; i++) {
+        const int row = (2 * i + wm) * 32 + l32;
+        if (i < mb_active && row < mvalid && (unsigned)(row0 + row) < (unsigned)a.rows_bound) {
+          const float m = fmaxf(fmaxf(samax[0][row], samax[1][row]), fmaxf(samax[2][row], samax[3][row]));
+          const float sc = m == 0.0f ? 1.0f : m / 448.0f;
+          uint8_t* qrow = a.out_q + (size_t)(row0 + row) * a.N + ntile * HN + wn * 32 + 4 * khalf;
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            *(uint32_t*)(qrow + 8 * q) = e4m3_encode4(hv[i][4 * q] / sc, hv[i][4 * q + 1] / sc,
+                                                      hv[i][4 * q + 2] / sc, hv[i][4 * q + 3] / sc);
+          if (wn == 0 && khalf == 0) a.out_qs[(size_t)(row0 + row) * tpr + ntile] = sc;
+        }
+      }
+      return;
+    }
+  }
+  // Without out_q, GEMM1 writes H in fp32; GEMM2 writes Y in bf16.
 #pragma unroll
   for (int i = 0; i < MB; i++) {
     const int row = (2 * i + wm) * 32 + l32;
@@ -574,6 +613,16 @@ hipError_t launch_pack_blocked_f8(const uint8_t* src, uint8_t* dst, int n_mat, i
 hipError_t launch_gemm_fp8(const GemmArgs& a, bool swiglu, int bm, hipStream_t s) {
   // K-blocked weights only on the LDS-DMA kernel; blocked activations are a bf16 feature
   if (a.x_blocked || a.out_blocked || (a.w_blocked && bm != 256 && bm != 320)) return hipErrorInvalidValue;
+  if (a.out_q && (!swiglu || !a.out_qs || a.N % 128)) return hipErrorInvalidValue;
+  if (a.out_q && bm == 192) {
+    // the 192-row kernel writes fp32 H (a.out); it is quantised by the activation quantiser
+    GemmArgs b = a;
+    b.out_q = nullptr;
+    b.out_qs = nullptr;
+    hipError_t e = launch_fp8_t<3, true>(b, s);
+    if (e != hipSuccess) return e;
+    return launch_quant_act(a.out, MOE_F32, a.rows_bound, a.N, nullptr, a.out_q, a.out_qs, s);
+  }
   // 256- and 320-row tiles: the LDS-DMA kernel (needs the down GEMM's width a multiple of 256)
   if (bm == 256) return swiglu ? launch_fp8_dma<4, true>(a, s) : launch_fp8_dma<4, false>(a, s);
   if (bm == 320) return swiglu ? launch_fp8_dma<5, true>(a, s) : launch_fp8_dma<5, false>(a, s);

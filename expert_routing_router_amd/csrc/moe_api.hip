@@ -403,16 +403,15 @@ static int run_ffn(const moe_desc_t* d, int inter, const void* x, long x_rows, c
                           rows_bound);
   g1.w1 = w13b; g1.ws1 = s13b; g1.n_first = n_first;
   g1.w_blocked = blocked;
-  g1.out_blocked = blocked && !f8;             // FP8: H is quantised row-major by its own pass
+  g1.out_blocked = blocked && !f8;
+  if (f8) {                                    // FP8: H comes out quantised (row-major codes, 1x128 scales)
+    g1.out_q = qh;
+    g1.out_qs = sh;
+  }
   MOE_TRY(launch_gemm_swiglu(g1, dt, bm, s));
   prof_mark(MOE_STAGE_GEMM1, s);
-  const void* x2 = H;
-  const float* xs2 = nullptr;
-  if (f8) {
-    MOE_TRY(launch_quant_act(H, MOE_F32, rows_bound, inter, nullptr, qh, sh, s));
-    x2 = qh;
-    xs2 = sh;
-  }
+  const void* x2 = f8 ? (const void*)qh : H;
+  const float* xs2 = f8 ? sh : nullptr;
   GemmArgs g2 = gemm_args(x2, rows_bound, xs2, nullptr, offsets, mtile, n_seg, w2, s2, ws2, ss2, Y, d->d, inter,
                           rows_bound);
   g2.w1 = w2b; g2.ws1 = s2b; g2.n_first = n_first;

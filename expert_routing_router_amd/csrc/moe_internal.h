@@ -85,6 +85,10 @@ struct GemmArgs {
   int w_blocked = 0;          // w0/w1: moe_pack_expert_weights layout
   int x_blocked = 0;          // x: per m-tile (mtile_prefix numbering) blocks of BM rows, K = this GEMM's K
   int out_blocked = 0;        // SwiGLU output H written in the x_blocked layout of the down GEMM
+  // FP8 SwiGLU GEMM: when out_q is set, H goes out as E4M3 codes out_q [rows][N] with 1x128
+  // scales out_qs [rows][N/128], quantised exactly as launch_quant_act does from fp32 H
+  uint8_t* out_q = nullptr;
+  float* out_qs = nullptr;
 };
 // bf16 weights [n_mat][rows][K] -> K-blocked tiles of 256 rows; swiglu_i > 0: rows = 2*swiglu_i and
 // tile t holds gate rows t*128.. and up rows swiglu_i + t*128..

@@ -141,3 +141,31 @@ def test_quant_act_bit_exact_special_tiles(src_dtype):
     cq, cs = nx.quant_act_1x128(x32)
     assert np.array_equal(host(s), cs)
     assert np.array_equal(host(q), cq)
+
+
+def test_quant_act_codes_dense_sweep():
+    """The activation quantiser's E4M3 codes against the oracle's encoder over a dense sweep of
+    fp32 values: every 509th bit pattern from 0 to 448 and every 511th from -0 to -448 (E4M3
+    subnormals, fp32 denormals and signed zeros included), plus each pair of neighbouring codes'
+    midpoint and the fp32 values just either side of it. Each 128-value tile holds 448 first,
+    so its scale is exactly 1 and the codes are those of the values themselves."""
+    pos = np.arange(0, 0x43E00001, 509, dtype=np.uint64).astype(np.uint32)
+    neg = (np.arange(0, 0x43E00001, 511, dtype=np.uint64) | 0x80000000).astype(np.uint32)
+    grid = nx.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))            # every finite non-negative code
+    mids = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(0))])
+    vals = np.concatenate([pos.view(np.float32), neg.view(np.float32), near, -near])
+    rows = -(-vals.size // 127)
+    body = np.zeros(rows * 127, dtype=np.float32)
+    body[:vals.size] = vals
+    x = np.concatenate([np.full((rows, 1), 448.0, dtype=np.float32), body.reshape(rows, 127)], axis=1)
+    q = torch.empty((rows, 128), dtype=torch.uint8, device="cuda")
+    s = torch.empty((rows, 1), dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8(M.MOE_QUANT_ACT_1x128, dev(x, "f32"), rows, 128, q, s)
+    torch.cuda.synchronize()
+    assert (host(s) == 1.0).all()
+    want = nx.e4m3_encode(x)
+    got = host(q)
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, "first mismatches: %s" % [(float(x[r, c]), int(got[r, c]), int(want[r, c]))
+                                                       for r, c in zip(bad[0][:5], bad[1][:5])]
