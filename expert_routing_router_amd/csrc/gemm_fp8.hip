@@ -326,7 +326,15 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
   // ---- per-lane global offsets of this wave's loads (fixed over K)
   const int lrow = lane >> 2;                                  // row within a 16-row load
   const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);           // chunk its slot holds
-  const i32x4 xr = rsrc_words(a.x, a.x_rows * (long)K);
+  // K-blocked activation codes (the down GEMM's H, written so by the gate/up GEMM's epilogue):
+  // per m-tile, per 64-element step, the tile's BM rows with the chunk swizzle applied, so
+  // load i of a stage reads its kilobyte i; rows past mvalid hold padding, whose products
+  // only reach output rows that are not stored
+  const bool xblk = a.x_blocked;
+  const int mt = sprefix[seg] + mtile;
+  const i32x4 xr = xblk ? rsrc_words((const uint8_t*)a.x + (size_t)mt * BM * K, (long)BM * K)
+                        : rsrc_words(a.x, a.x_rows * (long)K);
+  const int astep = xblk ? BM * F8_SK : F8_SK;
   const i32x4 sr = rsrc_words(a.x_scale, a.x_rows * (long)KB * 4);
   // K-blocked weights (moe_pack_expert_weights): the tile's 256 rows per 64-element step are
   // one contiguous 16 KB with this kernel's chunk swizzle applied, so load i of a stage reads
@@ -343,7 +351,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
     const int r = (wave + 8 * i) * 16 + lrow;
     const int rr = min(max(row0 + min(r, mvalid - 1), 0), a.rows_bound - 1);   // in range for any offsets
     const int src = a.row_index ? a.row_index[rr] : rr;
-    aoff[i] = r < mvalid ? src * K + lchunk * 16 : kOutOfRange;
+    aoff[i] = xblk ? (wave + 8 * i) * 1024 + lane * 16 : r < mvalid ? src * K + lchunk * 16 : kOutOfRange;
   }
   int soff_row;
   {
@@ -367,7 +375,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
     const uint32_t sbase = lds0 + buf * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::A_MAX; i++)
-      if (i < C::A_MIN || n_a == C::A_MAX) dma_b128(xr, aoff[i], ks * F8_SK, sbase + (wave + 8 * i) * 1024);
+      if (i < C::A_MIN || n_a == C::A_MAX) dma_b128(xr, aoff[i], ks * astep, sbase + (wave + 8 * i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::B_PER_WAVE; i++)
       // K-blocked gate/up weights are read with the non-temporal hint (measured: it helps the
@@ -514,11 +522,20 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
         if (i < mb_active && row < mvalid && (unsigned)(row0 + row) < (unsigned)a.rows_bound) {
           const float m = fmaxf(fmaxf(samax[0][row], samax[1][row]), fmaxf(samax[2][row], samax[3][row]));
           const float sc = m == 0.0f ? 1.0f : m / 448.0f;
-          uint8_t* qrow = a.out_q + (size_t)(row0 + row) * a.N + ntile * HN + wn * 32 + 4 * khalf;
+          // column c = ntile*128 + wn*32 + 8q + 4khalf of H: row-major, or K-blocked for the down
+          // GEMM (m-tile mt, step c/64, tile row `row`, 16-byte chunk (c%64)/16 at its swizzled slot)
+          const int c0 = ntile * HN + wn * 32 + 4 * khalf;
+          uint8_t* qrow = a.out_blocked ? a.out_q + (size_t)mt * BM * a.N + (size_t)row * F8_SK
+                                        : a.out_q + (size_t)(row0 + row) * a.N;
 #pragma unroll
-          for (int q = 0; q < 4; q++)
-            *(uint32_t*)(qrow + 8 * q) = e4m3_encode4(hv[i][4 * q] / sc, hv[i][4 * q + 1] / sc,
-                                                      hv[i][4 * q + 2] / sc, hv[i][4 * q + 3] / sc);
+          for (int q = 0; q < 4; q++) {
+            const int c = c0 + 8 * q;
+            const int at = a.out_blocked
+                ? (c / F8_SK) * BM * F8_SK + ((((c % F8_SK) >> 4) ^ ((row >> 2) & 3)) << 4) + (c & 15)
+                : c;
+            *(uint32_t*)(qrow + at) = e4m3_encode4(hv[i][4 * q] / sc, hv[i][4 * q + 1] / sc,
+                                                   hv[i][4 * q + 2] / sc, hv[i][4 * q + 3] / sc);
+          }
           if (wn == 0 && khalf == 0) a.out_qs[(size_t)(row0 + row) * tpr + ntile] = sc;
         }
       }
@@ -612,7 +629,12 @@ hipError_t launch_pack_blocked_f8(const uint8_t* src, uint8_t* dst, int n_mat, i
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, bool swiglu, int bm, hipStream_t s) {
   // K-blocked weights only on the LDS-DMA kernel; blocked activations are a bf16 feature
-  if (a.x_blocked || a.out_blocked || (a.w_blocked && bm != 256 && bm != 320)) return hipErrorInvalidValue;
+  // blocked activation codes: the down GEMM reads them (x_blocked), the gate/up GEMM's fused
+  // quantisation writes them (out_blocked), both on the LDS-DMA kernel (256- or 320-row tiles)
+  const bool dma = bm == 256 || bm == 320;
+  if ((a.x_blocked && (swiglu || !dma || a.row_index)) || (a.out_blocked && (!swiglu || !dma || !a.out_q)) ||
+      (a.w_blocked && !dma))
+    return hipErrorInvalidValue;
   if (a.out_q && (!swiglu || !a.out_qs || a.N % 128)) return hipErrorInvalidValue;
   if (a.out_q && bm == 192) {
     // the 192-row kernel writes fp32 H (a.out); it is quantised by the activation quantiser

@@ -169,11 +169,13 @@ static size_t route_scratch(const moe_desc_t* d) {
 static bool fused_shared(const moe_desc_t* d) { return d->n_shared == 0 || d->inter == d->inter_shared; }
 
 // rows of H: bf16 experts may store H K-blocked (each m-tile padded to its tile
-// height, at most kMaxTileRows), for the routed and shared passes together
+// height, at most kMaxTileRows), for the routed and shared passes together; FP8
+// experts store H's codes that way (qh_rows) and H itself row-major
 constexpr size_t kMaxTileRows = 320;
 static size_t h_rows(const moe_desc_t* d, size_t rows, size_t n_seg) {
   return d->expert_dtype == MOE_BF16 ? rows + (n_seg + 1) * kMaxTileRows : rows;
 }
+static size_t qh_rows(size_t rows, size_t n_seg) { return rows + (n_seg + 1) * kMaxTileRows; }
 
 // K-blocked weights apply to bf16 and FP8 experts whose products all take the LDS-DMA kernels
 // (FP8: 256-row tiles, which gemm_bm picks when d % 256 == 0)
@@ -213,7 +215,7 @@ static Ws layout(const moe_desc_t* d, bool capacity = false) {
   if (d->expert_dtype == MOE_FP8_E4M3) {
     w.qu = take(T * d->d);
     w.su = take(T * (d->d / 128) * 4);
-    w.qh = take(R * Imax);
+    w.qh = take(qh_rows(R, n_seg) * Imax);
     w.sh = take(R * (Imax / 128) * 4);
   } else {
     w.qu = w.su = w.qh = w.sh = 0;
@@ -403,8 +405,8 @@ static int run_ffn(const moe_desc_t* d, int inter, const void* x, long x_rows, c
                           rows_bound);
   g1.w1 = w13b; g1.ws1 = s13b; g1.n_first = n_first;
   g1.w_blocked = blocked;
-  g1.out_blocked = blocked && !f8;
-  if (f8) {                                    // FP8: H comes out quantised (row-major codes, 1x128 scales)
+  g1.out_blocked = blocked;
+  if (f8) {                                    // FP8: H comes out quantised (codes, 1x128 scales)
     g1.out_q = qh;
     g1.out_qs = sh;
   }
@@ -416,7 +418,7 @@ static int run_ffn(const moe_desc_t* d, int inter, const void* x, long x_rows, c
                           rows_bound);
   g2.w1 = w2b; g2.ws1 = s2b; g2.n_first = n_first;
   g2.w_blocked = blocked;
-  g2.x_blocked = blocked && !f8;
+  g2.x_blocked = blocked;
   MOE_TRY(launch_gemm_down(g2, dt, bm, s));
   prof_mark(MOE_STAGE_GEMM2, s);
   return MOE_OK;
@@ -619,7 +621,7 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
     if (d->expert_dtype != MOE_F32) MOE_TRY(launch_mtile_prefix(offs_s, Ns, bms, mtile_s, s));
     uint8_t* Hs = H + h_rows(d, TK, N) * (d->inter > d->inter_shared ? d->inter : d->inter_shared) * hy;
     uint8_t* Ys = Y + (size_t)TK * d->d * yy;
-    uint8_t* qhs = f8 ? qh + (size_t)TK * d->inter : nullptr;
+    uint8_t* qhs = f8 ? qh + qh_rows(TK, N) * (d->inter > d->inter_shared ? d->inter : d->inter_shared) : nullptr;
     float* shss = f8 ? shs + (size_t)TK * (d->inter / 128) : nullptr;
     int st2 = run_ffn(d, d->inter_shared, x, T, xs, row_token + TK, offs_s, mtile_s, Ns, Ns * T, w13s,
                       w->w13_shared_scale, w13s, w->w13_shared_scale, w2s, w->w2_shared_scale,
