@@ -227,8 +227,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs a) {
 // 128- and 64-row tiles): all but one are in flight while one is multiplied,
 // so each CU keeps ~108 KB of loads outstanding instead of one K step's worth.
 //
-// A stage holds RB bytes per row (RB = 64: K=32 stages; RB = 128: two K=64
-// stages, kept as an alternative), CPR = RB/16 chunks of 16 bytes. One load instruction of a
+// A stage holds RB = 64 bytes per row (K=32 stages: two 16-element k-substeps,
+// which the operand read-ahead of the kernel needs), CPR = RB/16 chunks of 16 bytes. One load instruction of a
 // wave fills one 1 KB block of RPB = 1024/RB rows; lane l writes block byte
 // 16*l, i.e. row l/CPR, slot l%CPR, and fetches the chunk
 // c = slot ^ ((row >> SH) & (CPR-1)), SH = log2(16/CPR). The MFMA operand
@@ -242,12 +242,11 @@ struct DmaCfg {
   static constexpr int BK = RB / 2;                     // bf16 elements per stage row
   static constexpr int CPR = RB / 16;
   static constexpr int RPB = 1024 / RB;
-  static constexpr int SH = RB == 64 ? 2 : 1;
+  static constexpr int SH = 2;
   static constexpr int SUB = RB / 32;                   // 16-element k-substeps per stage
   // as many K=32 stages as the LDS holds (up to 7: small-row tiles keep more weight bytes in flight)
-  static constexpr int STAGES = RB == 64 ? ((160 * 1024 - 2048) / ((BM + BN) * RB) < 7
-                                                ? (160 * 1024 - 2048) / ((BM + BN) * RB) : 7)
-                                         : 2;
+  static constexpr int STAGES = (160 * 1024 - 2048) / ((BM + BN) * RB) < 7
+                                    ? (160 * 1024 - 2048) / ((BM + BN) * RB) : 7;
   static constexpr int A_BLOCKS = BM / RPB;             // 1 KB blocks per stage
   static constexpr int B_BLOCKS = BN / RPB;
   static constexpr int A_BYTES = BM * RB;
@@ -256,7 +255,7 @@ struct DmaCfg {
   static constexpr int A_PER_WAVE = (A_BLOCKS + 7) / 8;  // waves below A_BLOCKS % 8 take one more
   static constexpr int A_EXTRA = A_BLOCKS % 8;
   static constexpr int B_PER_WAVE = B_BLOCKS / 8;
-  static_assert(RB == 64 || RB == 128, "stage row bytes");
+  static_assert(RB == 64, "stage row bytes");
   static_assert(B_BLOCKS % 8 == 0, "B blocks split evenly over 8 waves");
   static_assert(BYTES <= 160 * 1024 - 2048, "LDS budget");
 };
@@ -559,12 +558,9 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-#ifndef GEMM_DMA_RB
-#define GEMM_DMA_RB 64
-#endif
 template <int MB, bool SWIGLU>
 static hipError_t launch_bf16_dma(const GemmArgs& a, hipStream_t s) {
-  constexpr int RB = GEMM_DMA_RB;
+  constexpr int RB = 64;
   using C = DmaCfg<MB, RB>;
   const int n_tiles = SWIGLU ? a.N / (C::BN / 2) : a.N / C::BN;
   const long mtiles_bound = (long)a.rows_bound / C::BM + a.n_seg;
