@@ -248,11 +248,12 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
 //
 // The MFMA takes the weight rows as its first operand and the activation rows
 // as its second, so each lane's 16 results belong to one activation row (its
-// column) and 16 rows of one 32-row weight block, which share one weight
-// scale: the fold of a 64-wide partial p is acc += p * (s_act * s_w) with one
-// scale product per lane and block. (The pages promote every 128 elements;
-// folding each half with the same block scale gives the same sum up to fp32
-// rounding.)
+// column) and 16 rows of one 32-row weight block, which share one scale
+// s = s_act * s_w per 128-element block. The accumulator is kept in units of
+// the current block's s: at each block's first stage it is multiplied by
+// s_prev / s, and the MFMAs of both 64-element stages accumulate into it
+// directly. The sum is the pages' promotion every 128 elements,
+// sum_kb s_kb * p_kb, up to fp32 rounding of the ratios.
 //
 // A stage row is 64 bytes = 4 chunks of 16; one load instruction of a wave
 // fills 16 rows (1 KB): lane l writes row l>>2, slot l&3 and fetches chunk
@@ -414,18 +415,30 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
   // which staged weight-scale row each of this wave's two weight blocks uses
   const int wsel0 = SWIGLU ? 0 : (wn >> 1), wsel1 = SWIGLU ? 1 : (wn >> 1);
 
-  // One stage: per 32x32 block one MFMA into a fresh fp32 partial, then
-  // acc += partial * (s_act[this lane's row] * s_w[block]). The blocks are
-  // software-pipelined: each block's MFMA is issued before the fold of the
-  // block before it, so the matrix core and the VALU work side by side (with
-  // one partial register set the fold and the next MFMA would serialise).
-  auto compute_na = [&](auto na_tag, int buf, int ks) __attribute__((always_inline)) {
+  // Each accumulator holds its block's sum in units of the current 128-block's
+  // scale s = s_act[this lane's row] * s_w[block]: acc = sum_kb p_kb * s_kb / s_cur.
+  // At the first 64-element stage of a 128-block it is rescaled by s_prev / s_cur
+  // (one reciprocal and 16 multiplies per lane and block); then both stages'
+  // MFMAs accumulate into it directly, and the epilogue multiplies by the last
+  // block's s. This is the pages' fp32 promotion, sum_kb s_kb * p_kb, with the
+  // scale applied once per 128 elements instead of once per 64-element partial,
+  // and no partial registers. A zero scale (no such tile comes out of the
+  // quantisers; rows past the segment read zero scales) keeps the previous one.
+  float sprev[MB][2];
+#pragma unroll
+  for (int i = 0; i < MB; i++) sprev[i][0] = sprev[i][1] = 1.0f;
+  auto compute_na = [&](auto na_tag, auto first_tag, int buf, int ks) __attribute__((always_inline)) {
     constexpr int NA = decltype(na_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
     if constexpr (NA > 0) {
       const uint8_t* A = lds + buf * C::STAGE;
       const uint8_t* B = A + C::A_BYTES;
       const float* SA = (const float*)(B + C::B_BYTES);
-      const float swj[2] = {ssw[wsel0][ks >> 1], ssw[wsel1][ks >> 1]};
+      float swj[2] = {1.0f, 1.0f};
+      if constexpr (FIRST) {
+        swj[0] = ssw[wsel0][ks >> 1];
+        swj[1] = ssw[wsel1][ks >> 1];
+      }
       i32x8 bfr[2];
 #pragma unroll
       for (int j = 0; j < 2; j++) {
@@ -433,36 +446,28 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
         const i32x4 hi = *(const i32x4*)(B + bro[j] + roff1);
         bfr[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      auto load_a = [&](int i, i32x8& afr, float& sa) __attribute__((always_inline)) {
+      static_for<NA>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
         const int mrow = (2 * i + wm) * 32;
         const i32x4 lo = *(const i32x4*)(A + mrow * F8_SK + roff0);
         const i32x4 hi = *(const i32x4*)(A + mrow * F8_SK + roff1);
-        afr = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        sa = SA[mrow + l32];
-      };
-      // cbsz = blgp = 0: both operands E4M3; scale exponents 127 = 2^0
-      auto mma = [&](const i32x8& w, const i32x8& x) __attribute__((always_inline)) {
-        f32x16 z;
+        const i32x8 afr = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (FIRST) {
+          const float sa = SA[mrow + l32];
 #pragma unroll
-        for (int r = 0; r < 16; r++) z[r] = 0.f;
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, z, 0, 0, 0, 127, 0, 127);
-      };
-      auto fold = [&](f32x16& c, const f32x16& p, float sc) __attribute__((always_inline)) {
+          for (int j = 0; j < 2; j++) {
+            const float sc = sa * swj[j];
+            const float se = sc != 0.0f ? sc : sprev[i][j];
+            const float r = sprev[i][j] * __builtin_amdgcn_rcpf(se);
+            sprev[i][j] = se;
 #pragma unroll
-        for (int r = 0; r < 16; r++) c[r] = fmaf(p[r], sc, c[r]);
-      };
-      i32x8 afr;
-      float sa;
-      load_a(0, afr, sa);
-      f32x16 p0 = mma(bfr[0], afr);
-      static_for<NA>([&](auto I) __attribute__((always_inline)) {
-        constexpr int i = decltype(I)::value;
-        const f32x16 p1 = mma(bfr[1], afr);             // block (i, 1)
-        const float sc0 = sa * swj[0], sc1 = sa * swj[1];
-        if constexpr (i + 1 < NA) load_a(i + 1, afr, sa);
-        fold(acc[i][0], p0, sc0);                         // block (i, 0) while (i, 1) runs
-        if constexpr (i + 1 < NA) p0 = mma(bfr[0], afr);   // block (i + 1, 0)
-        fold(acc[i][1], p1, sc1);
+            for (int e = 0; e < 16; e++) acc[i][j][e] *= r;
+          }
+        }
+        // cbsz = blgp = 0: both operands E4M3; scale exponents 127 = 2^0
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], afr, acc[i][j], 0, 0, 0, 127, 0, 127);
       });
     }
   };
@@ -476,11 +481,16 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
     issue(0, 0);
     issue(min(1, last), 1);
     issue(min(2, last), 2);
-    for (int ks = 0; ks < KS; ks++) {
+    // K % 128 == 0: the stages come in pairs, the first of each pair rescales
+    for (int ks = 0; ks < KS; ks += 2) {
       wait_stage();
       __syncthreads();
       issue(min(ks + 3, last), (ks + 3) & 3);
-      compute_na(na_tag, ks & 3, ks);
+      compute_na(na_tag, std::true_type{}, ks & 3, ks);
+      wait_stage();
+      __syncthreads();
+      issue(min(ks + 4, last), (ks + 4) & 3);
+      compute_na(na_tag, std::false_type{}, (ks + 1) & 3, ks + 1);
     }
     wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
   };
@@ -492,6 +502,13 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
     case 4: k_loop(std::integral_constant<int, (MB >= 4 ? 4 : MB)>{}); break;
     default: k_loop(std::integral_constant<int, MB>{}); break;
   }
+  // back from units of the last 128-block's scale
+#pragma unroll
+  for (int i = 0; i < MB; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) acc[i][j][e] *= sprev[i][j];
 
   // Each lane holds one activation row (its column in the MFMA layout) and, per block,
   // 16 weight rows 8q + 4*khalf + e: 4 consecutive output columns per q.
