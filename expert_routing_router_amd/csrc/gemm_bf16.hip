@@ -406,8 +406,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
       static_for<MB>([&](auto q_tag) __attribute__((always_inline)) {
         constexpr int q = decltype(q_tag)::value;
         if constexpr (q < NA) {
-          acc[q][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[SS][q], rb[SS][0], acc[q][0], 0, 0, 0);
-          acc[q][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[SS][q], rb[SS][1], acc[q][1], 0, 0, 0);
+          // weight rows first: each lane's results are 4-column runs of one activation row
+          acc[q][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[SS][0], ra[SS][q], acc[q][0], 0, 0, 0);
+          acc[q][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[SS][1], ra[SS][q], acc[q][1], 0, 0, 0);
           if constexpr ((q + 1) % PER == 0 && (q + 1) / PER < NP) {
             __builtin_amdgcn_sched_barrier(0);
             issue_part(std::integral_constant<int, P0 + (q + 1) / PER>{}, kti, bufi);
@@ -462,27 +463,37 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
     default: k_loop(std::integral_constant<int, MB>{}); break;
   }
 
+  // The MFMA takes the weight rows as its first operand, so lane l holds activation row
+  // (block row + l32) and, in registers 4q..4q+3, the 4 output columns 8q + 4*khalf + e of
+  // each 32-column n-block: every (q) is one 8-byte store of 4 bf16.
   uint16_t* out = (uint16_t*)a.out;
   // K-blocked H (SwiGLU only): this wave's 32 columns are one 32-element step of the down GEMM
   uint16_t* hblk = out + ((size_t)mt * (a.N / 32) + (ntile * HN + wn * 32) / 32) * BM * 32;
+  auto pack4 = [](float v0, float v1, float v2, float v3) __attribute__((always_inline)) {
+    return make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+  };
 #pragma unroll
   for (int i = 0; i < MB; i++) {
-    if (i < mb_active) {
+    const int row = (2 * i + wm) * 32 + l32;
+    if (i < mb_active && row < mvalid && (unsigned)(row0 + row) < (unsigned)a.rows_bound) {
+      uint16_t* orow = out + (size_t)(row0 + row) * a.N;
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-        if (row < mvalid && (unsigned)(row0 + row) < (unsigned)a.rows_bound) {
-          uint16_t* orow = out + (size_t)(row0 + row) * a.N;
-          if (SWIGLU && a.out_blocked) {
-            hblk[row * 32 + (((l32 >> 3) ^ ((row >> 2) & 3)) << 3) + (l32 & 7)] =
-                f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
-          } else if (SWIGLU) {
-            orow[ntile * HN + wn * 32 + l32] = f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
-          } else {
-            const int col = ntile * BN + wn * 64 + l32;
-            orow[col] = f32_to_bf16(acc[i][0][r]);
-            orow[col + 32] = f32_to_bf16(acc[i][1][r]);
-          }
+      for (int q = 0; q < 4; q++) {
+        const int c = 8 * q + 4 * khalf;
+        if (SWIGLU) {
+          const uint2 h = pack4(silu_mul(acc[i][0][4 * q], acc[i][1][4 * q]),
+                                silu_mul(acc[i][0][4 * q + 1], acc[i][1][4 * q + 1]),
+                                silu_mul(acc[i][0][4 * q + 2], acc[i][1][4 * q + 2]),
+                                silu_mul(acc[i][0][4 * q + 3], acc[i][1][4 * q + 3]));
+          // blocked: chunk q of the row at its swizzled slot, elements 4*khalf.. within it
+          uint16_t* dst = a.out_blocked ? hblk + row * 32 + ((q ^ ((row >> 2) & 3)) << 3) + 4 * khalf
+                                        : orow + ntile * HN + wn * 32 + c;
+          *(uint2*)dst = h;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; j++)
+            *(uint2*)(orow + ntile * BN + wn * 64 + j * 32 + c) =
+                pack4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         }
       }
     }
