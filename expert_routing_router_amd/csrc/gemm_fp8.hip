@@ -370,13 +370,16 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
   }
   const uint32_t lds0 = lds_addr(lds);
   const bool sa_wave = wave < C::SA_WAVES;
-  // loads per stage of this wave (wave-uniform): its waits count them
-  const int n_loads = n_a + C::B_PER_WAVE + (sa_wave ? 1 : 0);
   // Load P of this wave's share of stage ks into buffer buf: its A blocks, then its
   // B blocks, then (waves below SA_WAVES) the row scales of the stage's 128-block.
+  // Only the first stage of a 128-block reads the row scales (it rescales the
+  // accumulators), so only stages of even index load them: each of those loads
+  // gathers 64 separate 4-byte values. Of any two consecutive stages exactly one
+  // is even, which keeps the waits' counts the same for every stage.
   constexpr int NPARTS = C::A_MAX + C::B_PER_WAVE + 1;
-  auto issue_part = [&](auto p_tag, int ks, int buf) __attribute__((always_inline)) {
+  auto issue_part = [&](auto p_tag, auto sa_tag, int ks, int buf) __attribute__((always_inline)) {
     constexpr int P = decltype(p_tag)::value;
+    constexpr bool SA = decltype(sa_tag)::value;
     const uint32_t sbase = lds0 + buf * C::STAGE;
     if constexpr (P < C::A_MAX) {
       if (P < C::A_MIN || n_a == C::A_MAX) dma_b128(xr, aoff[P], ks * astep, sbase + (wave + 8 * P) * 1024);
@@ -387,17 +390,20 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
       if (SWIGLU && wblk) dma_b128_nt(wr, boff[Q], ks * bstep, sbase + C::A_BYTES + (wave + 8 * Q) * 1024);
       else dma_b128(wr, boff[Q], ks * bstep, sbase + C::A_BYTES + (wave + 8 * Q) * 1024);
     } else {
-      if (sa_wave) dma_b32(sr, soff_row, (ks >> 1) * 4, sbase + C::A_BYTES + C::B_BYTES + wave * 256);
+      if (SA && sa_wave) dma_b32(sr, soff_row, (ks >> 1) * 4, sbase + C::A_BYTES + C::B_BYTES + wave * 256);
     }
   };
-  auto issue = [&](int ks, int buf) __attribute__((always_inline)) {
-    static_for<NPARTS>([&](auto p) __attribute__((always_inline)) { issue_part(p, ks, buf); });
+  auto issue = [&](auto sa_tag, int ks, int buf) __attribute__((always_inline)) {
+    static_for<NPARTS>([&](auto p) __attribute__((always_inline)) { issue_part(p, sa_tag, ks, buf); });
   };
-  // this wave's loads of stage ks are done when at most those of the two later stages are pending
+  // this wave's loads of stage ks are done when at most those of the two later stages are
+  // pending: its A and B loads of both and one row-scale load (waves below SA_WAVES)
+  const int n_pend = 2 * (n_a + C::B_PER_WAVE) + (sa_wave ? 1 : 0);
   auto wait_stage = [&]() __attribute__((always_inline)) {
-    if (n_loads == 6) wait_vmcnt<12>();
-    else if (n_loads == 5) wait_vmcnt<10>();
-    else if (n_loads == 4) wait_vmcnt<8>();
+    if (n_pend == 11) wait_vmcnt<11>();
+    else if (n_pend == 10) wait_vmcnt<10>();
+    else if (n_pend == 9) wait_vmcnt<9>();
+    else if (n_pend == 8) wait_vmcnt<8>();
     else wait_vmcnt<0>();
   };
 
@@ -446,8 +452,10 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
                         __attribute__((always_inline)) {
     constexpr int NA = decltype(na_tag)::value;
     constexpr bool FIRST = decltype(first_tag)::value;
-    if constexpr (SPREAD) issue_part(std::integral_constant<int, 0>{}, ksl, bufl);
-    else issue(ksl, bufl);
+    // the loads go 3 stages ahead: the first stage of a pair loads an odd stage, the second an even
+    using SAL = std::integral_constant<bool, !FIRST>;
+    if constexpr (SPREAD) issue_part(std::integral_constant<int, 0>{}, SAL{}, ksl, bufl);
+    else issue(SAL{}, ksl, bufl);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NA > 0) {
       const uint8_t* A = lds + buf * C::STAGE;
@@ -489,14 +497,14 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], afr, acc[i][j], 0, 0, 0, 127, 0, 127);
         if constexpr (SPREAD && i + 1 < NPARTS) {
           __builtin_amdgcn_sched_barrier(0);
-          issue_part(std::integral_constant<int, i + 1>{}, ksl, bufl);
+          issue_part(std::integral_constant<int, i + 1>{}, SAL{}, ksl, bufl);
           __builtin_amdgcn_sched_barrier(0);
         }
       });
     }
     static_for<NPARTS>([&](auto p_tag) __attribute__((always_inline)) {
       constexpr int P = decltype(p_tag)::value;
-      if constexpr (SPREAD && P > NA) issue_part(p_tag, ksl, bufl);
+      if constexpr (SPREAD && P > NA) issue_part(p_tag, SAL{}, ksl, bufl);
     });
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -508,9 +516,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_dma_kernel(GemmArgs a) {
   // so every wave issues the same loads per stage.
   auto k_loop = [&](auto na_tag) __attribute__((always_inline)) {
     const int last = KS - 1;
-    issue(0, 0);
-    issue(min(1, last), 1);
-    issue(min(2, last), 2);
+    issue(std::true_type{}, 0, 0);
+    issue(std::false_type{}, min(1, last), 1);
+    issue(std::true_type{}, min(2, last), 2);
     // K % 128 == 0: the stages come in pairs, the first of each pair rescales
     for (int ks = 0; ks < KS; ks += 2) {
       wait_stage();
