@@ -169,3 +169,53 @@ def test_quant_act_codes_dense_sweep():
     bad = np.nonzero(got != want)
     assert bad[0].size == 0, "first mismatches: %s" % [(float(x[r, c]), int(got[r, c]), int(want[r, c]))
                                                        for r, c in zip(bad[0][:5], bad[1][:5])]
+
+
+def test_fp8_wide_scale_range_along_k():
+    """The FP8 grouped GEMMs with block scales that jump along K: each row's 128-column
+    activation tiles are scaled by 2^-10, 1 and 2^10 in turn (the phase shifting from row to
+    row) and the 128x128 weight blocks by 2^-5, 1 and 2^5 in a diagonal pattern, so consecutive
+    blocks' scale products differ by up to 2^30. The kernel keeps each accumulator in units of
+    the current block's scale and rescales it at every block; against oracle B (the same E4M3
+    recipe in fp64) the error must stay at the level of ordinary inputs. 320-row tiles (the
+    LDS-DMA kernel at MB = 5), d = 1024 (8 blocks along K for the gate/up GEMM), I = 512
+    (4 for the down GEMM)."""
+    rng = np.random.default_rng(11)
+    d, inter = 1024, 512
+    counts = [310, 1, 330, 650]
+    n, rows = len(counts), sum(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    kb = np.arange(d) // 128
+    x = rng.standard_normal((rows, d)).astype(np.float32)
+    x *= np.exp2(10.0 * (((kb[None, :] + np.arange(rows)[:, None]) % 3) - 1)).astype(np.float32)
+    w13, w2 = _weights(rng, n, inter, d, "f32")
+    w13 *= np.exp2(5.0 * (((np.arange(2 * inter)[:, None] // 128 + kb[None, :]) % 3) - 1)).astype(np.float32)
+    ki = np.arange(inter) // 128
+    w2 *= np.exp2(5.0 * (((np.arange(d)[:, None] // 128 + ki[None, :]) % 3) - 1)).astype(np.float32)
+    desc = M.make_desc(T=rows, d=d, n_routed=16, top_k=1, n_shared=0, inter=inter, in_dtype="bf16",
+                       router_dtype="f32", expert_dtype="fp8")
+    xb = gen.f32_to_bf16_bits(x)
+    xq = torch.empty((rows, d), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((rows, d // 128), dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8(M.MOE_QUANT_ACT_1x128, dev(xb, "bf16"), rows, d, xq, xs)
+    q13 = torch.empty((n, 2 * inter, d), dtype=torch.uint8, device="cuda")
+    s13 = torch.empty((n, 2 * inter // 128, d // 128), dtype=torch.float32, device="cuda")
+    q2 = torch.empty((n, d, inter), dtype=torch.uint8, device="cuda")
+    s2 = torch.empty((n, d // 128, inter // 128), dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8(M.MOE_QUANT_W_128x128, dev(w13.reshape(-1, d), "f32"), n * 2 * inter, d, q13, s13)
+    M.moe_quantize_fp8(M.MOE_QUANT_W_128x128, dev(w2.reshape(-1, inter), "f32"), n * d, inter, q2, s2)
+    ws = torch.empty(M.moe_expert_ffn_workspace_bytes(desc, n, inter, rows), dtype=torch.uint8, device="cuda")
+    y = torch.empty((rows, d), dtype=torch.bfloat16, device="cuda")
+    M.moe_expert_ffn(desc, n, inter, rows, xq, dev(offsets, "i32"), q13, q2, y, ws, x_scale=xs,
+                     w13_scale=s13, w2_scale=s2)
+    torch.cuda.synchronize()
+    got = host(y)
+    assert np.isfinite(got).all()
+    x64 = nx.bf16_to_f64(xb)
+    for e in range(n):
+        lo, hi = offsets[e], offsets[e + 1]
+        xq64 = nx.dequant_act(*nx.quant_act_1x128(x64[lo:hi].astype(np.float32)))
+        refB = ffn._expert(xq64, *ffn.fp8_weights(w13[e].astype(np.float64), w2[e].astype(np.float64)), True)
+        eB = rel_l2(got[lo:hi], refB)
+        log("fp8 wide scales, expert", e, "rows", hi - lo, "vs oracle B %.2e" % eB)
+        assert eB < 5e-3
