@@ -379,7 +379,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmArgs a) {
   // of substep 0 of the next iteration, before its barrier.
   static_assert(C::SUB == 2, "two 16-element k-substeps per stage");
   constexpr int S = C::STAGES;
-  constexpr int PA = NPARTS / 2;
+  // loads of stage kt+S issued right after the barrier (the rest go before the next one):
+  // the gate/up GEMM at MB = 5 issues 3 of its 5 there (measured at V3: 4.28 -> 4.23 ms
+  // against 2; 4 gained nothing), the down GEMM half (1 or 3 moved it within noise)
+  constexpr int PA = SWIGLU && NPARTS == 5 ? 3 : NPARTS / 2;
   const int nk = K / C::BK;
   auto k_loop = [&](auto na_tag) __attribute__((always_inline)) {
     constexpr int NA = decltype(na_tag)::value;
