@@ -4,9 +4,11 @@
 // pwwt.cn note section 3): E4M3 inputs, one scale per 1x128 activation tile
 // and per 128x128 weight block, partial sums promoted to fp32 every 128
 // K-elements. On gfx950 the MFMA already accumulates in fp32, so the promotion
-// becomes: for every 128-wide K block, two v_mfma 32x32x64 f8f6f4 produce a
-// fresh fp32 partial, which is folded into the accumulator as
-//   acc += partial * (s_act[row, kb] * s_w[nblock, kb]).
+// becomes a scale applied once per 128-wide K block of
+// acc = sum_kb partial_kb * (s_act[row, kb] * s_w[nblock, kb]): the register-staged
+// kernel below folds each block's fresh fp32 partial (two v_mfma 32x32x64
+// f8f6f4) into the accumulator; the LDS-DMA kernel keeps the accumulator in
+// units of the current block's scale and rescales it at each block.
 // The per-row activation scales of the tile are staged in LDS beside A.
 // Tiling, ragged segments and the SwiGLU epilogue follow the bf16 kernel.
 #include "common.h"
@@ -239,9 +241,9 @@ __global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp8_kernel(GemmArgs a) {
 
 // ---------------------------------------------------------------- LDS-DMA path
 // 8 waves (2 along M x 4 along N), tile 64*MB rows x 256 weight rows. A stage
-// holds 64 elements of K (half a scale block) of both operands and the tile
-// rows' activation scales of that stage's 128-element block; four stages in a
-// ring, three in flight while one is multiplied. Buffer loads write the E4M3
+// holds 64 elements of K (half a scale block) of both operands and, at the
+// first stage of each 128-element block, the tile rows' activation scales of
+// that block; four stages in a ring, three in flight while one is multiplied. Buffer loads write the E4M3
 // rows and the row scales straight into LDS. The two weight-block scales a
 // workgroup needs per K block (gate and up rows for SwiGLU, the two 128-row
 // halves of the tile for the down GEMM) are staged in LDS once, for all K.
