@@ -9,109 +9,14 @@ namespace moe {
 // ---------------------------------------------------------------- combine
 // out_t = u_t + sum_s Ys[s][t] + sum_k gate[t,k] * Y[slot_row[t*K+k]]
 // (output equation of the DeepSeek-V3 guides, "Metodo" section 2; the pwwt.cn
-// note's section 4 combine). fp32 accumulation in that fixed order, one
-// workgroup of 128 threads per token, 8 elements per thread per step. A step
-// issues the loads of all its rows (u, the shared rows, up to 8 routed rows)
-// before it adds any of them, so each wave keeps ~10 loads in flight instead
-// of one row at a time.
-constexpr int CB_THREADS = 128;
-constexpr int CB_ROWS = 8;           // routed rows loaded together (K > 8 runs in groups of 8)
-
-template <bool BF>
-__device__ __forceinline__ void combine_load8(const void* base, size_t row, int d, int c, float* v) {
-  if (BF) {
-    const i32x4 q = *(const i32x4*)((const uint16_t*)base + row * d + c);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      v[2 * i] = __uint_as_float(((uint32_t)q[i]) << 16);
-      v[2 * i + 1] = __uint_as_float(((uint32_t)q[i]) & 0xFFFF0000u);
-    }
-  } else {
-    const f32x4 p0 = *(const f32x4*)((const float*)base + row * d + c);
-    const f32x4 p1 = *(const f32x4*)((const float*)base + row * d + c + 4);
-#pragma unroll
-    for (int i = 0; i < 4; i++) { v[i] = p0[i]; v[4 + i] = p1[i]; }
-  }
-}
-
-template <bool IO_BF16, bool Y_BF16>
-__global__ __launch_bounds__(CB_THREADS) void combine_kernel(CombineArgs a) {
-  const int t = blockIdx.x;
-  __shared__ int32_t srow[64];
-  __shared__ float sg[64];
-  if (threadIdx.x < a.K) {
-    srow[threadIdx.x] = a.slot_row[(size_t)t * a.K + threadIdx.x];
-    sg[threadIdx.x] = a.gate[(size_t)t * a.K + threadIdx.x];
-  }
-  __syncthreads();
-  const unsigned n_rows = (unsigned)(a.T * a.K);
-  for (int c = threadIdx.x * 8; c < a.d; c += CB_THREADS * 8) {
-    // A dropped selection (capacity limit) has no row, and rows outside Y are skipped too:
-    // their slots load row 0 (always inside Y) and add nothing, so every load is
-    // unconditional. Group g's routed rows are loaded before anything is added (group 0
-    // before the shared rows), and added after, in the fixed order.
-    float acc[8];
-    bool use[CB_ROWS];
-    float v[CB_ROWS][8];
-    auto load_group = [&](int k0) __attribute__((always_inline)) {
-#pragma unroll
-      for (int j = 0; j < CB_ROWS; j++) {
-        use[j] = k0 + j < a.K && (unsigned)srow[k0 + j] < n_rows;
-        combine_load8<Y_BF16>(a.y, use[j] ? (size_t)srow[k0 + j] : 0, a.d, c, v[j]);
-      }
-    };
-    auto add_group = [&](int k0) __attribute__((always_inline)) {
-#pragma unroll
-      for (int j = 0; j < CB_ROWS; j++) {
-        if (use[j]) {
-          const float g = sg[k0 + j];
-#pragma unroll
-          for (int i = 0; i < 8; i++) acc[i] = fmaf(g, v[j][i], acc[i]);
-        }
-      }
-    };
-    combine_load8<IO_BF16>(a.u, t, a.d, c, acc);
-    load_group(0);
-    for (int s = 0; s < a.n_shared; s++) {
-      float w[8];
-      combine_load8<Y_BF16>(a.y_shared, (size_t)s * a.shared_stride + t, a.d, c, w);
-#pragma unroll
-      for (int i = 0; i < 8; i++) acc[i] += w[i];
-    }
-    add_group(0);
-    for (int k0 = CB_ROWS; k0 < a.K; k0 += CB_ROWS) {
-      load_group(k0);
-      add_group(k0);
-    }
-    if (IO_BF16) {
-      i32x4 q;
-#pragma unroll
-      for (int i = 0; i < 4; i++) q[i] = (int)pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-      *(i32x4*)((uint16_t*)a.out + (size_t)t * a.d + c) = q;
-    } else {
-      float* o = (float*)a.out + (size_t)t * a.d + c;
-      *(f32x4*)o = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *(f32x4*)(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-    }
-  }
-}
-
-// The same sum with one wave per token: the token's row indices and gates are
-// wave-uniform, so they come through the scalar cache (no LDS, no barrier),
-// and every lane handles 8 consecutive elements of CW chunks of 512 elements
-// at once, so a lane has CW * (2 + K) loads in flight. Everything here is read
-// or written once: loads and stores carry the non-temporal hint.
-#ifndef COMBINE_WAVE
-#define COMBINE_WAVE 1
-#endif
-#ifndef COMBINE_CW
-#define COMBINE_CW 8
-#endif
-#ifndef COMBINE_ROWS
-#define COMBINE_ROWS 2
-#endif
-constexpr int CW = COMBINE_CW;
-constexpr int CWR = COMBINE_ROWS;    // routed rows loaded together
+// note's section 4 combine), fp32 accumulation in that fixed order. One wave
+// per token: the token's row indices and gates are wave-uniform, so they come
+// through the scalar cache (no LDS, no barrier), and every lane handles 8
+// consecutive elements of CW chunks of 512 elements at once, so a lane has
+// CW * (2 + K) loads in flight. Everything here is read or written once:
+// loads and stores carry the non-temporal hint.
+constexpr int CW = 8;                // 512-element chunks per lane and pass
+constexpr int CWR = 2;               // routed rows loaded together
 
 template <bool BF>
 __device__ __forceinline__ void combine_load8_nt(const void* base, size_t row, int d, int c, float* v) {
@@ -201,17 +106,10 @@ __global__ __launch_bounds__(64) void combine_wave_kernel(CombineArgs a) {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   const bool io = a.io_dtype == MOE_BF16, yb = a.y_dtype == MOE_BF16;
-  if (COMBINE_WAVE) {
-    if (io && yb) combine_wave_kernel<true, true><<<a.T, 64, 0, s>>>(a);
-    else if (io) combine_wave_kernel<true, false><<<a.T, 64, 0, s>>>(a);
-    else if (yb) combine_wave_kernel<false, true><<<a.T, 64, 0, s>>>(a);
-    else combine_wave_kernel<false, false><<<a.T, 64, 0, s>>>(a);
-    return hipGetLastError();
-  }
-  if (io && yb) combine_kernel<true, true><<<a.T, CB_THREADS, 0, s>>>(a);
-  else if (io) combine_kernel<true, false><<<a.T, CB_THREADS, 0, s>>>(a);
-  else if (yb) combine_kernel<false, true><<<a.T, CB_THREADS, 0, s>>>(a);
-  else combine_kernel<false, false><<<a.T, CB_THREADS, 0, s>>>(a);
+  if (io && yb) combine_wave_kernel<true, true><<<a.T, 64, 0, s>>>(a);
+  else if (io) combine_wave_kernel<true, false><<<a.T, 64, 0, s>>>(a);
+  else if (yb) combine_wave_kernel<false, true><<<a.T, 64, 0, s>>>(a);
+  else combine_wave_kernel<false, false><<<a.T, 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
