@@ -178,7 +178,7 @@ static size_t h_rows(const moe_desc_t* d, size_t rows, size_t n_seg) {
 static size_t qh_rows(size_t rows, size_t n_seg) { return rows + (n_seg + 1) * kMaxTileRows; }
 
 // K-blocked weights apply to bf16 and FP8 experts whose products all take the LDS-DMA kernels
-// (FP8: 256-row tiles, which gemm_bm picks when d % 256 == 0)
+// (FP8: 256- or 320-row tiles, which gemm_bm picks when d % 256 == 0)
 static bool blocked_ok(const moe_desc_t* d) {
   const bool shared_ok = d->n_shared == 0 || d->inter_shared % 128 == 0;
   const bool dt_ok = d->expert_dtype == MOE_BF16 || d->expert_dtype == MOE_FP8_E4M3;
@@ -892,7 +892,9 @@ extern "C" int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const m
   // which also keeps the affinities for the gate gradients), then A|B, H, Y
   RouteArgs ra = route_args(d, u, w->centroids, b, nullptr, scores, idx, gate, nullptr);   // loads not needed
   MOE_TRY(run_router(ra, base + L.rscratch, s));
-  const int bm = f8 ? 256 : gemm_bm(d->expert_dtype, (int)(TK / N), d->d, d->inter);
+  // the forward's tile height (FP8: 256 or 320 rows by the mean load; every product's width
+  // is a multiple of 256 here, as the LDS-DMA kernels need)
+  const int bm = gemm_bm(d->expert_dtype, (int)(TK / N), d->d, d->inter);
   PermuteArgs p;
   p.idx = idx; p.T = T; p.K = K; p.n_routed = N;
   p.bitmap = (uint64_t*)(base + L.bitmap); p.wprefix = (int32_t*)(base + L.wprefix);
